@@ -1,0 +1,154 @@
+"""fp64 oracle of the Mamba-2 layer core -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product library never links, calls
+or falls back to it.
+
+The arithmetic lives in ``mamba2_oracle.c`` (gcc, double precision) and in
+``brute.py`` (numpy, unrolled products); this module only builds and marshals.
+Every input is converted to float64 from its exact stored value (bf16 or fp32).
+
+Pins (tests/test_oracle_*.py) and the one function left without its own pin
+are listed in each test module's docstring; none of the functions here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mamba2_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int)
+_L = ctypes.c_long
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP, no fast-math, no -march=native)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_conv1d.argtypes = [_L, _L, _L, _L, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
+        scan = [_L] * 6 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
+        lib.oracle_ssd_scan.argtypes = scan
+        lib.oracle_ssd_chunked.argtypes = [_L] * 7 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
+        lib.oracle_state_update.argtypes = [_L] * 6 + [_dp] * 3 + [_dp] + [_dp] * 4 + [_dp, _dp, _dp, ctypes.c_int]
+        for f in ("oracle_conv1d", "oracle_ssd_scan", "oracle_ssd_chunked", "oracle_state_update"):
+            getattr(lib, f).restype = None
+        _lib = lib
+    return _lib
+
+
+def _d(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def threads(requested: int = 0) -> int:
+    return _load().oracle_threads(int(requested))
+
+
+def conv1d(u, w, bias=None, state_in=None, nthreads: int = 0):
+    """u [B][L][Cc] -> (out [B][L][Cc], state_out [B][W-1][Cc]); fp64."""
+    u, w, bias, state_in = _d(u), _d(w), _d(bias), _d(state_in)
+    B, L, Cc = u.shape
+    W = w.shape[1]
+    out = np.empty_like(u)
+    st = np.empty((B, W - 1, Cc), dtype=np.float64)
+    _load().oracle_conv1d(B, L, Cc, W, _p(u), _p(w), _p(bias), _p(state_in), _p(out), _p(st),
+                          int(nthreads))
+    return out, st
+
+
+def _scan_args(x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, ngroups):
+    x, Bm, Cm, dt_raw = _d(x), _d(Bm), _d(Cm), _d(dt_raw)
+    dt_bias, A, D, z, h0 = _d(dt_bias), _d(A), _d(D), _d(z), _d(h0)
+    B, L, H = dt_raw.shape
+    P = x.shape[2] // H
+    N = Bm.shape[2] // ngroups
+    return x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, B, L, H, P, N
+
+
+def _heads(heads):
+    if heads is None:
+        return None, 0, None
+    arr = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    return arr, len(arr), arr.ctypes.data_as(_ip)
+
+
+def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, z=None, h0=None, *, ngroups: int,
+             heads: Optional[Sequence[int]] = None, nthreads: int = 0, y_out=None):
+    """O1: the recurrence token by token. Returns (y [B][L][H*P], h_final [B][H][N][P])."""
+    x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, B, L, H, P, N = _scan_args(
+        x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, ngroups)
+    y = np.zeros((B, L, H * P)) if y_out is None else y_out
+    hf = np.zeros((B, H, N, P))
+    keep, n_sel, hp = _heads(heads)
+    _load().oracle_ssd_scan(B, L, H, P, ngroups, N, _p(x), _p(Bm), _p(Cm), _p(dt_raw),
+                            _p(dt_bias), _p(A), _p(D), _p(z), _p(h0), _p(y), _p(hf), hp, n_sel,
+                            int(nthreads))
+    del keep
+    return y, hf
+
+
+def ssd_chunked(x, Bm, Cm, dt_raw, dt_bias, A, D=None, z=None, h0=None, *, ngroups: int,
+                chunk: int, heads: Optional[Sequence[int]] = None, nthreads: int = 0):
+    """O2: chunk-by-chunk evaluation of the same map."""
+    x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, B, L, H, P, N = _scan_args(
+        x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, ngroups)
+    y = np.zeros((B, L, H * P))
+    hf = np.zeros((B, H, N, P))
+    keep, n_sel, hp = _heads(heads)
+    _load().oracle_ssd_chunked(B, L, H, P, ngroups, N, int(chunk), _p(x), _p(Bm), _p(Cm),
+                               _p(dt_raw), _p(dt_bias), _p(A), _p(D), _p(z), _p(h0), _p(y),
+                               _p(hf), hp, n_sel, int(nthreads))
+    del keep
+    return y, hf
+
+
+def state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, *,
+                 nheads: int, ngroups: int, headdim: int = 64, dstate: int = 128,
+                 nthreads: int = 0):
+    """One decode token. Returns (y_t [B][H*P], conv_state', ssm_state') as new arrays."""
+    u_t, w, bias, dt_raw_t = _d(u_t), _d(w), _d(bias), _d(dt_raw_t)
+    dt_bias, A, D, z_t = _d(dt_bias), _d(A), _d(D), _d(z_t)
+    cs = np.array(conv_state, dtype=np.float64, copy=True, order="C")
+    ss = np.array(ssm_state, dtype=np.float64, copy=True, order="C")
+    B = u_t.shape[0]
+    y = np.zeros((B, nheads * headdim))
+    _load().oracle_state_update(B, nheads, headdim, ngroups, dstate, w.shape[1], _p(u_t), _p(w),
+                                _p(bias), _p(cs), _p(dt_raw_t), _p(dt_bias), _p(A), _p(D),
+                                _p(z_t), _p(ss), _p(y), int(nthreads))
+    return y, cs, ss
+
+
+def split_xbc(xbc, nheads: int, ngroups: int, headdim: int = 64, dstate: int = 128):
+    """Views of the x, B and C channel ranges of an xBC tensor [..][Cc]."""
+    di, gn = nheads * headdim, ngroups * dstate
+    return xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:di + 2 * gn]
