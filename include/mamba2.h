@@ -1,0 +1,164 @@
+/*
+ * mamba2.h -- C ABI of the MI355X (gfx950) Mamba-2 layer core.
+ *
+ * The layer is the Mamba-2 mixer of the Nemotron-Nano-2 hybrid model (hyper.ai
+ * summary of arXiv 2508.14444, section "方法"; neurohive article, section
+ * "Архитектура"): 8 groups, state dimension 128, head dimension 64, expansion 2,
+ * conv window 4, no bias in the surrounding linear layers. Its core is
+ *
+ *   xBC' = SiLU(causal depthwise conv1d(xBC) + bias)       width 4, per channel
+ *   dt   = softplus(dt_raw + dt_bias),  a = exp(dt * A)      per token and head
+ *   h_t  = a_t h_{t-1} + dt_t B_t x_t^T                      N x P state, fp32
+ *   y_t  = h_t^T C_t + D x_t,   out = y * SiLU(z)
+ *
+ * with B and C shared by the contiguous heads of each group (head h uses group
+ * h / (H / G)). The SSM state is always fp32, as the deployment section of the
+ * neurohive article ("Развертывание") requires of the Mamba cache.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory).
+ *    `dims` is host memory, read during the call only.
+ *  - Row-major layouts as commented. "io" means the element type selected by
+ *    dims->io_dtype (MAMBA2_BF16 or MAMBA2_F32); parameters (w, bias, dt_bias,
+ *    A, D) and SSM states are float32 in every mode.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    null stream). Nothing synchronizes, nothing is allocated, no state is kept
+ *    between calls. The caller owns every buffer and the stream.
+ *  - Validation runs on the host before anything is enqueued. On failure the
+ *    call returns a nonzero status, enqueues nothing and leaves every buffer
+ *    untouched; mamba2_last_error() describes the failure. Launch failures
+ *    return MAMBA2_ERR_HIP. Faults inside kernels surface asynchronously, as
+ *    for any stream work.
+ *  - Supported shapes: headdim 64, dstate 128, conv_width 4, nheads % ngroups
+ *    == 0, batch/seqlen/nheads >= 1 (seqlen 0 is accepted by the prefill calls
+ *    and does nothing). io pointers must be 16-byte aligned and io row strides
+ *    multiples of 16 bytes; f32 state pointers 16-byte aligned.
+ */
+#ifndef MAMBA2_H
+#define MAMBA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA2_ABI_VERSION 1
+
+enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
+
+enum mamba2_status {
+  MAMBA2_OK = 0,
+  MAMBA2_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  MAMBA2_ERR_SHAPE = 2,       /* a dimension or stride is out of range             */
+  MAMBA2_ERR_UNSUPPORTED = 3, /* valid but not implemented (headdim != 64, ...)    */
+  MAMBA2_ERR_DTYPE = 4,       /* io_dtype is neither MAMBA2_F32 nor MAMBA2_BF16    */
+  MAMBA2_ERR_ALIGN = 5,       /* pointer or stride breaks the 16-byte rule         */
+  MAMBA2_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap   */
+  MAMBA2_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required           */
+  MAMBA2_ERR_HIP = 8          /* the HIP runtime reported an error at launch       */
+};
+
+typedef struct mamba2_dims {
+  int32_t batch;      /* B: independent sequences                                  */
+  int32_t seqlen;     /* L: tokens per sequence (must be 1 for mamba2_state_update)*/
+  int32_t nheads;     /* H: SSM heads; d_inner = H * headdim                       */
+  int32_t headdim;    /* P: must be 64                                             */
+  int32_t ngroups;    /* G: B/C groups, divides H                                  */
+  int32_t dstate;     /* N: must be 128                                            */
+  int32_t conv_width; /* W: must be 4                                              */
+  int32_t chunk;      /* Q: prefill chunk length; 64 or 128 for bf16, 64 for f32   */
+  int32_t io_dtype;   /* enum mamba2_dtype                                         */
+} mamba2_dims;
+
+/*
+ * mamba2_conv1d -- causal depthwise conv of width W over `channels` channels,
+ * plus bias, then SiLU (the Mamba-2 block's "conv window 4": hyper.ai summary,
+ * section "方法"). For token t and channel c:
+ *     v = bias[c] + sum_{k=0}^{W-1} w[c*W + k] * u[t-(W-1)+k][c],   out = v / (1 + e^-v)
+ * Taps are a cross-correlation: w[c*W + W-1] multiplies the current token.
+ * Tokens before t = 0 come from conv_state (zeros if conv_state is NULL).
+ *
+ *   u          [B][L][channels] io, row stride u_stride elements (>= channels)
+ *   w          [channels][W] f32
+ *   bias       [channels] f32, or NULL for no bias
+ *   conv_state [B][W-1][channels] io, dense, or NULL. In: the W-1 raw inputs
+ *              preceding token 0 (slot 0 the oldest). Out: the last W-1 raw
+ *              inputs of the extended sequence (history, then u), i.e. the
+ *              history a following call or decode step needs. Updated in place.
+ *   out        [B][L][channels] io, row stride out_stride; must not overlap u,
+ *              w, bias or conv_state.
+ * channels must be a multiple of 8 (bf16) or 4 (f32). dims->headdim, dstate,
+ * ngroups, nheads and chunk are not used by this call. With seqlen 0 the call
+ * does nothing and returns MAMBA2_OK.
+ */
+int mamba2_conv1d(const mamba2_dims* dims, int32_t channels, const void* u, int64_t u_stride,
+                  const float* w, const float* bias, void* conv_state, void* out,
+                  int64_t out_stride, void* stream);
+
+/*
+ * mamba2_ssd_prefill_workspace_bytes -- device workspace mamba2_ssd_prefill
+ * needs for `dims`. The fused scan keeps its state on chip and needs none, so
+ * this returns 0 for every supported shape; it exists so that callers need not
+ * change if a future variant does.
+ */
+size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
+
+/*
+ * mamba2_ssd_prefill -- the selective scan over whole sequences (the
+ * spec recurrence above, evaluated chunk by chunk: inside a chunk of Q
+ * tokens as a causally masked quadratic form on MFMA, across chunks by carrying
+ * the fp32 state).
+ *
+ *   x       [B][L][H*P] io, token row stride x_stride (elements)
+ *   Bm, Cm  [B][L][G*N] io, row strides b_stride, c_stride
+ *   dt_raw  [B][L][H] io, dense
+ *   dt_bias, A [H] f32 (A <= 0 expected, not checked; A > 0 may overflow)
+ *   D       [H] f32, or NULL for no skip term
+ *   z       [B][L][H*P] io with row stride z_stride, or NULL for no gate
+ *   h0      [B][H][N][P] f32 initial state, or NULL for zeros
+ *   h_final [B][H][N][P] f32 final state, or NULL; may equal h0 (in place)
+ *   y       [B][L][H*P] io, row stride y_stride; must not overlap any input
+ *   workspace, workspace_bytes: at least mamba2_ssd_prefill_workspace_bytes
+ *           (may be NULL when that is 0)
+ * x/B/C may be views into one xBC tensor (row stride = its channel count).
+ * With seqlen 0 nothing per-token is read or written (those pointers may be
+ * NULL) and h_final receives h0 (or zeros).
+ */
+int mamba2_ssd_prefill(const mamba2_dims* dims, const void* x, int64_t x_stride, const void* Bm,
+                       int64_t b_stride, const void* Cm, int64_t c_stride, const void* dt_raw,
+                       const float* dt_bias, const float* A, const float* D, const void* z,
+                       int64_t z_stride, const float* h0, float* h_final, void* y,
+                       int64_t y_stride, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mamba2_state_update -- one decode token per sequence (dims->seqlen must be
+ * 1), updating both caches in place: the conv step above on the token's raw
+ * xBC, then one step of the recurrence on the fp32 state.
+ *
+ *   u_t        [B][Cc] io raw xBC of the new token, Cc = H*P + 2*G*N, dense
+ *   w, bias    conv parameters as in mamba2_conv1d ([Cc][W], [Cc] or NULL)
+ *   conv_state [B][W-1][Cc] io, updated in place (shifted by one token)
+ *   dt_raw_t   [B][H] io, dense
+ *   dt_bias, A, D as in mamba2_ssd_prefill (D may be NULL)
+ *   z_t        [B][H*P] io or NULL
+ *   ssm_state  [B][H][N][P] f32, updated in place
+ *   y_t        [B][H*P] io; must not overlap any other argument
+ */
+int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w,
+                        const float* bias, void* conv_state, const void* dt_raw_t,
+                        const float* dt_bias, const float* A, const float* D, const void* z_t,
+                        float* ssm_state, void* y_t, void* stream);
+
+/* Description of the last failure on the calling thread ("" after success). */
+const char* mamba2_last_error(void);
+
+/* MAMBA2_ABI_VERSION of the built library. */
+int mamba2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_H */

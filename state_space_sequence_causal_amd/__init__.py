@@ -1,0 +1,144 @@
+"""Python binding of libmamba2.so, the gfx950 Mamba-2 layer core.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the C library (include/mamba2.h). Torch is used for device memory and the
+current stream. There is no CPU fallback: if the library is missing, importing
+this package raises.
+
+Functions take torch CUDA tensors (bf16 or fp32 io, fp32 parameters and states)
+and enqueue on ``torch.cuda.current_stream()``; they return nothing and raise
+``Mamba2Error`` on a nonzero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "LIB_PATH", "Mamba2Error", "Dims", "lib", "io_dtype_of",
+    "mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update",
+    "mamba2_ssd_prefill_workspace_bytes", "mamba2_abi_version", "mamba2_last_error",
+    "MAMBA2_F32", "MAMBA2_BF16", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmamba2.so")
+
+MAMBA2_F32, MAMBA2_BF16 = 0, 1
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_DTYPE",
+          5: "ERR_ALIGN", 6: "ERR_ALIAS", 7: "ERR_WORKSPACE", 8: "ERR_HIP"}
+
+
+class Mamba2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "seqlen", "nheads", "headdim", "ngroups", "dstate", "conv_width",
+                 "chunk", "io_dtype")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m state_space_sequence_causal_amd.build`")
+
+# torch first: it loads its own HIP runtime (soname libamdhip64.so.7), and the
+# library's dependency of the same soname must bind to that one, so that device
+# pointers and streams handed over from torch belong to the runtime that
+# launches the kernels.
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_dims = ctypes.POINTER(Dims)
+lib.mamba2_abi_version.restype = ctypes.c_int
+lib.mamba2_last_error.restype = ctypes.c_char_p
+lib.mamba2_conv1d.argtypes = [_dims, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp]
+lib.mamba2_ssd_prefill_workspace_bytes.argtypes = [_dims]
+lib.mamba2_ssd_prefill_workspace_bytes.restype = _sz
+lib.mamba2_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                                   _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
+lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update"):
+    getattr(lib, _f).restype = ctypes.c_int
+
+
+def mamba2_abi_version() -> int:
+    return lib.mamba2_abi_version()
+
+
+def mamba2_last_error() -> str:
+    return lib.mamba2_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Mamba2Error(status, mamba2_last_error())
+
+
+def io_dtype_of(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MAMBA2_BF16
+    if t.dtype == torch.float32:
+        return MAMBA2_F32
+    raise Mamba2Error(4, f"io tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _row_stride(t) -> int:
+    """Token-row stride (elements) of a [.., L, width] view whose rows are evenly spaced."""
+    if t.numel() == 0:
+        return t.shape[-1]
+    if t.stride(-1) != 1:
+        raise Mamba2Error(2, "the last dimension must be contiguous")
+    return t.stride(-2)
+
+
+def _stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_dims(batch, seqlen, nheads, ngroups, chunk, io, headdim=64, dstate=128, conv_width=4) -> Dims:
+    return Dims(batch, seqlen, nheads, headdim, ngroups, dstate, conv_width, chunk, io)
+
+
+def mamba2_conv1d(u, w, bias, conv_state, out) -> None:
+    """out = SiLU(causal depthwise conv1d(u) + bias); conv_state updated in place (or None)."""
+    B, L, Cc = u.shape
+    d = make_dims(B, L, 1, 1, 64, io_dtype_of(u))
+    _check(lib.mamba2_conv1d(ctypes.byref(d), Cc, _ptr(u), _row_stride(u), _ptr(w), _ptr(bias),
+                             _ptr(conv_state), _ptr(out), _row_stride(out), _stream()))
+
+
+def mamba2_ssd_prefill_workspace_bytes(d: Dims) -> int:
+    return lib.mamba2_ssd_prefill_workspace_bytes(ctypes.byref(d))
+
+
+def mamba2_ssd_prefill(x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, h_final, y, *, ngroups: int,
+                       chunk: int, workspace=None) -> None:
+    """The chunked selective scan; x/Bm/Cm/z/y may be row-strided views (e.g. slices of xBC)."""
+    B, L, H = dt_raw.shape
+    d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(x))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mamba2_ssd_prefill(
+        ctypes.byref(d), _ptr(x), _row_stride(x), _ptr(Bm), _row_stride(Bm), _ptr(Cm),
+        _row_stride(Cm), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z),
+        0 if z is None else _row_stride(z), _ptr(h0), _ptr(h_final), _ptr(y), _row_stride(y),
+        _ptr(workspace), ws_bytes, _stream()))
+
+
+def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,
+                        *, ngroups: int) -> None:
+    """One decode token; conv_state and ssm_state are updated in place."""
+    B, H = dt_raw_t.shape
+    d = make_dims(B, 1, H, ngroups, 64, io_dtype_of(u_t))
+    _check(lib.mamba2_state_update(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_state),
+                                   _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
+                                   _ptr(ssm_state), _ptr(y_t), _stream()))

@@ -1,0 +1,123 @@
+// Device helpers for the gfx950 kernels: io element types, 16-byte vectors,
+// MFMA fragments and small math. Included by the .hip sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }  // RNE
+
+// ---------------------------------------------------------------- 16-byte io vectors
+// VE elements of T in 16 bytes.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> {
+  static constexpr int VE = 8;
+  bf16x8 v;
+  __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
+  __device__ __forceinline__ void set(int i, float f) { v[i] = (bf16)f; }
+};
+template <> struct Vec<float> {
+  static constexpr int VE = 4;
+  f32x4 v;
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+  __device__ __forceinline__ void set(int i, float f) { v[i] = f; }
+};
+
+template <typename T> __device__ __forceinline__ Vec<T> ld16(const T* p) {
+  Vec<T> r;
+  r.v = *reinterpret_cast<const decltype(r.v)*>(p);
+  return r;
+}
+template <typename T> __device__ __forceinline__ void st16(T* p, const Vec<T>& r) {
+  *reinterpret_cast<decltype(r.v)*>(p) = r.v;
+}
+template <typename T> __device__ __forceinline__ Vec<T> zero16() {
+  Vec<T> r;
+  for (int i = 0; i < Vec<T>::VE; ++i) r.v[i] = from_f<T>(0.f);
+  return r;
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(expf(v)); }
+__device__ __forceinline__ float silu_f(float v) { return v / (1.f + expf(-v)); }
+
+// ---------------------------------------------------------------- MFMA 32x32, K in steps of 16
+// An operand fragment holds, per lane, 8 values along K for one row (A) or one
+// column (B) of a 32-wide tile: lane l covers row/col l % 32 and lane group
+// g = l / 32 holds the 8 K-indices kappa(g, e), e = 0..7, of the 16-wide K step.
+// Any kappa works as long as A and B use the same one.
+// Accumulator (16 fp32 per lane): element r of lane l is D[row][col] with
+//   col = l % 32,  row = 8 * (r / 4) + 4 * (l / 32) + (r % 4).
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Fragment with contiguous kappa(g, e) = 8 g + e: p points at K-index 0 of the step;
+// 16-byte aligned.
+__device__ __forceinline__ Frag<bf16> frag_contig(const bf16* p, int g) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p + 8 * g);
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_contig(const float* p, int g) {
+  Frag<float> f;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p + 8 * g);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 8 * g + 4);
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+// Fragment with the accumulator-row kappa(g, e) = 8 (e / 4) + 4 g + (e % 4), which lets
+// accumulator registers 8m..8m+7 serve directly as the B operand of K rows 16m..16m+15.
+__device__ __forceinline__ Frag<bf16> frag_accrows(const bf16* p, int g) {
+  Frag<bf16> f;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p + 4 * g);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8 + 4 * g);
+  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_accrows(const float* p, int g) {
+  Frag<float> f;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 8 + 4 * g);
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+
+template <typename T> __device__ __forceinline__ void frag_set(Frag<T>& f, int e, float v);
+template <> __device__ __forceinline__ void frag_set<bf16>(Frag<bf16>& f, int e, float v) { f.v[e] = (bf16)v; }
+template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int e, float v) { f.v[e] = v; }
+__device__ __forceinline__ float frag_get(const Frag<bf16>& f, int e) { return (float)f.v[e]; }
+__device__ __forceinline__ float frag_get(const Frag<float>& f, int e) { return f.v[e]; }
+
+// Blocks are dispatched round-robin over the chip's 8 XCDs (each with its own L2).
+// Map dispatch order to a logical order in which consecutive logical ids share an XCD.
+__device__ __forceinline__ int xcd_local_order(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
+}  // namespace m2

@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (one per .hip source). Called by the
+// C-ABI layer after validation; each returns the HIP status of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+hipError_t launch_conv1d(int io_bf16, const void* u, int64_t u_stride, const float* w,
+                         const float* bias, void* conv_state, void* out, int64_t out_stride,
+                         int B, int L, int Cc, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* x; int64_t x_stride;
+  const void* Bm; int64_t b_stride;
+  const void* Cm; int64_t c_stride;
+  const void* dt_raw;
+  const float* dt_bias; const float* A; const float* D;
+  const void* z; int64_t z_stride;
+  const float* h0; float* h_final;
+  void* y; int64_t y_stride;
+  int B, L, H, G;
+};
+hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream);
+size_t ssd_prefill_lds_bytes(int io_bf16, int chunk);
+
+struct DecodeArgs {
+  const void* u_t;
+  const float* w; const float* bias;
+  void* conv_state;
+  const void* dt_raw_t;
+  const float* dt_bias; const float* A; const float* D;
+  const void* z_t;
+  float* ssm_state;
+  void* y_t;
+  int B, H, G;
+};
+hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace m2

@@ -1,0 +1,197 @@
+// C ABI of the Mamba-2 layer core: argument validation (pure host code, run
+// before anything touches the device) and dispatch to the gfx950 launchers.
+#include "../../include/mamba2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+#define M2_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return MAMBA2_OK;
+}
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi) in bytes; empty when lo == hi
+};
+Range span(const void* p, int64_t rows, int64_t stride, int64_t width, int64_t esize) {
+  Range r;
+  if (!p || rows <= 0 || width <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + (uintptr_t)(((rows - 1) * stride + width) * esize);
+  return r;
+}
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize_of(int io) { return io == MAMBA2_BF16 ? 2 : 4; }
+
+// Checks shared by every call. `need_model` also checks the SSM shape fields.
+int check_dims(const mamba2_dims* d, bool need_model) {
+  if (!d) return fail(MAMBA2_ERR_NULL, "dims is NULL");
+  if (d->io_dtype != MAMBA2_F32 && d->io_dtype != MAMBA2_BF16)
+    return fail(MAMBA2_ERR_DTYPE, "io_dtype %d is neither MAMBA2_F32 nor MAMBA2_BF16", d->io_dtype);
+  if (d->batch < 1 || d->batch > 65535) return fail(MAMBA2_ERR_SHAPE, "batch %d out of [1, 65535]", d->batch);
+  if (d->seqlen < 0) return fail(MAMBA2_ERR_SHAPE, "seqlen %d < 0", d->seqlen);
+  if (d->conv_width != 4) return fail(MAMBA2_ERR_UNSUPPORTED, "conv_width %d (only 4)", d->conv_width);
+  if (!need_model) return MAMBA2_OK;
+  if (d->nheads < 1 || d->ngroups < 1) return fail(MAMBA2_ERR_SHAPE, "nheads %d / ngroups %d < 1", d->nheads, d->ngroups);
+  if (d->nheads % d->ngroups) return fail(MAMBA2_ERR_SHAPE, "nheads %d not a multiple of ngroups %d", d->nheads, d->ngroups);
+  if (d->headdim != 64) return fail(MAMBA2_ERR_UNSUPPORTED, "headdim %d (only 64)", d->headdim);
+  if (d->dstate != 128) return fail(MAMBA2_ERR_UNSUPPORTED, "dstate %d (only 128)", d->dstate);
+  if ((int64_t)d->batch * d->nheads > (int64_t)1 << 30)
+    return fail(MAMBA2_ERR_SHAPE, "batch * nheads too large");
+  return MAMBA2_OK;
+}
+
+int check_stride(const char* name, const void* p, int64_t stride, int64_t width, int io) {
+  int ve = 16 / esize_of(io);
+  if (stride < width) return fail(MAMBA2_ERR_SHAPE, "%s stride %lld < row width %lld", name, (long long)stride, (long long)width);
+  if (stride % ve) return fail(MAMBA2_ERR_ALIGN, "%s stride %lld not a multiple of 16 bytes", name, (long long)stride);
+  if (!aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MAMBA2_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MAMBA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+M2_EXPORT int mamba2_abi_version(void) { return MAMBA2_ABI_VERSION; }
+
+M2_EXPORT const char* mamba2_last_error(void) { return g_err.c_str(); }
+
+M2_EXPORT int mamba2_conv1d(const mamba2_dims* d, int32_t channels, const void* u, int64_t u_stride,
+                            const float* w, const float* bias, void* conv_state, void* out,
+                            int64_t out_stride, void* stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (d->seqlen == 0) return ok();  // nothing read or written; the history is unchanged
+  if (!u || !w || !out) return fail(MAMBA2_ERR_NULL, "u, w and out must not be NULL");
+  const int io = d->io_dtype, es = esize_of(io), ve = 16 / es;
+  if (channels < 1 || channels % ve)
+    return fail(MAMBA2_ERR_SHAPE, "channels %d must be a positive multiple of %d", channels, ve);
+  if ((st = check_stride("u", u, u_stride, channels, io))) return st;
+  if ((st = check_stride("out", out, out_stride, channels, io))) return st;
+  if (!aligned16(w)) return fail(MAMBA2_ERR_ALIGN, "w is not 16-byte aligned");
+  if (conv_state && !aligned16(conv_state)) return fail(MAMBA2_ERR_ALIGN, "conv_state is not 16-byte aligned");
+  const int64_t BL = (int64_t)d->batch * d->seqlen;
+  Range ro = span(out, BL, out_stride, channels, es);
+  Range ins[] = {span(u, BL, u_stride, channels, es), span(w, 1, 0, (int64_t)channels * 4, 4),
+                 span(bias, 1, 0, channels, 4),
+                 span(conv_state, 1, 0, (int64_t)d->batch * 3 * channels, es)};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return fail(MAMBA2_ERR_ALIAS, "out overlaps an input");
+  if (overlap(ins[3], ins[0])) return fail(MAMBA2_ERR_ALIAS, "conv_state overlaps u");
+  if ((d->seqlen + 63) / 64 > 65535) return fail(MAMBA2_ERR_SHAPE, "seqlen too large");
+  return hip_status(m2::launch_conv1d(io == MAMBA2_BF16, u, u_stride, w, bias, conv_state, out,
+                                      out_stride, d->batch, d->seqlen, channels,
+                                      static_cast<hipStream_t>(stream)),
+                    "conv1d launch");
+}
+
+M2_EXPORT size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
+  (void)d;
+  return 0;
+}
+
+M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_stride,
+                                 const void* Bm, int64_t b_stride, const void* Cm,
+                                 int64_t c_stride, const void* dt_raw, const float* dt_bias,
+                                 const float* A, const float* D, const void* z, int64_t z_stride,
+                                 const float* h0, float* h_final, void* y, int64_t y_stride,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_dims(d, true);
+  if (st) return st;
+  const int io = d->io_dtype, es = esize_of(io);
+  if (io == MAMBA2_BF16 ? (d->chunk != 64 && d->chunk != 128) : d->chunk != 64)
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64 or 128; f32: 64)",
+                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+  if (!dt_bias || !A) return fail(MAMBA2_ERR_NULL, "dt_bias and A must not be NULL");
+  if (d->seqlen > 0 && (!x || !Bm || !Cm || !dt_raw || !y))
+    return fail(MAMBA2_ERR_NULL, "x, Bm, Cm, dt_raw and y must not be NULL when seqlen > 0");
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
+  const int64_t BL = (int64_t)d->batch * d->seqlen;
+  if ((st = check_stride("x", x, x_stride, H * P, io))) return st;
+  if ((st = check_stride("Bm", Bm, b_stride, G * N, io))) return st;
+  if ((st = check_stride("Cm", Cm, c_stride, G * N, io))) return st;
+  if ((st = check_stride("y", y, y_stride, H * P, io))) return st;
+  if (z && (st = check_stride("z", z, z_stride, H * P, io))) return st;
+  if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
+    return fail(MAMBA2_ERR_ALIGN, "h0 / h_final must be 16-byte aligned");
+  const int64_t state_elems = (int64_t)d->batch * H * N * P;
+  Range ry = span(y, BL, y_stride, H * P, es);
+  Range rh0 = span(h0, 1, 0, state_elems, 4), rhf = span(h_final, 1, 0, state_elems, 4);
+  Range ins[] = {span(x, BL, x_stride, H * P, es),  span(Bm, BL, b_stride, G * N, es),
+                 span(Cm, BL, c_stride, G * N, es), span(dt_raw, BL, H, H, es),
+                 span(z, BL, z_stride, H * P, es),  rh0,
+                 rhf,                               span(dt_bias, 1, 0, H, 4),
+                 span(A, 1, 0, H, 4),               span(D, 1, 0, H, 4)};
+  for (const Range& r : ins)
+    if (overlap(ry, r)) return fail(MAMBA2_ERR_ALIAS, "y overlaps an input or the state");
+  for (int i = 0; i < 5; ++i)
+    if (overlap(rhf, ins[i])) return fail(MAMBA2_ERR_ALIAS, "h_final overlaps an input");
+  if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
+    return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
+  m2::PrefillArgs a{x, x_stride, Bm, b_stride, Cm, c_stride, dt_raw, dt_bias, A, D,
+                    z, z_stride, h0, h_final, y, y_stride, d->batch, d->seqlen, d->nheads, d->ngroups};
+  return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, static_cast<hipStream_t>(stream)),
+                    "ssd_prefill launch");
+}
+
+M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const float* w,
+                                  const float* bias, void* conv_state, const void* dt_raw_t,
+                                  const float* dt_bias, const float* A, const float* D,
+                                  const void* z_t, float* ssm_state, void* y_t, void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if (d->seqlen != 1) return fail(MAMBA2_ERR_SHAPE, "state_update needs seqlen 1 (got %d)", d->seqlen);
+  if (!u_t || !w || !conv_state || !dt_raw_t || !dt_bias || !A || !ssm_state || !y_t)
+    return fail(MAMBA2_ERR_NULL, "u_t, w, conv_state, dt_raw_t, dt_bias, A, ssm_state and y_t must not be NULL");
+  const int io = d->io_dtype, es = esize_of(io);
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, B = d->batch;
+  if (H / G > 256) return fail(MAMBA2_ERR_UNSUPPORTED, "more than 256 heads per group");
+  const int64_t Cc = H * P + 2 * G * N;
+  const void* al[] = {u_t, w, conv_state, ssm_state, y_t, z_t};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "u_t, w, conv_state, ssm_state, y_t, z_t must be 16-byte aligned");
+  Range ry = span(y_t, B, H * P, H * P, es);
+  Range rcs = span(conv_state, 1, 0, B * 3 * Cc, es), rss = span(ssm_state, 1, 0, B * H * N * P, 4);
+  Range ins[] = {span(u_t, B, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
+                 span(dt_raw_t, B, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
+                 span(D, 1, 0, H, 4),         span(z_t, B, H * P, H * P, es)};
+  for (const Range& r : ins)
+    if (overlap(ry, r) || overlap(rcs, r) || overlap(rss, r))
+      return fail(MAMBA2_ERR_ALIAS, "y_t, conv_state or ssm_state overlaps an input");
+  if (overlap(ry, rcs) || overlap(ry, rss) || overlap(rcs, rss))
+    return fail(MAMBA2_ERR_ALIAS, "y_t, conv_state and ssm_state must not overlap");
+  m2::DecodeArgs a{u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,
+                   d->batch, d->nheads, d->ngroups};
+  return hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, static_cast<hipStream_t>(stream)),
+                    "state_update launch");
+}

@@ -1,0 +1,134 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function include/mamba2.h declares, and rejects bad arguments before touching
+the device. The fake pointers below are never dereferenced: validation fails
+first, so no HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mamba2.h")
+
+m2 = pytest.importorskip("state_space_sequence_causal_amd")
+
+OK, ENULL, ESHAPE, EUNSUP, EDTYPE, EALIGN, EALIAS = 0, 1, 2, 3, 4, 5, 6
+BASE = 1 << 40          # fake, 16-byte aligned device addresses far apart
+MB = 1 << 30
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(mamba2_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared()
+    for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update",
+              "mamba2_ssd_prefill_workspace_bytes", "mamba2_last_error", "mamba2_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m2.LIB_PATH)
+    for n in declared():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert m2.mamba2_abi_version() == 1
+
+
+def dims(**kw):
+    d = dict(batch=1, seqlen=256, nheads=4, ngroups=1, chunk=64, io=m2.MAMBA2_F32)
+    d.update(kw)
+    return m2.make_dims(**d)
+
+
+def prefill(d, **kw):
+    H, G = d.nheads, d.ngroups
+    a = dict(x=BASE, xs=H * 64, Bm=BASE + 4 * MB, bs=G * 128, Cm=BASE + 6 * MB, cs=G * 128,
+             dt=BASE + 8 * MB, dtb=BASE + 9 * MB, A=BASE + 10 * MB, D=BASE + 11 * MB,
+             z=BASE + 12 * MB, zs=H * 64, h0=BASE + 16 * MB, hf=BASE + 20 * MB, y=BASE + 24 * MB,
+             ys=H * 64)
+    a.update(kw)
+    return m2.lib.mamba2_ssd_prefill(ctypes.byref(d), a["x"], a["xs"], a["Bm"], a["bs"], a["Cm"],
+                                     a["cs"], a["dt"], a["dtb"], a["A"], a["D"], a["z"], a["zs"],
+                                     a["h0"], a["hf"], a["y"], a["ys"], None, 0, None)
+
+
+def conv(d, channels=512, **kw):
+    a = dict(u=BASE, us=channels, w=BASE + 4 * MB, b=BASE + 5 * MB, cs=BASE + 6 * MB,
+             out=BASE + 8 * MB, os=channels)
+    a.update(kw)
+    return m2.lib.mamba2_conv1d(ctypes.byref(d), channels, a["u"], a["us"], a["w"], a["b"], a["cs"],
+                                a["out"], a["os"], None)
+
+
+def decode(d, **kw):
+    a = dict(u=BASE, w=BASE + 1 * MB, b=BASE + 2 * MB, cs=BASE + 3 * MB, dt=BASE + 4 * MB,
+             dtb=BASE + 5 * MB, A=BASE + 6 * MB, D=BASE + 7 * MB, z=BASE + 8 * MB,
+             ss=BASE + 16 * MB, y=BASE + 9 * MB)
+    a.update(kw)
+    return m2.lib.mamba2_state_update(ctypes.byref(d), a["u"], a["w"], a["b"], a["cs"], a["dt"],
+                                      a["dtb"], a["A"], a["D"], a["z"], a["ss"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(io=7), EDTYPE), (dict(batch=0), ESHAPE), (dict(seqlen=-1), ESHAPE),
+    (dict(nheads=6, ngroups=4), ESHAPE), (dict(nheads=0), ESHAPE),
+    (dict(headdim=32), EUNSUP), (dict(dstate=64), EUNSUP), (dict(conv_width=3), EUNSUP),
+    (dict(chunk=128), EUNSUP), (dict(chunk=256, io=m2.MAMBA2_BF16), EUNSUP), (dict(chunk=48), EUNSUP),
+])
+def test_prefill_rejects_dims(kw, code):
+    assert prefill(dims(**kw)) == code
+    assert m2.mamba2_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), ENULL), (dict(Bm=None), ENULL), (dict(Cm=None), ENULL), (dict(dt=None), ENULL),
+    (dict(dtb=None), ENULL), (dict(A=None), ENULL), (dict(y=None), ENULL),
+    (dict(x=BASE + 4), EALIGN), (dict(xs=255), ESHAPE), (dict(xs=258), EALIGN),
+    (dict(bs=100), ESHAPE), (dict(ys=250), ESHAPE), (dict(h0=BASE + 16 * MB + 8), EALIGN),
+    (dict(y=BASE + 4 * MB), EALIAS), (dict(y=BASE), EALIAS), (dict(hf=BASE + 12 * MB), EALIAS),
+    (dict(y=BASE + 20 * MB), EALIAS), (dict(hf=BASE + 16 * MB + 4096), EALIAS),
+])
+def test_prefill_rejects_pointers(kw, code):
+    assert prefill(dims(), **kw) == code, m2.mamba2_last_error()
+
+
+def test_dims_null():
+    assert m2.lib.mamba2_ssd_prefill(None, BASE, 256, BASE, 128, BASE, 128, BASE, BASE, BASE, None,
+                                     None, 0, None, None, BASE, 256, None, 0, None) == ENULL
+
+
+@pytest.mark.parametrize("kw,chan,code", [
+    (dict(u=None), 512, ENULL), (dict(w=None), 512, ENULL), (dict(out=None), 512, ENULL),
+    (dict(), 510, ESHAPE), (dict(), 0, ESHAPE), (dict(us=500), 512, ESHAPE),
+    (dict(u=BASE + 8), 512, EALIGN), (dict(w=BASE + 4 * MB + 4), 512, EALIGN),
+    (dict(out=BASE), 512, EALIAS), (dict(cs=BASE + 8 * MB), 512, EALIAS), (dict(cs=BASE), 512, EALIAS),
+])
+def test_conv_rejects(kw, chan, code):
+    assert conv(dims(), channels=chan, **kw) == code, m2.mamba2_last_error()
+
+
+def test_conv_bf16_needs_multiple_of_8():
+    assert conv(dims(io=m2.MAMBA2_BF16), channels=4, us=8, os=8) == ESHAPE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), ENULL), (dict(cs=None), ENULL), (dict(ss=None), ENULL), (dict(y=None), ENULL),
+    (dict(ss=BASE + 16 * MB + 4), EALIGN), (dict(y=BASE), EALIAS), (dict(cs=BASE + 16 * MB), EALIAS),
+])
+def test_decode_rejects(kw, code):
+    assert decode(dims(seqlen=1), **kw) == code, m2.mamba2_last_error()
+
+
+def test_decode_needs_one_token():
+    assert decode(dims(seqlen=2)) == ESHAPE
+    assert decode(dims(seqlen=1, nheads=512, ngroups=1)) == EUNSUP
+
+
+def test_workspace_query_is_zero():
+    assert m2.mamba2_ssd_prefill_workspace_bytes(dims(io=m2.MAMBA2_BF16, chunk=128)) == 0
