@@ -1,0 +1,292 @@
+"""Benchmark of the Mamba-2 layer core on one MI355X.
+
+One step = one pass of the prefill hot path over one batch of synthetic input
+already resident in HBM: mamba2_conv1d (width-4 causal conv + SiLU over the xBC
+channels) followed by mamba2_ssd_prefill (the fused chunked scan), on the
+12B-shape single-layer workload: B=1, L=8192, 160 heads x 64, 8 groups,
+d_state 128, chunk 128, bf16 io, fp32 state. ``value`` is prefill tokens/s of
+that step. The one-token decode state update is measured in the same run on
+the 9B-shape batch-64 decode workload and reported under "decode".
+
+Per-kernel durations come from HIP events recorded around each launch on the
+stream the kernels run on (torch's current stream). Algorithmic bytes count
+every input read once, every output written once and the fp32 state read and
+written once; they are the roofline numerators.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K]
+       [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "SSD prefill tokens/s @12B-shape L=8k; decode state-update GB/s % of HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "ssd_prefill": ["ssd_prefill.hip", "device.h"],
+    "state_update": ["state_update.hip", "device.h"],
+    "conv1d": ["conv1d.hip", "device.h"],
+}
+
+
+def kernel_source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "state_space_sequence_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str, launches_bytes_unit: float = 1.0):
+    """HBM bytes per launch from the committed counter summary, or None when the kernel
+    source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash(name):
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------ workloads
+def prefill_bytes(cfg) -> dict:
+    """Algorithmic HBM bytes of one prefill pass (inputs once, outputs once)."""
+    e = 2 if cfg.io == "bf16" else 4
+    B, L, H, P, G, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    Cc = cfg.conv_channels
+    tok = B * L
+    ssd = tok * (3 * H * P * e + 2 * G * N * e + H * e)        # x, z, y; B, C; dt
+    ssd += B * H * N * P * 4                                     # h_final (h0 = 0 is not read)
+    ssd += 3 * H * 4                                             # dt_bias, A, D
+    conv = tok * 2 * Cc * e + Cc * 5 * 4 + 2 * B * 3 * Cc * e    # u, out; w, bias; conv cache
+    return {"ssd": ssd, "conv": conv}
+
+
+def prefill_flops(cfg) -> float:
+    """Algorithmic flops of the chunked scan: per token G(Q+1)N + H(Q+1)P (the causal halves
+    of C.B^T and M.X) + 4HNP (chunk state and carried-state output)."""
+    H, P, G, N, Q = cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.chunk
+    return cfg.batch * cfg.seqlen * (G * (Q + 1) * N + H * (Q + 1) * P + 4 * H * N * P)
+
+
+def decode_bytes(cfg) -> int:
+    e = 2 if cfg.io == "bf16" else 4
+    B, H, P, G, N, Cc = cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.conv_channels
+    per_seq = 2 * H * N * P * 4 + 2 * 3 * Cc * e + Cc * e + H * P * e + H * e + H * P * e
+    params = Cc * 5 * 4 + 3 * H * 4
+    return B * per_seq + params
+
+
+# ------------------------------------------------------------------------------ GPU parts
+def run_prefill(args, torch, m2, si):
+    cfg = si.CONFIGS[1]
+    inp = si.draw_prefill(cfg)
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    u, z, dt = dev(inp["xbc"]), dev(inp["z"]), dev(inp["dt_raw"])
+    w, bias, dtb, A, D = (f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
+    del inp
+    di, gn = cfg.d_inner, cfg.ngroups * cfg.dstate
+    xbc = torch.empty_like(u)
+    x, Bm, Cm = xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:]
+    cs = torch.zeros((cfg.batch, 3, cfg.conv_channels), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((cfg.batch, cfg.seqlen, di), dtype=torch.bfloat16, device="cuda")
+    hf = torch.empty((cfg.batch, cfg.nheads, cfg.dstate, cfg.headdim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m2.mamba2_ssd_prefill_workspace_bytes(
+        m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, cfg.chunk, m2.MAMBA2_BF16)),
+        dtype=torch.uint8, device="cuda")
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        m2.mamba2_conv1d(u, w, bias, cs, xbc)
+        if evs:
+            evs[1].record()
+        m2.mamba2_ssd_prefill(x, Bm, Cm, dt, dtb, A, D, z, None, hf, y, ngroups=cfg.ngroups,
+                              chunk=cfg.chunk, workspace=ws)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    conv_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / args.steps
+    ssd_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1e3 / args.steps
+    return cfg, total_ms / args.steps, wall, conv_us, ssd_us
+
+
+def run_decode(args, torch, m2, si):
+    cfg = si.CONFIGS[2]
+    p = si.draw_params(cfg)
+    step_inp = si.draw_decode_step(cfg, 0)
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    u, z, dt = (dev(step_inp[k][:, 0]) for k in ("xbc", "z", "dt_raw"))
+    w, bias, dtb, A, D = (f32(p[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
+    h0 = f32(si.draw_h0(cfg))
+    cs0 = dev(si.draw_conv_state(cfg))
+    # two independent (state, cache) sets used in turn: 512 MiB of state, twice the
+    # 256 MB Infinity Cache, so each step streams its state from HBM
+    states = [h0, h0.clone()]
+    caches = [cs0, cs0.clone()]
+    y = torch.empty((cfg.batch, cfg.d_inner), dtype=torch.bfloat16, device="cuda")
+
+    def step(k):
+        m2.mamba2_state_update(u, w, bias, caches[k & 1], dt, dtb, A, D, z, states[k & 1], y,
+                               ngroups=cfg.ngroups)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    n = args.decode_steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for k in range(n):
+        evs[k][0].record()
+        step(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return cfg, sum(times) / n, times[n // 2]
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, so counter runs can scale FETCH_SIZE and
+    WRITE_SIZE to bytes: it reads and writes exactly 1 GiB."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return 1 << 30
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(si):
+    """The fp64 oracle timed on a bounded sample of the prefill workload: the conv over all
+    8192 tokens and the sequential scan over 16 of the 160 heads (every tenth head, two per
+    group), all 8192 tokens; the scan time is scaled by 10 to the full layer."""
+    import numpy as np
+    import oracle
+    cfg = si.CONFIGS[1]
+    inp = si.draw_prefill(cfg)
+    heads = list(range(0, cfg.nheads, 10))
+    u = np.ascontiguousarray(inp["xbc"], dtype=np.float64)
+    threads = oracle.threads(0)
+    t0 = time.perf_counter()
+    xr, _ = oracle.conv1d(u, inp["conv_w"], inp["conv_b"], None)
+    t_conv = time.perf_counter() - t0
+    x, Bm, Cm = (np.ascontiguousarray(a) for a in oracle.split_xbc(xr, cfg.nheads, cfg.ngroups))
+    z = np.ascontiguousarray(inp["z"], dtype=np.float64)
+    dt = np.ascontiguousarray(inp["dt_raw"], dtype=np.float64)
+    t0 = time.perf_counter()
+    oracle.ssd_scan(x, Bm, Cm, dt, inp["dt_bias"], inp["A"], inp["D"], z, None, ngroups=cfg.ngroups,
+                    heads=heads)
+    t_scan = time.perf_counter() - t0
+    full = t_conv + t_scan * cfg.nheads / len(heads)
+    return {"value": cfg.batch * cfg.seqlen / full, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle on the same prefill workload: conv1d over all {cfg.seqlen} tokens "
+                      f"({t_conv:.2f} s) and the sequential scan over {len(heads)} of {cfg.nheads} heads "
+                      f"(all groups) x {cfg.seqlen} tokens ({t_scan:.2f} s), scan scaled x"
+                      f"{cfg.nheads // len(heads)} to the full layer"}
+
+
+# ------------------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer core runs on a single MI355X with no "
+              "collectives, so --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import seeded_inputs as si
+    import state_space_sequence_causal_amd as m2
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(torch)
+    cfg, ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si)
+    by = prefill_bytes(cfg)
+    fl = prefill_flops(cfg)
+    tokens = cfg.batch * cfg.seqlen
+    ssd_gbs = by["ssd"] / (ssd_us * 1e-6) / 1e9
+    dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
+    dby = decode_bytes(dcfg)
+    dec_gbs = dby / (dec_us * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "12B-shape Mamba-2 layer-core prefill: conv1d + chunked SSD scan",
+                   "batch": cfg.batch, "seq_len": cfg.seqlen, "nheads": cfg.nheads,
+                   "headdim": cfg.headdim, "ngroups": cfg.ngroups, "dstate": cfg.dstate,
+                   "conv_width": cfg.conv_width, "chunk": cfg.chunk, "io": "bf16",
+                   "state": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "ssd_prefill", "bound": "hbm", "achieved": ssd_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ssd_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("ssd_prefill"),
+                     "algorithmic_bytes": by["ssd"], "avg_launch_us": ssd_us},
+        "kernels": {
+            "ssd_prefill": {"us": ssd_us, "tokens_per_s": tokens / (ssd_us * 1e-6), "GB_s": ssd_gbs,
+                            "algorithmic_TFLOP_s": fl / (ssd_us * 1e-6) / 1e12,
+                            "mfma_frac_algorithmic": fl / (ssd_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+            "conv1d": {"us": conv_us, "GB_s": by["conv"] / (conv_us * 1e-6) / 1e9,
+                       "frac": by["conv"] / (conv_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "traffic": measured_traffic("conv1d")},
+        },
+        "decode": {"workload": "9B-shape decode state update: B=64, 128 heads x 64, 8 groups, "
+                               "d_state 128, bf16 io, fp32 state (256 MiB), in place",
+                   "us_per_step": dec_us, "us_p50": dec_p50, "GB_s": dec_gbs,
+                   "hbm_frac": dec_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dby,
+                   "tokens_per_s": dcfg.batch / (dec_us * 1e-6),
+                   "traffic": measured_traffic("state_update")},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(si)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -68,7 +68,7 @@ typedef struct mamba2_dims {
   int32_t ngroups;    /* G: B/C groups, divides H                                  */
   int32_t dstate;     /* N: must be 128                                            */
   int32_t conv_width; /* W: must be 4                                              */
-  int32_t chunk;      /* Q: prefill chunk length; 64 or 128 for bf16, 64 for f32   */
+  int32_t chunk;      /* Q: prefill chunk; 64, 128 or 256 for bf16, 64 for f32     */
   int32_t io_dtype;   /* enum mamba2_dtype                                         */
 } mamba2_dims;
 
@@ -99,9 +99,14 @@ int mamba2_conv1d(const mamba2_dims* dims, int32_t channels, const void* u, int6
 
 /*
  * mamba2_ssd_prefill_workspace_bytes -- device workspace mamba2_ssd_prefill
- * needs for `dims`. The fused scan keeps its state on chip and needs none, so
- * this returns 0 for every supported shape; it exists so that callers need not
- * change if a future variant does.
+ * needs for `dims` (0 if `dims` is invalid or the sequence is empty). The scan
+ * first computes, once per (sequence, group, chunk), the causal Gram tiles
+ * B_s . C_t of the chunk in fp32 and B^T and C laid out as MFMA operands, which
+ * every head of the group then reads, and per (sequence, head, chunk) dt and
+ * its prefix sums. With T = chunk / 32 and e = sizeof(io):
+ *   nchunks * (batch * ngroups * (4096 T(T+1)/2 + 2 * 128 * chunk * e)
+ *              + batch * nheads * 8 * chunk)            nchunks = ceil(seqlen / chunk)
+ * The caller owns it; its contents are scratch (nothing is kept between calls).
  */
 size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
 
@@ -120,8 +125,10 @@ size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
  *   h0      [B][H][N][P] f32 initial state, or NULL for zeros
  *   h_final [B][H][N][P] f32 final state, or NULL; may equal h0 (in place)
  *   y       [B][L][H*P] io, row stride y_stride; must not overlap any input
- *   workspace, workspace_bytes: at least mamba2_ssd_prefill_workspace_bytes
- *           (may be NULL when that is 0)
+ *   workspace, workspace_bytes: device scratch of at least
+ *           mamba2_ssd_prefill_workspace_bytes(dims) bytes, 16-byte aligned, not
+ *           overlapping any other argument (may be NULL when that is 0);
+ *           MAMBA2_ERR_WORKSPACE if missing or too small
  * x/B/C may be views into one xBC tensor (row stride = its channel count).
  * With seqlen 0 nothing per-token is read or written (those pointers may be
  * NULL) and h_final receives h0 (or zeros).

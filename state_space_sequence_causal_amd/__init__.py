@@ -126,6 +126,11 @@ def mamba2_ssd_prefill(x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, h_final, y, *, n
     """The chunked selective scan; x/Bm/Cm/z/y may be row-strided views (e.g. slices of xBC)."""
     B, L, H = dt_raw.shape
     d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(x))
+    if workspace is None:
+        need = lib.mamba2_ssd_prefill_workspace_bytes(ctypes.byref(d))
+        if need:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=dt_raw.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.mamba2_ssd_prefill(
         ctypes.byref(d), _ptr(x), _row_stride(x), _ptr(Bm), _row_stride(Bm), _ptr(Cm),

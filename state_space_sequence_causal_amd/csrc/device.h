@@ -51,9 +51,50 @@ template <typename T> __device__ __forceinline__ Vec<T> zero16() {
   return r;
 }
 
+// 4 io elements (8 or 16 bytes)
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
+};
+template <> struct Raw4<float> {
+  f32x4 v;
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+template <typename T> __device__ __forceinline__ Raw4<T> ld4(const T* p) {
+  Raw4<T> r;
+  r.v = *reinterpret_cast<const decltype(r.v)*>(p);
+  return r;
+}
+__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<bf16x4*>(p) = (bf16x4){(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = (f32x4){a, b, c, d};
+}
+
+// two consecutive io elements as one 32-bit (bf16) or 64-bit (f32) store
+__device__ __forceinline__ void st_pair(bf16* p, bf16 a, bf16 b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<bf16x2*>(p) = (bf16x2){a, b};
+}
+__device__ __forceinline__ void st_pair(float* p, float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<f32x2*>(p) = (f32x2){a, b};
+}
+
 // ---------------------------------------------------------------- math
+constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + expf(-v)); }
+// 2^v with the hardware exponential (v_exp_f32, about 1 ulp); used for decay factors,
+// whose arguments are <= 0.
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+// z * sigmoid(z) from the hardware exponential and reciprocal (each about 1 ulp); for
+// z -> -inf the exponential overflows to inf and the result is -0.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
 
 // ---------------------------------------------------------------- MFMA 32x32, K in steps of 16
 // An operand fragment holds, per lane, 8 values along K for one row (A) or one
@@ -104,6 +145,28 @@ __device__ __forceinline__ Frag<float> frag_accrows(const float* p, int g) {
   f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
   f32x4 b = *reinterpret_cast<const f32x4*>(p + 8 + 4 * g);
   f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+
+// frag_accrows with the two 4-element runs at independent (8- or 16-byte aligned) places
+__device__ __forceinline__ Frag<bf16> frag_accrows2(const bf16* a, const bf16* b) {
+  Frag<bf16> f;
+  bf16x4 u = *reinterpret_cast<const bf16x4*>(a);
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(b);
+  f.v = (bf16x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+  return f;
+}
+__device__ __forceinline__ Frag<float> frag_accrows2(const float* a, const float* b) {
+  Frag<float> f;
+  f32x4 u = *reinterpret_cast<const f32x4*>(a);
+  f32x4 v = *reinterpret_cast<const f32x4*>(b);
+  f.v = (f32x8){u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+  return f;
+}
+
+template <typename T> __device__ __forceinline__ Frag<T> frag_zero() {
+  Frag<T> f;
+  for (int e = 0; e < 8; ++e) f.v[e] = from_f<T>(0.f);
   return f;
 }
 

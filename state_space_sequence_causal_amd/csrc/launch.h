@@ -20,10 +20,14 @@ struct PrefillArgs {
   const void* z; int64_t z_stride;
   const float* h0; float* h_final;
   void* y; int64_t y_stride;
+  void* workspace;
   int B, L, H, G;
 };
 hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream);
-size_t ssd_prefill_lds_bytes(int io_bf16, int chunk);
+// Workspace bytes the prep/scan pair needs: per (sequence, group, chunk) the causal Gram
+// tiles in fp32 and B^T and C in MFMA operand order; per (sequence, head, chunk) dt and
+// its block prefix sums.
+size_t ssd_prefill_workspace(int io_bf16, int chunk, int B, int L, int H, int G);
 
 struct DecodeArgs {
   const void* u_t;

@@ -113,9 +113,17 @@ M2_EXPORT int mamba2_conv1d(const mamba2_dims* d, int32_t channels, const void* 
                     "conv1d launch");
 }
 
+namespace {
+bool chunk_supported(const mamba2_dims* d) {
+  return d->io_dtype == MAMBA2_BF16 ? (d->chunk == 64 || d->chunk == 128 || d->chunk == 256)
+                                    : d->chunk == 64;
+}
+}  // namespace
+
 M2_EXPORT size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
-  (void)d;
-  return 0;
+  if (check_dims(d, true) != MAMBA2_OK || !chunk_supported(d)) return 0;
+  return m2::ssd_prefill_workspace(d->io_dtype == MAMBA2_BF16, d->chunk, d->batch, d->seqlen,
+                                   d->nheads, d->ngroups);
 }
 
 M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_stride,
@@ -124,14 +132,14 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
                                  const float* A, const float* D, const void* z, int64_t z_stride,
                                  const float* h0, float* h_final, void* y, int64_t y_stride,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_dims(d, true);
   if (st) return st;
   const int io = d->io_dtype, es = esize_of(io);
-  if (io == MAMBA2_BF16 ? (d->chunk != 64 && d->chunk != 128) : d->chunk != 64)
-    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64 or 128; f32: 64)",
+  if (!chunk_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
                 d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+  const size_t ws_need = m2::ssd_prefill_workspace(io == MAMBA2_BF16, d->chunk, d->batch,
+                                                   d->seqlen, d->nheads, d->ngroups);
   if (!dt_bias || !A) return fail(MAMBA2_ERR_NULL, "dt_bias and A must not be NULL");
   if (d->seqlen > 0 && (!x || !Bm || !Cm || !dt_raw || !y))
     return fail(MAMBA2_ERR_NULL, "x, Bm, Cm, dt_raw and y must not be NULL when seqlen > 0");
@@ -144,6 +152,11 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
   if (z && (st = check_stride("z", z, z_stride, H * P, io))) return st;
   if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
     return fail(MAMBA2_ERR_ALIGN, "h0 / h_final must be 16-byte aligned");
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", ws_need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (ws_need > 0 && !aligned16(workspace))
+    return fail(MAMBA2_ERR_ALIGN, "workspace is not 16-byte aligned");
   const int64_t state_elems = (int64_t)d->batch * H * N * P;
   Range ry = span(y, BL, y_stride, H * P, es);
   Range rh0 = span(h0, 1, 0, state_elems, 4), rhf = span(h_final, 1, 0, state_elems, 4);
@@ -156,10 +169,15 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
     if (overlap(ry, r)) return fail(MAMBA2_ERR_ALIAS, "y overlaps an input or the state");
   for (int i = 0; i < 5; ++i)
     if (overlap(rhf, ins[i])) return fail(MAMBA2_ERR_ALIAS, "h_final overlaps an input");
+  Range rws = span(workspace, 1, 0, (int64_t)ws_need, 1);
+  if (overlap(rws, ry)) return fail(MAMBA2_ERR_ALIAS, "workspace overlaps y");
+  for (const Range& r : ins)
+    if (overlap(rws, r)) return fail(MAMBA2_ERR_ALIAS, "workspace overlaps an input or the state");
   if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
     return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
   m2::PrefillArgs a{x, x_stride, Bm, b_stride, Cm, c_stride, dt_raw, dt_bias, A, D,
-                    z, z_stride, h0, h_final, y, y_stride, d->batch, d->seqlen, d->nheads, d->ngroups};
+                    z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
+                    d->nheads, d->ngroups};
   return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, static_cast<hipStream_t>(stream)),
                     "ssd_prefill launch");
 }

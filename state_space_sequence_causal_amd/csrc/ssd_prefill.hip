@@ -2,36 +2,42 @@
 //
 // Computes, per sequence b and head h (group g = h / (H/G)), the recurrence
 //   h_t = exp(dt_t A) h_{t-1} + dt_t B_t x_t^T,   y_t = h_t^T C_t + D x_t,  out = y SiLU(z)
-// (Mamba-2 block of Nemotron-Nano-2: hyper.ai summary, section "方法"; fp32 state as
-// the neurohive section "Развертывание" requires), chunk by chunk. Inside a chunk of
-// Q tokens with l_t = sum_{r=c0..t} dt_r A (inclusive, relative to the chunk start):
+// (Mamba-2 block of Nemotron-Nano-2: hyper.ai summary, section "方法"; fp32 state as the
+// neurohive section "Развертывание" requires), chunk by chunk. Inside a chunk of Q
+// tokens, with l_t = sum_{r=c0..t} dt_r A:
 //   y_t   = exp(l_t) C_t . H_prev                              (state carried in)
 //         + sum_{s<=t} (C_t . B_s) exp(l_t - l_s) dt_s x_s      (causal quadratic form)
 //         + D x_t,  gated by SiLU(z_t);
 //   H_new = exp(l_end) H_prev + sum_s exp(l_end - l_s) dt_s B_s x_s^T.
 //
-// Design (one workgroup of 4 waves per (b, h), the fp32 state never leaves the chip):
-//  * The state H (N x P = 128 x 64 fp32) lives in MFMA accumulators spread over the
-//    waves; a copy H^T in LDS feeds the C.H product.
-//  * Precision: x, B, C, z, dt enter the MFMAs exactly (they are bf16 inputs). The three
-//    computed operands -- the masked decay matrix M, the state H and the decay-weighted
-//    x -- are passed as hi + lo bf16 pairs (hi = bf16(v), lo = bf16(v - hi)), i.e. two
-//    MFMAs each, which keeps them to ~2^-16 relative instead of bf16's 2^-8. With one
-//    bf16 rounding the error of outputs dominated by a single term reaches 4e-2 to
-//    2e-1 of rms(y), outside the 2e-2 bar; with the split it stays below 1e-4. The
-//    fp32 io mode uses fp32 MFMAs and needs no split.
-//  * Per chunk, B, C (Q x 128) and x (Q x 64) are staged in LDS with coalesced 16-byte
-//    loads (prefetched one chunk ahead into registers); B and x are also stored
-//    transposed so that contractions over tokens read contiguous K runs.
-//  * dt and the inclusive log-decay l are built with a wavefront shuffle scan.
-//  * Wave w owns token block w (32 tokens) of the chunk: G^T = B C^T tiles for the
-//    source blocks s <= w (MFMA), masked and scaled in registers, then used directly
-//    as the B operand of Y^T += X^T M^T (no LDS round trip), plus Y^T = H^T C^T for
-//    the carried state. Waves with light token blocks take more state tiles
-//    (H += (B^T) (w * X)), so the MFMA work per wave is balanced.
-//  * The epilogue adds D x, gates with SiLU(z) and stores y with 8/16-byte stores.
-//  * Blocks of the same group are dispatched to the same XCD so B and C chunks are
-//    shared through one L2.
+// Two kernels:
+//  * ssd_prep, one workgroup per (sequence, group, chunk). For the group it writes the
+//    Gram tiles G^T[s][t] = B_s . C_t of the causal lower triangle in fp32 (MFMA, exact
+//    products of the bf16 inputs) in MFMA accumulator order, and B^T and C in MFMA operand
+//    order, so that each wave later reads every operand as 1 KiB contiguous per
+//    instruction; these are shared by all heads of the group. For each head of the group
+//    it writes dt = softplus(dt_raw + dt_bias) and the inclusive prefix of dt*A*log2(e)
+//    inside 32-token blocks.
+//  * ssd_scan, one workgroup of 8 waves per (b, h). The fp32 state stays on chip for the
+//    whole sequence. Waves 0-3 ("Y waves") own 32-token blocks of the chunk: they build
+//    the masked decay matrix M from the Gram tiles and compute Y^T = X^T M^T + H^T C^T
+//    and the gated epilogue. Waves 4-7 ("H waves") own 32x32 tiles of the state and run
+//    H = exp(l_end) H + B^T (w x). Each SIMD hosts one wave of each kind; the state tiles
+//    are dealt so that the MFMA work per SIMD is balanced. Per chunk: stage (x, z, decay
+//    vectors) | barrier | compute | barrier | publish the new state.
+//
+// Decay factors are formed in log2 units from prefix sums taken inside 32-token blocks, so
+// no factor is the difference of two large prefix sums: inside a block exp2(pi_t - pi_s);
+// across blocks the factor splits into a per-row part F[s] and a per-column part U[t],
+// both <= 1, so off-diagonal tiles need no exponentials. D is added to the diagonal of M,
+// so the skip term D x_t comes out of the same MFMAs.
+//
+// Precision: x, B, C, z and dt enter exactly (bf16 inputs). The three computed MFMA
+// operands -- M, the state H and the decay-weighted x -- are passed as hi + lo bf16 pairs
+// (hi = bf16(v), lo = bf16(v - hi)), i.e. two MFMAs each, which keeps them to ~2^-16
+// relative. With a single bf16 rounding the error of outputs dominated by one term reaches
+// 4e-2 to 2e-1 of rms(y) on these heavy-tailed outputs, outside the 2e-2 bar; with the
+// split it stays below 1e-4. The fp32 io mode uses fp32 MFMAs and needs no split.
 #include "device.h"
 #include "launch.h"
 
@@ -39,392 +45,721 @@ namespace m2 {
 
 constexpr int SP = 64;   // head dim
 constexpr int SN = 128;  // state dim
-constexpr int SSD_THREADS = 256;
-constexpr int MAX_HT = 4;
+constexpr int PREP_THREADS = 256;
+constexpr int SCAN_THREADS = 512;
 
 template <typename T, int Q>
-struct SsdCfg {
-  static constexpr int VE = Vec<T>::VE;
-  static constexpr int PAD = VE;                        // 16 bytes per LDS row
-  static constexpr int LDN = SN + PAD;                  // rows with n contiguous
-  static constexpr int LDQ = Q + PAD;                   // rows with tokens contiguous
-  static constexpr int NTB = Q / 32;
+struct Cfg {
+  static constexpr int VE = Vec<T>::VE;        // elements per 16 bytes
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  static constexpr int NTB = Q / 32;           // 32-token blocks per chunk
+  static constexpr int NTILES = NTB * (NTB + 1) / 2;
   static constexpr int KS_N = SN / 16;
   static constexpr int KS_Q = Q / 16;
-  static constexpr int VPR_N = SN / VE;
-  static constexpr int VPR_P = SP / VE;
-  static constexpr int NVB = Q * VPR_N / SSD_THREADS;
-  static constexpr int NVX = Q * VPR_P / SSD_THREADS;
-  static_assert(Q * VPR_N % SSD_THREADS == 0 && Q * VPR_P % SSD_THREADS == 0, "tiling");
-  static_assert(Q <= 128, "one 32-token block per wave");
-  static constexpr bool SPLIT = sizeof(T) == 2;         // hi/lo operands for bf16 io
+  static constexpr int PAD = VE;
+  static constexpr int LDN = SN + PAD;         // LDS rows with n contiguous
+  static constexpr int LDQ = Q + PAD;          // LDS rows with tokens contiguous
+  static constexpr size_t FB = sizeof(Frag<T>);
+  // workspace record per (b, g, chunk): Gram tiles | B^T operand frags | C operand frags
+  static constexpr size_t G_BYTES = (size_t)NTILES * 64 * 16 * sizeof(float);
+  static constexpr size_t BT_BYTES = (size_t)(SN / 32) * KS_Q * 64 * FB;
+  static constexpr size_t CF_BYTES = (size_t)NTB * KS_N * 64 * FB;
+  static constexpr size_t REC_BYTES = G_BYTES + BT_BYTES + CF_BYTES;
+  // workspace record per (b, h, chunk): dt[Q] | pi[Q]
+  static constexpr size_t HREC_BYTES = 2 * Q * sizeof(float);
+  static constexpr int XV = Q * SP / VE / SCAN_THREADS;     // 16-byte x vectors per thread
+  static constexpr bool PAIRS = XV % 2 == 0;                // two tokens per transposed write
+  static constexpr int TPL = Q / 64;                        // decay tokens per lane (lane + 64 k)
+  static constexpr int NBD = Q == 128 ? 2 : 1;              // distinct state row blocks per H wave
+  static constexpr bool STAGE_Z = Q <= 128;                 // z / y through LDS (LDS budget)
+  static_assert(Q * SP % (VE * SCAN_THREADS) == 0, "x staging");
 };
 
+// Token position of (row p, token s) in the transposed LDS tiles x^T and (w x)^T. The
+// staging writes of a wave cover 8 rows p = 8 cv + e (cv = 0..7) with 8 consecutive token
+// pairs each; XOR-ing the token index with 16 (cv mod 8) puts the 8 rows on distinct
+// banks. Readers only touch aligned runs of 4 or 8 tokens, which the XOR keeps intact.
+template <int Q>
+__device__ __forceinline__ int xsw(int p, int s) {
+  constexpr int MASK = Q >= 128 ? 7 : Q / 16 - 1;
+  return s ^ (16 * ((p >> 3) & MASK));
+}
+
+__device__ __forceinline__ int tile_tb(int k) {  // column block of lower-triangle tile k
+  int tb = 0;
+  while ((tb + 1) * (tb + 2) / 2 <= k) ++tb;
+  return tb;
+}
+
+// frag_accrows on a swizzled row: the two 4-token runs are looked up separately.
+template <int Q, typename T>
+__device__ __forceinline__ Frag<T> frag_accrows_sw(const T* row, int p, int k0, int g) {
+  Frag<T> f;
+  const int a = xsw<Q>(p, k0 + 4 * g), b = xsw<Q>(p, k0 + 8 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = row[a + e];
+    f.v[4 + e] = row[b + e];
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_frag(void* p, const Frag<T>& f) {
+  *reinterpret_cast<decltype(f.v)*>(p) = f.v;
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> ld_frag(const void* p) {
+  Frag<T> f;
+  f.v = *reinterpret_cast<const decltype(f.v)*>(p);
+  return f;
+}
+
+// ---------------------------------------------------------------------------- prep kernel
 template <typename T, int Q>
-struct SsdSmem {
-  using C = SsdCfg<T, Q>;
-  T sB[Q][C::LDN];     // B rows (k = n)           : A operand of G^T
-  T sC[Q][C::LDN];     // C rows (k = n)           : B operand of G^T and of Y_off
-  T sBt[SN][C::LDQ];   // B^T (k = s)              : A operand of the state update
-  T sXt[SP][C::LDQ];   // x^T (k = s)              : A operand of Y_diag, B operand of the update
-  T sHt[SP][C::LDN];   // H^T of the carried state : A operand of Y_off (hi part)
-  T sHtLo[C::SPLIT ? SP : 1][C::LDN];  // lo part of H^T (bf16 io only)
-  float sL[Q];         // inclusive log-decay
-  float sDt[Q];        // dt
-  float sW[Q];         // exp(l_end - l_s) dt_s
-  float sPart[Q];      // per-wave partial scans
-};
+__global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
+    const T* __restrict__ Bm, int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
+    const T* __restrict__ dt_raw, const float* __restrict__ dt_bias, const float* __restrict__ A,
+    unsigned char* __restrict__ ws, int L, int H, int G, int nC) {
+  using C = Cfg<T, Q>;
+  constexpr int VE = C::VE;
+  extern __shared__ __align__(16) unsigned char prep_smem[];
+  T (*sB)[C::LDN] = reinterpret_cast<T (*)[C::LDN]>(prep_smem);
+  T (*sC)[C::LDN] = reinterpret_cast<T (*)[C::LDN]>(prep_smem + sizeof(T) * Q * C::LDN);
 
-// State tiles (32 x 32 of H[n][p]) each wave updates, balanced against the token-block
-// work of wave w. At Q = 128 with split operands, in 32x32x16 MFMA units: token block w
-// costs 16 (w+1) + 32 (G^T, Y_diag, Y_off) and a state tile 16, so waves get 4, 3, 1, 0
-// tiles: 112, 112, 96, 96.
-struct HTiles { int n; int nb[MAX_HT]; int pb[MAX_HT]; };
-template <int Q> __device__ __forceinline__ HTiles htiles(int w);
-template <> __device__ __forceinline__ HTiles htiles<128>(int w) {
-  switch (w) {
-    case 0: return {4, {0, 0, 1, 1}, {0, 1, 0, 1}};
-    case 1: return {3, {2, 2, 3, 0}, {0, 1, 0, 0}};
-    case 2: return {1, {3, 0, 0, 0}, {1, 0, 0, 0}};
-    default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  const int rec = blockIdx.x;
+  const int c = rec % nC, bg = rec / nC, g = bg % G, b = bg / G;
+  const int t0 = c * Q;
+  const int64_t row0 = (int64_t)b * L + t0;
+  const T* Bb = Bm + row0 * b_stride + g * SN;
+  const T* Cb = Cm + row0 * c_stride + g * SN;
+  unsigned char* recp = ws + (size_t)rec * C::REC_BYTES;
+  float* gout = reinterpret_cast<float*>(recp);
+  unsigned char* btf = recp + C::G_BYTES;
+  unsigned char* cff = btf + C::BT_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, g2 = lane >> 5;
+  const int nvalid = min(Q, L - t0);
+
+  // B and C rows of the chunk into LDS (zero past the end of the sequence)
+  for (int v = tid; v < Q * SN / VE; v += PREP_THREADS) {
+    int s = v / (SN / VE), cv = v % (SN / VE);
+    bool ok = s < nvalid;
+    st16(&sB[s][cv * VE], ok ? ld16(Bb + (int64_t)s * b_stride + cv * VE) : zero16<T>());
+    st16(&sC[s][cv * VE], ok ? ld16(Cb + (int64_t)s * c_stride + cv * VE) : zero16<T>());
+  }
+  // per head of the group: dt and the 32-token block prefix of dt*A*log2(e)
+  {
+    const int hpg = H / G;
+    const size_t hrec0 = (size_t)b * H * nC;
+    unsigned char* hbase = ws + (size_t)gridDim.x * C::REC_BYTES;
+    for (int item = wave; item < hpg * C::TPL; item += PREP_THREADS / 64) {
+      const int j = item / C::TPL, k = item % C::TPL;
+      const int h = g * hpg + j;
+      const int s = 64 * k + lane;
+      float dt = 0.f;
+      if (s < nvalid) dt = softplus_f(to_f(dt_raw[(row0 + s) * H + h]) + dt_bias[h]);
+      float run = dt * A[h] * kLog2e;
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) {
+        float o = __shfl_up(run, d, 32);
+        if ((lane & 31) >= d) run += o;
+      }
+      float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
+      hr[s] = dt;
+      hr[Q + s] = run;
+    }
+  }
+  __syncthreads();
+  // Gram tiles: wave w computes lower-triangle tiles k = w, w+4, ...
+  for (int k = wave; k < C::NTILES; k += 4) {
+    const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
+    f32x16 acc = (f32x16){};
+#pragma unroll
+    for (int j = 0; j < C::KS_N; ++j)
+      mma(acc, frag_contig(&sB[si * 32 + col][16 * j], g2), frag_contig(&sC[tb * 32 + col][16 * j], g2));
+    float* dst = gout + ((size_t)k * 64 + lane) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(dst + 4 * q) =
+          (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+  }
+  // B^T operand frags (row n = nb*32 + col, k = s): record (nb, j), lane
+  for (int idx = tid; idx < (SN / 32) * C::KS_Q * 64; idx += PREP_THREADS) {
+    const int r = idx >> 6, ln = idx & 63;
+    const int nb = r / C::KS_Q, j = r % C::KS_Q;
+    const int n = nb * 32 + (ln & 31), s0 = 16 * j + 8 * (ln >> 5);
+    Frag<T> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = sB[s0 + e][n];
+    st_frag<T>(btf + (size_t)idx * C::FB, f);
+  }
+  // C operand frags (col t = tb*32 + col, k = n): record (tb, j), lane
+  for (int idx = tid; idx < C::NTB * C::KS_N * 64; idx += PREP_THREADS) {
+    const int r = idx >> 6, ln = idx & 63;
+    const int tb = r / C::KS_N, j = r % C::KS_N;
+    st_frag<T>(cff + (size_t)idx * C::FB, frag_contig(&sC[tb * 32 + (ln & 31)][16 * j], ln >> 5));
   }
 }
-template <> __device__ __forceinline__ HTiles htiles<64>(int w) {
-  switch (w) {
-    case 2: return {4, {0, 0, 1, 1}, {0, 1, 0, 1}};
-    case 3: return {4, {2, 2, 3, 3}, {0, 1, 0, 1}};
-    default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
+
+// ---------------------------------------------------------------------------- scan kernel
+template <typename T, int Q>
+struct ScanSmem {
+  using C = Cfg<T, Q>;
+  T sXt[SP][C::LDQ];                       // x^T (k = s): A operand of Y_diag
+  T sXW[SP][C::LDQ];                       // (w x)^T hi: B operand of the state update
+  T sXWlo[C::SPLIT ? SP : 1][C::LDQ];      //        lo
+  T sHt[SP][C::LDN];                       // H^T hi: A operand of Y_off
+  T sHtlo[C::SPLIT ? SP : 1][C::LDN];      //     lo
+  float sG[C::STAGE_Z ? Q : 1][SP + 4];    // SiLU(z) of the chunk in fp32, then y (fp32)
+  float sPi[Q];                            // inclusive prefix of dt*A*log2e inside 32-token blocks
+  float sDt[Q];
+  float sE[Q];                             // exp2(lambda_t), lambda from the chunk start
+  float sF[C::NTB][Q];                     // sF[tb][s] = exp2(lambda_{32tb-1} - lambda_s) dt_s, s < 32 tb
+};
+
+// State tiles (32x32 of H[n][p], nb = n / 32, pb = p / 32) updated by H wave hw, dealt so
+// that each SIMD (one Y wave + one H wave) gets about the same number of MFMAs. slot[i]
+// indexes the distinct row blocks nbs[] whose B^T operands the wave keeps in registers.
+struct HList { int n; int nb[4]; int pb[4]; int slot[4]; int nbs[2]; };
+template <int Q> __device__ __forceinline__ HList hlist(int hw);
+template <> __device__ __forceinline__ HList hlist<64>(int hw) {
+  return {2, {hw, hw, 0, 0}, {0, 1, 0, 0}, {0, 0, 0, 0}, {hw, hw}};
+}
+template <> __device__ __forceinline__ HList hlist<128>(int hw) {
+  switch (hw) {
+    case 0: return {3, {0, 0, 1, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 1}};
+    case 1: return {2, {1, 2, 0, 0}, {1, 0, 0, 0}, {0, 1, 0, 0}, {1, 2}};
+    case 2: return {2, {2, 3, 0, 0}, {1, 0, 0, 0}, {0, 1, 0, 0}, {2, 3}};
+    default: return {1, {3, 0, 0, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}, {3, 3}};
   }
 }
+template <> __device__ __forceinline__ HList hlist<256>(int hw) {
+  return {2, {hw, hw, 0, 0}, {0, 1, 0, 0}, {0, 0, 0, 0}, {hw, hw}};
+}
+// Token blocks and p-blocks owned by Y wave y: Q=64: one (tb, pb) each; Q=128: block y,
+// both p-blocks; Q=256: blocks y and 7-y (light + heavy), both p-blocks.
+template <int Q> struct YPlan;
+template <> struct YPlan<64> {
+  static constexpr int NT = 1, NPB = 1;
+  __device__ static int tb(int y, int) { return y & 1; }
+  __device__ static int pb(int y, int) { return y >> 1; }
+};
+template <> struct YPlan<128> {
+  static constexpr int NT = 1, NPB = 2;
+  __device__ static int tb(int y, int) { return y; }
+  __device__ static int pb(int, int i) { return i; }
+};
+template <> struct YPlan<256> {
+  static constexpr int NT = 2, NPB = 2;
+  __device__ static int tb(int y, int k) { return k == 0 ? y : 7 - y; }
+  __device__ static int pb(int, int i) { return i; }
+};
 
-template <typename T> struct Raw4;
-template <> struct Raw4<bf16> {
-  bf16x4 v;
-  __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
-};
-template <> struct Raw4<float> {
-  f32x4 v;
-  __device__ __forceinline__ float get(int i) const { return v[i]; }
-};
-template <typename T> __device__ __forceinline__ Raw4<T> ld4(const T* p) {
-  Raw4<T> r;
-  r.v = *reinterpret_cast<const decltype(r.v)*>(p);
+template <typename T>
+__device__ __forceinline__ void split_set(Frag<T>& hi, Frag<T>& lo, int e, float v) {
+  frag_set<T>(hi, e, v);
+  if constexpr (sizeof(T) == 2) frag_set<T>(lo, e, v - frag_get(hi, e));
+}
+
+__device__ __forceinline__ f32x16 load_tile16(const float* src) {
+  f32x16 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
+    r[4 * q] = v[0];
+    r[4 * q + 1] = v[1];
+    r[4 * q + 2] = v[2];
+    r[4 * q + 3] = v[3];
+  }
   return r;
 }
-__device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
-  *reinterpret_cast<bf16x4*>(p) = (bf16x4){(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-}
-__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = (f32x4){a, b, c, d};
-}
 
 template <typename T, int Q>
-__global__ __launch_bounds__(SSD_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ssd_prefill_kernel(const T* __restrict__ x, int64_t x_stride, const T* __restrict__ Bm,
-                        int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
-                        const T* __restrict__ dt_raw, const float* __restrict__ dt_bias,
-                        const float* __restrict__ A, const float* __restrict__ D,
-                        const T* __restrict__ z, int64_t z_stride, const float* h0,
-                        float* h_final, T* __restrict__ y, int64_t y_stride, int L, int H, int G) {
-  using C = SsdCfg<T, Q>;
+__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
+                     const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
+                     T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
+                     int L, int H, int G) {
+  using C = Cfg<T, Q>;
+  using YP = YPlan<Q>;
   constexpr int VE = C::VE;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  SsdSmem<T, Q>& S = *reinterpret_cast<SsdSmem<T, Q>*>(smem_raw);
+  extern __shared__ __align__(16) unsigned char scan_smem[];
+  ScanSmem<T, Q>& S = *reinterpret_cast<ScanSmem<T, Q>*>(scan_smem);
 
   const int id = xcd_local_order(blockIdx.x, gridDim.x);
   const int b = id / H, h = id % H;
   const int g = h / (H / G);
+  const int nC = (L + Q - 1) / Q;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g2 = lane >> 5;
+  const bool ywave = wave < 4;
+  const int hw = ywave ? 0 : wave - 4;
 
   const int64_t row0 = (int64_t)b * L;
   const T* xb = x + h * SP;
-  const T* Bb = Bm + g * SN;
-  const T* Cb = Cm + g * SN;
-  const float Ah = A[h], dtb = dt_bias[h], Dh = D ? D[h] : 0.f;
-  const int nC = (L + Q - 1) / Q;
+  const T* zb = z ? z + h * SP : nullptr;
+  T* yb = y + h * SP;
+  const float Dh = D ? D[h] : 0.f;
+  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
+  const float* hrec = reinterpret_cast<const float*>(
+      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
+      ((size_t)b * H + h) * nC * C::HREC_BYTES);
 
-  // ---------------------------------------------------------------- prefetch registers
-  Vec<T> rB[C::NVB], rC[C::NVB], rX[C::NVX];
-  float rdt = 0.f;
-  bool rdt_ok = false;
+  // ------------------------------------------------------------ staging registers
+  // x: XV 16-byte vectors per thread. With PAIRS, vectors 2i and 2i+1 are tokens 2sp and
+  // 2sp+1 of one 16-byte column, 8 lanes per token row (coalesced loads), so x^T and
+  // (w x)^T go to LDS as 32-bit token pairs. z: the same row-major mapping, 16-byte
+  // vectors straight into sZ.
+  Vec<T> rX[C::XV], rZ[C::XV];
+  float rdt[C::TPL], rpi[C::TPL];
+  auto xcoord = [&](int i, int& s, int& cv) {
+    constexpr int VPR = SP / VE;  // vectors per token row
+    if constexpr (C::PAIRS) {
+      const int u = tid + SCAN_THREADS * (i >> 1);
+      s = 2 * (u / VPR) + (i & 1);
+      cv = u % VPR;
+    } else {
+      const int v = tid + SCAN_THREADS * i;
+      s = v / VPR;
+      cv = v % VPR;
+    }
+  };
   auto load_chunk = [&](int c) {
     const int t0 = c * Q;
 #pragma unroll
-    for (int i = 0; i < C::NVB; ++i) {
-      int v = tid + SSD_THREADS * i, s = v / C::VPR_N, cv = v % C::VPR_N;
-      int t = t0 + s;
-      if (t < L) {
-        rB[i] = ld16(Bb + (row0 + t) * b_stride + cv * VE);
-        rC[i] = ld16(Cb + (row0 + t) * c_stride + cv * VE);
-      } else {
-        rB[i] = zero16<T>();
-        rC[i] = zero16<T>();
+    for (int i = 0; i < C::XV; ++i) {
+      int s_, cv;
+      xcoord(i, s_, cv);
+      const int t = t0 + s_;
+      const bool ok = t < L;
+      rX[i] = ok ? ld16(xb + (row0 + t) * x_stride + cv * VE) : zero16<T>();
+      if constexpr (C::STAGE_Z) {
+        if (zb) rZ[i] = ok ? ld16(zb + (row0 + t) * z_stride + cv * VE) : zero16<T>();
       }
     }
+    const float* hr = hrec + (size_t)c * (2 * Q);
 #pragma unroll
-    for (int i = 0; i < C::NVX; ++i) {
-      int v = tid + SSD_THREADS * i, s = v / C::VPR_P, cv = v % C::VPR_P;
-      int t = t0 + s;
-      rX[i] = t < L ? ld16(xb + (row0 + t) * x_stride + cv * VE) : zero16<T>();
-    }
-    if (tid < Q) {
-      int t = t0 + tid;
-      rdt_ok = t < L;
-      rdt = rdt_ok ? to_f(dt_raw[(row0 + t) * H + h]) : 0.f;
+    for (int k = 0; k < C::TPL; ++k) {
+      rdt[k] = hr[lane + 64 * k];
+      rpi[k] = hr[Q + lane + 64 * k];
     }
   };
 
-  // ---------------------------------------------------------------- state init
-  const HTiles ht = htiles<Q>(wave);
-  f32x16 hacc[MAX_HT];
-  const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
+  // ------------------------------------------------------------ chunk phase S1
+  // y of the previous chunk out of sZ (coalesced), z of this chunk in; decay vectors
+  // (every wave derives them, so staging threads get w_s by a cross-lane shuffle); x^T and
+  // (w x)^T into LDS; prefetch of the next chunk.
+  auto phase_s1 = [&](int c) {
+    if constexpr (C::STAGE_Z) {
 #pragma unroll
-  for (int i = 0; i < MAX_HT; ++i) {
-    if (i < ht.n) {
+      for (int i = 0; i < C::XV; ++i) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        float* grow = &S.sG[s_][cv * VE];
+        if (c > 0) {
+          const int t = (c - 1) * Q + s_;
+          if (t < L) {
+            Vec<T> o;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int n = ht.nb[i] * 32 + acc_row(r, lane), p = ht.pb[i] * 32 + col;
-        hacc[i][r] = h0 ? h0[sbase + n * SP + p] : 0.f;
-      }
-    }
-  }
-  auto write_state_lds = [&]() {
-#pragma unroll
-    for (int i = 0; i < MAX_HT; ++i) {
-      if (i < ht.n) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          int n = ht.nb[i] * 32 + 8 * r4 + 4 * g2, p = ht.pb[i] * 32 + col;
-          float v[4], lo[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k] = hacc[i][4 * r4 + k];
-            lo[k] = v[k] - to_f(from_f<T>(v[k]));
+            for (int e = 0; e < VE; ++e) o.set(e, grow[e]);
+            st16(yb + (row0 + t) * y_stride + cv * VE, o);
           }
-          st4(&S.sHt[p][n], v[0], v[1], v[2], v[3]);
-          if constexpr (C::SPLIT) st4(&S.sHtLo[p][n], lo[0], lo[1], lo[2], lo[3]);
+        }
+        if (zb) {
+#pragma unroll
+          for (int e = 0; e < VE; e += 4)
+            *reinterpret_cast<f32x4*>(grow + e) =
+                (f32x4){silu_fast(rZ[i].get(e)), silu_fast(rZ[i].get(e + 1)),
+                        silu_fast(rZ[i].get(e + 2)), silu_fast(rZ[i].get(e + 3))};
         }
       }
     }
-  };
-
-  if (nC > 0) load_chunk(0);
-  write_state_lds();
-
-  const int tb = wave < C::NTB ? wave : -1;  // token block owned by this wave
-
-  for (int c = 0; c < nC; ++c) {
-    const int t0 = c * Q;
-    // ------------------------------------------------------------ stage chunk c
+    float tot[C::NTB];
 #pragma unroll
-    for (int i = 0; i < C::NVB; ++i) {
-      int v = tid + SSD_THREADS * i, s = v / C::VPR_N, cv = v % C::VPR_N;
-      st16(&S.sB[s][cv * VE], rB[i]);
-      st16(&S.sC[s][cv * VE], rC[i]);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) S.sBt[cv * VE + e][s] = rB[i].v[e];
+    for (int k = 0; k < C::TPL; ++k) {
+      tot[2 * k] = __shfl(rpi[k], 31);
+      tot[2 * k + 1] = __shfl(rpi[k], 63);
     }
+    float wv[C::TPL];
 #pragma unroll
-    for (int i = 0; i < C::NVX; ++i) {
-      int v = tid + SSD_THREADS * i, s = v / C::VPR_P, cv = v % C::VPR_P;
+    for (int k = 0; k < C::TPL; ++k) {
+      const int blk = 2 * k + (lane >> 5);
+      float before = 0.f, after = 0.f;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) S.sXt[cv * VE + e][s] = rX[i].v[e];
-    }
-    if (tid < Q) {
-      float dt = rdt_ok ? softplus_f(rdt + dtb) : 0.f;
-      float run = dt * Ah;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        float o = __shfl_up(run, d);
-        if (lane >= d) run += o;
+      for (int bb = 0; bb < C::NTB; ++bb) {
+        if (bb < blk) before += tot[bb];
+        if (bb > blk) after += tot[bb];
       }
-      S.sPart[tid] = run;
-      S.sDt[tid] = dt;
+      const float tail = tot[blk] - rpi[k];  // lambda_{end of blk} - lambda_t
+      wv[k] = exp2_hw(tail + after) * rdt[k];
+      if (wave == 0) {
+        const int t = lane + 64 * k;
+        S.sPi[t] = rpi[k];
+        S.sDt[t] = rdt[k];
+        S.sE[t] = exp2_hw(before + rpi[k]);
+        float acc = tail;
+#pragma unroll
+        for (int tb = 1; tb < C::NTB; ++tb) {
+          if (tb > blk) {
+            S.sF[tb][t] = exp2_hw(acc) * rdt[k];
+            acc += tot[tb];
+          }
+        }
+      }
+    }
+    // w of token s lives in lane s % 64, register s / 64
+    auto w_of = [&](int s_) {
+      float r = 0.f;
+#pragma unroll
+      for (int k = 0; k < C::TPL; ++k) {
+        const float o = __shfl(wv[k], s_ & 63);
+        if ((s_ >> 6) == k) r = o;
+      }
+      return r;
+    };
+    if constexpr (C::PAIRS) {
+#pragma unroll
+      for (int i = 0; i < C::XV; i += 2) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        const float w0 = w_of(s_), w1 = w_of(s_ + 1);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const T x0 = rX[i].v[e], x1 = rX[i + 1].v[e];
+          const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
+          const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
+          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
+          st_pair(&S.sXt[p][sw], x0, x1);
+          st_pair(&S.sXW[p][sw], h0_, h1_);
+          if constexpr (C::SPLIT)
+            st_pair(&S.sXWlo[p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::XV; ++i) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        const float w0 = w_of(s_);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const T x0 = rX[i].v[e];
+          const float v0 = to_f(x0) * w0;
+          const T h0_ = from_f<T>(v0);
+          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
+          S.sXt[p][sw] = x0;
+          S.sXW[p][sw] = h0_;
+          if constexpr (C::SPLIT) S.sXWlo[p][sw] = from_f<T>(v0 - to_f(h0_));
+        }
+      }
     }
     if (c + 1 < nC) load_chunk(c + 1);
-    __syncthreads();
-    if (tid < Q) {
-      float off = 0.f, tot = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < (Q + 63) / 64; ++w2) {
-        float pw = S.sPart[min(64 * w2 + 63, Q - 1)];
-        if (w2 < (tid >> 6)) off += pw;
-        tot += pw;
-      }
-      float l = S.sPart[tid] + off;
-      S.sL[tid] = l;
-      S.sW[tid] = expf(tot - l) * S.sDt[tid];
-    }
-    __syncthreads();
+  };
 
-    // ------------------------------------------------------------ token block: y
-    if (tb >= 0) {
-      const int tl = tb * 32 + col;  // lane's token within the chunk
-      const int t = t0 + tl;
-      const bool tvalid = t < L;
-      // epilogue operands, fetched early (L2-resident: x was just staged)
-      Raw4<T> xe[2][4], ze[2][4];
+  // The two roles run separate chunk loops with the same barrier sequence (two barriers
+  // per chunk), so each role's registers are allocated on their own.
+  if (ywave) {
+    // ========================================================== Y waves: outputs
+    Frag<T> cf[C::KS_N];                // C operand frags of the token block
+    f32x16 gq0, gq1;                    // Gram tiles, fetched two ahead
+    Raw4<T> ze[YP::NPB][4];             // z when it is not staged through LDS
+    auto yfetch = [&](int c, int tb) {
+      const unsigned char* rec = wsg + (size_t)c * C::REC_BYTES;
+      const unsigned char* cfp = rec + C::G_BYTES + C::BT_BYTES;
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
+      for (int j = 0; j < C::KS_N; ++j)
+        cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
+      const float* gt = reinterpret_cast<const float*>(rec);
+      const int k0 = tb * (tb + 1) / 2;
+      gq0 = load_tile16(gt + ((size_t)k0 * 64 + lane) * 16);
+      if (tb > 0) gq1 = load_tile16(gt + ((size_t)(k0 + 1) * 64 + lane) * 16);
+      if constexpr (!C::STAGE_Z) {
+        const int t = c * Q + tb * 32 + col;
+        if (zb && t < L) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          int p0 = pb * 32 + 8 * r4 + 4 * g2;
-          if (tvalid) {
-            xe[pb][r4] = ld4(xb + (row0 + t) * x_stride + p0);
-            if (z) ze[pb][r4] = ld4(z + (row0 + t) * z_stride + h * SP + p0);
-          }
-        }
-      Frag<T> cf[C::KS_N];
+          for (int i = 0; i < YP::NPB; ++i)
 #pragma unroll
-      for (int j = 0; j < C::KS_N; ++j) cf[j] = frag_contig(&S.sC[tl][16 * j], g2);
-      const float lt = S.sL[tl];
-
-      f32x16 yacc[2];
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        yacc[pb] = (f32x16){};
-#pragma unroll
-        for (int j = 0; j < C::KS_N; ++j) {
-          mma(yacc[pb], frag_contig(&S.sHt[pb * 32 + col][16 * j], g2), cf[j]);
-          if constexpr (C::SPLIT) mma(yacc[pb], frag_contig(&S.sHtLo[pb * 32 + col][16 * j], g2), cf[j]);
+            for (int r4 = 0; r4 < 4; ++r4)
+              ze[i][r4] = ld4(zb + (row0 + t) * z_stride + YP::pb(wave, i) * 32 + 8 * r4 + 4 * g2);
         }
       }
-      const float elt = expf(lt);
+    };
+    if (nC > 0) load_chunk(0);
+    for (int c = 0; c < nC; ++c) {
+      const int t0 = c * Q;
+      const float* gt = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES);
+      yfetch(c, YP::tb(wave, 0));
+      phase_s1(c);
+      __syncthreads();
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
+      for (int k = 0; k < YP::NT; ++k) {
+        const int tb = YP::tb(wave, k);
+        if (k > 0) yfetch(c, tb);
+        const int tl = tb * 32 + col;
+        const int t = t0 + tl;
+        f32x16 yoff[YP::NPB], yd[YP::NPB];
+        // carried state: Y^T = H^T C^T (scaled by exp2(lambda_t) in the epilogue)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) yacc[pb][r] *= elt;
-
-      for (int si = 0; si <= tb; ++si) {
-        f32x16 gacc = (f32x16){};
+        for (int i = 0; i < YP::NPB; ++i) {
+          const int prow = YP::pb(wave, i) * 32 + col;
+          yoff[i] = (f32x16){};
+          yd[i] = (f32x16){};
 #pragma unroll
-        for (int j = 0; j < C::KS_N; ++j)
-          mma(gacc, frag_contig(&S.sB[si * 32 + col][16 * j], g2), cf[j]);
-        Frag<T> mf[2], mlo[2];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int s0 = si * 32 + 8 * r4 + 4 * g2;
-          const f32x4 ls = *reinterpret_cast<const f32x4*>(&S.sL[s0]);
-          const f32x4 ds = *reinterpret_cast<const f32x4*>(&S.sDt[s0]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * r4 + i;
-            float v = (s0 + i <= tl) ? gacc[r] * expf(lt - ls[i]) * ds[i] : 0.f;
-            frag_set<T>(mf[r >> 3], r & 7, v);
-            if constexpr (C::SPLIT) frag_set<T>(mlo[r >> 3], r & 7, v - frag_get(mf[r >> 3], r & 7));
+          for (int j = 0; j < C::KS_N; ++j) {
+            mma(yoff[i], frag_contig(&S.sHt[prow][16 * j], g2), cf[j]);
+            if constexpr (C::SPLIT) mma(yoff[i], frag_contig(&S.sHtlo[prow][16 * j], g2), cf[j]);
           }
         }
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-          for (int pb = 0; pb < 2; ++pb) {
-            Frag<T> xa = frag_accrows(&S.sXt[pb * 32 + col][si * 32 + 16 * m2], g2);
-            mma(yacc[pb], xa, mf[m2]);
-            if constexpr (C::SPLIT) mma(yacc[pb], xa, mlo[m2]);
-          }
-      }
-
-      if (tvalid) {
-#pragma unroll
-        for (int pb = 0; pb < 2; ++pb)
+        // off-diagonal source blocks si < tb: M = G * F[s]; the column factor U[t] after
+        const int k0 = tb * (tb + 1) / 2;
+        for (int si = 0; si < tb; ++si) {
+          const f32x16 gcur = gq0;
+          gq0 = gq1;
+          if (si + 2 <= tb) gq1 = load_tile16(gt + ((size_t)(k0 + si + 2) * 64 + lane) * 16);
+          Frag<T> mh[2], ml[2];
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            int p0 = pb * 32 + 8 * r4 + 4 * g2;
-            float o[4];
+            const f32x4 fs = *reinterpret_cast<const f32x4*>(&S.sF[tb][si * 32 + 8 * r4 + 4 * g2]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v = yacc[pb][4 * r4 + i] + Dh * xe[pb][r4].get(i);
-              if (z) v *= silu_f(ze[pb][r4].get(i));
-              o[i] = v;
+            for (int q = 0; q < 4; ++q) {
+              const int r = 4 * r4 + q;
+              split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gcur[r] * fs[q]);
             }
-            st4(y + (row0 + t) * y_stride + h * SP + p0, o[0], o[1], o[2], o[3]);
+          }
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < YP::NPB; ++i) {
+              const int prow = YP::pb(wave, i) * 32 + col;
+              Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, si * 32 + 16 * m2, g2);
+              mma(yd[i], xa, mh[m2]);
+              if constexpr (C::SPLIT) mma(yd[i], xa, ml[m2]);
+            }
+        }
+        const float pit = S.sPi[tl];
+        if (tb > 0) {
+          const float ut = exp2_hw(pit);  // exp2(lambda_t - lambda_{32tb-1})
+#pragma unroll
+          for (int i = 0; i < YP::NPB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yd[i][r] *= ut;
+        }
+        // diagonal block: exp2(pi_t - pi_s) dt_s for s <= t, plus D on the diagonal (the
+        // skip term); its Gram tile is in gq0
+        {
+          Frag<T> mh[2], ml[2];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int s0 = tb * 32 + 8 * r4 + 4 * g2;
+            const f32x4 ps = *reinterpret_cast<const f32x4*>(&S.sPi[s0]);
+            const f32x4 ds = *reinterpret_cast<const f32x4*>(&S.sDt[s0]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 4 * r4 + q;
+              float v = (s0 + q <= tl) ? gq0[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+              if (s0 + q == tl) v += Dh;
+              split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
+            }
+          }
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int i = 0; i < YP::NPB; ++i) {
+              const int prow = YP::pb(wave, i) * 32 + col;
+              Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, tb * 32 + 16 * m2, g2);
+              mma(yd[i], xa, mh[m2]);
+              if constexpr (C::SPLIT) mma(yd[i], xa, ml[m2]);
+            }
+        }
+        // epilogue: y = (E_t Y_off + Y_diag) SiLU(z)
+        const float et = S.sE[tl];
+#pragma unroll
+        for (int i = 0; i < YP::NPB; ++i)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int p0 = YP::pb(wave, i) * 32 + 8 * r4 + 4 * g2;
+            float o[4];
+            if constexpr (C::STAGE_Z) {
+              f32x4 gg = {1.f, 1.f, 1.f, 1.f};
+              if (zb) gg = *reinterpret_cast<const f32x4*>(&S.sG[tl][p0]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) o[q] = (et * yoff[i][4 * r4 + q] + yd[i][4 * r4 + q]) * gg[q];
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float v = et * yoff[i][4 * r4 + q] + yd[i][4 * r4 + q];
+                if (zb) v *= silu_fast(ze[i][r4].get(q));
+                o[q] = v;
+              }
+            }
+            if constexpr (C::STAGE_Z) {
+              *reinterpret_cast<f32x4*>(&S.sG[tl][p0]) = (f32x4){o[0], o[1], o[2], o[3]};
+            } else {
+              if (t < L) st4(yb + (row0 + t) * y_stride + p0, o[0], o[1], o[2], o[3]);
+            }
           }
       }
+      __syncthreads();
     }
-
-    // ------------------------------------------------------------ state update
-    if (ht.n > 0) {
-      const float eend = expf(S.sL[Q - 1]);
+  } else {
+    // ========================================================== H waves: state
+    const HList hl = hlist<Q>(hw);
+    f32x16 hacc[4];
+    Frag<T> af[C::NBD][C::KS_Q];        // B^T operand frags of the chunk
+    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
 #pragma unroll
-      for (int i = 0; i < MAX_HT; ++i)
-        if (i < ht.n)
+    for (int i = 0; i < 4; ++i)
+      if (i < hl.n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int n = hl.nb[i] * 32 + acc_row(r, lane), p = hl.pb[i] * 32 + col;
+          hacc[i][r] = h0 ? h0[sbase + n * SP + p] : 0.f;
+        }
+      }
+    auto write_state = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < hl.n) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            int n = hl.nb[i] * 32 + 8 * r4 + 4 * g2, p = hl.pb[i] * 32 + col;
+            float v[4], lo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[k] = hacc[i][4 * r4 + k];
+              lo[k] = v[k] - to_f(from_f<T>(v[k]));
+            }
+            st4(&S.sHt[p][n], v[0], v[1], v[2], v[3]);
+            if constexpr (C::SPLIT) st4(&S.sHtlo[p][n], lo[0], lo[1], lo[2], lo[3]);
+          }
+        }
+    };
+    write_state();
+    if (nC > 0) load_chunk(0);
+    for (int c = 0; c < nC; ++c) {
+      const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
+#pragma unroll
+      for (int d = 0; d < C::NBD; ++d)
+#pragma unroll
+        for (int j = 0; j < C::KS_Q; ++j)
+          af[d][j] = ld_frag<T>(btf + ((size_t)(hl.nbs[d] * C::KS_Q + j) * 64 + lane) * C::FB);
+      phase_s1(c);
+      __syncthreads();
+      const float eend = S.sE[Q - 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < hl.n)
 #pragma unroll
           for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-        bool any = false;
+      for (int j = 0; j < C::KS_Q; ++j) {
+        Frag<T> bh[2], bl[2];
 #pragma unroll
-        for (int i = 0; i < MAX_HT; ++i) any |= (i < ht.n && ht.pb[i] == pb);
-        if (!any) continue;
-#pragma unroll 2
-        for (int j = 0; j < C::KS_Q; ++j) {
-          Frag<T> xw = frag_contig(&S.sXt[pb * 32 + col][16 * j], g2), xlo;
-          const f32x4 w0 = *reinterpret_cast<const f32x4*>(&S.sW[16 * j + 8 * g2]);
-          const f32x4 w1 = *reinterpret_cast<const f32x4*>(&S.sW[16 * j + 8 * g2 + 4]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float v = frag_get(xw, e) * (e < 4 ? w0[e] : w1[e - 4]);
-            frag_set<T>(xw, e, v);
-            if constexpr (C::SPLIT) frag_set<T>(xlo, e, v - frag_get(xw, e));
-          }
-#pragma unroll
-          for (int i = 0; i < MAX_HT; ++i)
-            if (i < ht.n && ht.pb[i] == pb) {
-              Frag<T> ba = frag_contig(&S.sBt[ht.nb[i] * 32 + col][16 * j], g2);
-              mma(hacc[i], ba, xw);
-              if constexpr (C::SPLIT) mma(hacc[i], ba, xlo);
-            }
+        for (int pb = 0; pb < 2; ++pb) {
+          const int prow = pb * 32 + col, k0 = xsw<Q>(prow, 16 * j + 8 * g2);
+          bh[pb] = frag_contig(&S.sXW[prow][k0], 0);
+          if constexpr (C::SPLIT) bl[pb] = frag_contig(&S.sXWlo[prow][k0], 0);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < hl.n) {
+            const Frag<T>& a = (C::NBD > 1 && hl.slot[i]) ? af[C::NBD - 1][j] : af[0][j];
+            mma(hacc[i], a, hl.pb[i] ? bh[1] : bh[0]);
+            if constexpr (C::SPLIT) mma(hacc[i], a, hl.pb[i] ? bl[1] : bl[0]);
+          }
       }
+      __syncthreads();
+      write_state();
     }
-    __syncthreads();
-    write_state_lds();
+    if (h_final) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < hl.n) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int n = hl.nb[i] * 32 + acc_row(r, lane), p = hl.pb[i] * 32 + col;
+            h_final[sbase + n * SP + p] = hacc[i][r];
+          }
+        }
+    }
   }
 
-  if (h_final) {
+  // y of the last chunk out of sZ
+  if constexpr (C::STAGE_Z) {
+    if (nC > 0) {
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MAX_HT; ++i) {
-      if (i < ht.n) {
+      for (int i = 0; i < C::XV; ++i) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        const int t = (nC - 1) * Q + s_;
+        if (t < L) {
+          Vec<T> o;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int n = ht.nb[i] * 32 + acc_row(r, lane), p = ht.pb[i] * 32 + col;
-          h_final[sbase + n * SP + p] = hacc[i][r];
+          for (int e = 0; e < VE; ++e) o.set(e, S.sG[s_][cv * VE + e]);
+          st16(yb + (row0 + t) * y_stride + cv * VE, o);
         }
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------- host side
+static hipError_t set_lds(const void* fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 template <typename T, int Q>
 static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(SsdSmem<T, Q>);
+  using C = Cfg<T, Q>;
+  const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
+  const size_t scan_lds = sizeof(ScanSmem<T, Q>);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ssd_prefill_kernel<T, Q>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q>), prep_lds);
+    if (e == hipSuccess) e = set_lds(reinterpret_cast<const void*>(&ssd_scan_kernel<T, Q>), scan_lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL((ssd_prefill_kernel<T, Q>), dim3(a.B * a.H), dim3(SSD_THREADS), lds, stream,
-                     static_cast<const T*>(a.x), a.x_stride, static_cast<const T*>(a.Bm),
-                     a.b_stride, static_cast<const T*>(a.Cm), a.c_stride,
-                     static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, a.D,
-                     static_cast<const T*>(a.z), a.z_stride, a.h0, a.h_final,
-                     static_cast<T*>(a.y), a.y_stride, a.L, a.H, a.G);
+  const int nC = (a.L + Q - 1) / Q;
+  if (nC > 0) {
+    hipLaunchKernelGGL((ssd_prep_kernel<T, Q>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
+                       stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
+                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
+                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC);
+  }
+  hipLaunchKernelGGL((ssd_scan_kernel<T, Q>), dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
+                     static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                     a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);
   return hipGetLastError();
 }
 
-size_t ssd_prefill_lds_bytes(int io_bf16, int chunk) {
-  if (io_bf16) return chunk == 128 ? sizeof(SsdSmem<bf16, 128>) : sizeof(SsdSmem<bf16, 64>);
-  return sizeof(SsdSmem<float, 64>);
+template <typename T, int Q>
+static size_t ws_bytes(int B, int L, int H, int G) {
+  using C = Cfg<T, Q>;
+  const size_t nC = ((size_t)L + Q - 1) / Q;
+  return nC * ((size_t)B * G * C::REC_BYTES + (size_t)B * H * C::HREC_BYTES);
+}
+
+size_t ssd_prefill_workspace(int io_bf16, int chunk, int B, int L, int H, int G) {
+  if (io_bf16) {
+    if (chunk == 64) return ws_bytes<bf16, 64>(B, L, H, G);
+    if (chunk == 128) return ws_bytes<bf16, 128>(B, L, H, G);
+    if (chunk == 256) return ws_bytes<bf16, 256>(B, L, H, G);
+  } else if (chunk == 64) {
+    return ws_bytes<float, 64>(B, L, H, G);
+  }
+  return 0;
 }
 
 hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream) {
   if (io_bf16) {
-    if (chunk == 128) return launch_tq<bf16, 128>(a, stream);
     if (chunk == 64) return launch_tq<bf16, 64>(a, stream);
+    if (chunk == 128) return launch_tq<bf16, 128>(a, stream);
+    if (chunk == 256) return launch_tq<bf16, 256>(a, stream);
   } else if (chunk == 64) {
     return launch_tq<float, 64>(a, stream);
   }

@@ -55,7 +55,8 @@ def prefill(d, **kw):
     a.update(kw)
     return m2.lib.mamba2_ssd_prefill(ctypes.byref(d), a["x"], a["xs"], a["Bm"], a["bs"], a["Cm"],
                                      a["cs"], a["dt"], a["dtb"], a["A"], a["D"], a["z"], a["zs"],
-                                     a["h0"], a["hf"], a["y"], a["ys"], None, 0, None)
+                                     a["h0"], a["hf"], a["y"], a["ys"], a.get("ws", BASE + 64 * MB),
+                                     a.get("wsb", 1 << 30), None)
 
 
 def conv(d, channels=512, **kw):
@@ -79,7 +80,7 @@ def decode(d, **kw):
     (dict(io=7), EDTYPE), (dict(batch=0), ESHAPE), (dict(seqlen=-1), ESHAPE),
     (dict(nheads=6, ngroups=4), ESHAPE), (dict(nheads=0), ESHAPE),
     (dict(headdim=32), EUNSUP), (dict(dstate=64), EUNSUP), (dict(conv_width=3), EUNSUP),
-    (dict(chunk=128), EUNSUP), (dict(chunk=256, io=m2.MAMBA2_BF16), EUNSUP), (dict(chunk=48), EUNSUP),
+    (dict(chunk=128), EUNSUP), (dict(chunk=512, io=m2.MAMBA2_BF16), EUNSUP), (dict(chunk=48), EUNSUP),
 ])
 def test_prefill_rejects_dims(kw, code):
     assert prefill(dims(**kw)) == code
@@ -101,6 +102,7 @@ def test_prefill_rejects_pointers(kw, code):
 def test_dims_null():
     assert m2.lib.mamba2_ssd_prefill(None, BASE, 256, BASE, 128, BASE, 128, BASE, BASE, BASE, None,
                                      None, 0, None, None, BASE, 256, None, 0, None) == ENULL
+    assert m2.lib.mamba2_ssd_prefill_workspace_bytes(None) == 0
 
 
 @pytest.mark.parametrize("kw,chan,code", [
@@ -130,5 +132,24 @@ def test_decode_needs_one_token():
     assert decode(dims(seqlen=1, nheads=512, ngroups=1)) == EUNSUP
 
 
-def test_workspace_query_is_zero():
-    assert m2.mamba2_ssd_prefill_workspace_bytes(dims(io=m2.MAMBA2_BF16, chunk=128)) == 0
+def test_workspace_size_formula():
+    """Per (sequence, group, chunk): fp32 causal Gram tiles + B^T and C operand tiles;
+    per (sequence, head, chunk): dt and its prefix sums."""
+    for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_BF16, 2, 256),
+                          (m2.MAMBA2_F32, 4, 64)):
+        d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
+        t = chunk // 32
+        rec = 4 * 1024 * t * (t + 1) // 2 + 2 * 128 * chunk * es
+        nc = -(-1000 // chunk)
+        assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 8 * chunk)
+    assert m2.mamba2_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
+    assert m2.mamba2_ssd_prefill_workspace_bytes(dims(chunk=100)) == 0
+    assert m2.lib.mamba2_ssd_prefill_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), 7), (dict(wsb=1000), 7), (dict(ws=BASE + 64 * MB + 8), EALIGN),
+    (dict(ws=BASE + 4 * MB), EALIAS), (dict(ws=BASE + 24 * MB), EALIAS),
+])
+def test_prefill_rejects_workspace(kw, code):
+    assert prefill(dims(), **kw) == code, m2.mamba2_last_error()

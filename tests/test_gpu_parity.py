@@ -98,9 +98,9 @@ def test_prefill_f32_ragged_with_state():
     check_prefill(small(101, io="f32", chunk=64, seqlen=197, nheads=8, ngroups=2))
 
 
-@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
 def test_prefill_bf16_ragged_multichunk(chunk):
-    check_prefill(small(102, chunk=chunk))
+    check_prefill(small(102, chunk=chunk, seqlen=600))
 
 
 @pytest.mark.parametrize("opts", [dict(z=False), dict(D=False), dict(h0=False),
@@ -143,8 +143,9 @@ def test_prefill_chunk_invariance_and_determinism():
     yr, hr = oracle_prefill(cfg, inp)
     y64, h64 = gpu_prefill(cfg, inp, chunk=64)
     y128, h128 = gpu_prefill(cfg, inp, chunk=128)
+    y256, h256 = gpu_prefill(cfg, inp, chunk=256)
     y128b, h128b = gpu_prefill(cfg, inp, chunk=128)
-    for yg, hg, q in ((y64, h64, 64), (y128, h128, 128)):
+    for yg, hg, q in ((y64, h64, 64), (y128, h128, 128), (y256, h256, 256)):
         assert_close(yg, yr, "bf16", f"chunk {q} y")
         assert_close(hg, hr, "bf16", f"chunk {q} h_final", rounded=False)
     assert compute_err(y64, y128, "bf16") <= 2 * TOL["bf16"]
