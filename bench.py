@@ -15,6 +15,7 @@ written once; they are the roofline numerators.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K]
        [--no-cpu-baseline] [--copy-calibration]
+       python bench.py --summarize-counters FETCH_CSV WRITE_CSV
 """
 from __future__ import annotations
 
@@ -90,14 +91,11 @@ def decode_bytes(cfg) -> int:
 
 
 # ------------------------------------------------------------------------------ GPU parts
-def run_prefill(args, torch, m2, si):
-    cfg = si.CONFIGS[1]
-    inp = si.draw_prefill(cfg)
+def run_prefill(args, torch, m2, si, cfg, inp):
     dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
     f32 = lambda a: torch.from_numpy(a).cuda()
     u, z, dt = dev(inp["xbc"]), dev(inp["z"]), dev(inp["dt_raw"])
     w, bias, dtb, A, D = (f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
-    del inp
     di, gn = cfg.d_inner, cfg.ngroups * cfg.dstate
     xbc = torch.empty_like(u)
     x, Bm, Cm = xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:]
@@ -135,7 +133,7 @@ def run_prefill(args, torch, m2, si):
     total_ms = t_start.elapsed_time(t_end)
     conv_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / args.steps
     ssd_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1e3 / args.steps
-    return cfg, total_ms / args.steps, wall, conv_us, ssd_us
+    return total_ms / args.steps, wall, conv_us, ssd_us
 
 
 def run_decode(args, torch, m2, si):
@@ -172,27 +170,27 @@ def run_decode(args, torch, m2, si):
     return cfg, sum(times) / n, times[n // 2]
 
 
+CALIB_BYTES = 1 << 30
+
+
 def copy_calibration(torch):
-    """A plain device copy of known size, so counter runs can scale FETCH_SIZE and
-    WRITE_SIZE to bytes: it reads and writes exactly 1 GiB."""
-    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    """One elementwise kernel of known traffic (torch.neg over 2^28 fp32: reads 1 GiB,
+    writes 1 GiB), so counter runs can scale FETCH_SIZE and WRITE_SIZE to bytes."""
+    a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
-    b.copy_(a)
+    torch.neg(a, out=b)
     torch.cuda.synchronize()
-    return 1 << 30
+    del a, b
 
 
 # ------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(si):
-    """The fp64 oracle timed on a bounded sample of the prefill workload: the conv over all
-    8192 tokens and the sequential scan over 16 of the 160 heads (every tenth head, two per
-    group), all 8192 tokens; the scan time is scaled by 10 to the full layer."""
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle timed on the whole prefill workload (same seeded inputs as the GPU
+    step): conv1d over all tokens and channels, then the sequential scan over all heads.
+    About 30 s of CPU work, a few seconds of wall time on a multi-core host."""
     import numpy as np
     import oracle
-    cfg = si.CONFIGS[1]
-    inp = si.draw_prefill(cfg)
-    heads = list(range(0, cfg.nheads, 10))
     u = np.ascontiguousarray(inp["xbc"], dtype=np.float64)
     threads = oracle.threads(0)
     t0 = time.perf_counter()
@@ -202,16 +200,72 @@ def cpu_baseline(si):
     z = np.ascontiguousarray(inp["z"], dtype=np.float64)
     dt = np.ascontiguousarray(inp["dt_raw"], dtype=np.float64)
     t0 = time.perf_counter()
-    oracle.ssd_scan(x, Bm, Cm, dt, inp["dt_bias"], inp["A"], inp["D"], z, None, ngroups=cfg.ngroups,
-                    heads=heads)
+    oracle.ssd_scan(x, Bm, Cm, dt, inp["dt_bias"], inp["A"], inp["D"], z, None, ngroups=cfg.ngroups)
     t_scan = time.perf_counter() - t0
-    full = t_conv + t_scan * cfg.nheads / len(heads)
+    full = t_conv + t_scan
     return {"value": cfg.batch * cfg.seqlen / full, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 oracle on the same prefill workload: conv1d over all {cfg.seqlen} tokens "
-                      f"({t_conv:.2f} s) and the sequential scan over {len(heads)} of {cfg.nheads} heads "
-                      f"(all groups) x {cfg.seqlen} tokens ({t_scan:.2f} s), scan scaled x"
-                      f"{cfg.nheads // len(heads)} to the full layer"}
+            "sample": f"the whole prefill step once, unscaled: fp64 conv1d over {cfg.seqlen} tokens x "
+                      f"{cfg.conv_channels} channels ({t_conv:.2f} s) and the sequential fp64 scan "
+                      f"over all {cfg.nheads} heads x {cfg.seqlen} tokens ({t_scan:.2f} s), "
+                      f"{threads} OpenMP threads"}
+
+
+# ------------------------------------------------------------------------------ counters
+COUNTER_KERNELS = {          # traffic entry -> kernel-name fragments summed per call
+    "ssd_prefill": ["ssd_prep_kernel", "ssd_scan_kernel"],
+    "conv1d": ["conv1d_kernel"],
+    "state_update": ["state_update_kernel"],
+}
+
+
+def _counter_means(path: str, counter: str):
+    """Mean counter value per kernel name over its dispatches in a rocprofv3
+    counter_collection.csv, and the largest single-dispatch value of torch's elementwise
+    kernels (the calibration kernel is by far the largest of those in a bench run)."""
+    import csv
+    acc, calib = {}, 0.0
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            v = float(row["Counter_Value"])
+            a = acc.setdefault(row["Kernel_Name"], [0.0, 0])
+            a[0] += v
+            a[1] += 1
+            if "elementwise_kernel" in row["Kernel_Name"]:
+                calib = max(calib, v)
+    return {k: v[0] / v[1] for k, v in acc.items()}, calib
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration kernel (torch.neg over
+    1 GiB in, 1 GiB out). Writes profiles/traffic.json keyed by the kernel source hash."""
+    fetch, f_kib = _counter_means(fetch_csv, "FETCH_SIZE")
+    write, w_kib = _counter_means(write_csv, "WRITE_SIZE")
+    if f_kib <= 0 or w_kib <= 0:
+        raise SystemExit("no calibration dispatch found: run the counter passes with --copy-calibration")
+
+    def pick(table, frag):
+        hits = [v for k, v in table.items() if frag in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {frag!r}, found {len(hits)}: "
+                             f"{sorted(table)}")
+        return hits[0]
+
+    f_cal = CALIB_BYTES / (f_kib * 1024.0)
+    w_cal = CALIB_BYTES / (w_kib * 1024.0)
+    out = {"_calibration": {"kernel": "torch.neg over 2^28 fp32 (1 GiB read, 1 GiB written)",
+                            "fetch_factor": f_cal, "write_factor": w_cal}}
+    for key, frags in COUNTER_KERNELS.items():
+        fb = sum(pick(fetch, fr) for fr in frags) * 1024.0 * f_cal
+        wb = sum(pick(write, fr) for fr in frags) * 1024.0 * w_cal
+        out[key] = {"source_hash": kernel_source_hash(key), "fetch_bytes": fb, "write_bytes": wb,
+                    "bytes_per_launch": fb + wb, "kernels": frags}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 # ------------------------------------------------------------------------------ main
@@ -223,7 +277,12 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer core runs on a single MI355X with no "
               "collectives, so --gpus above 1 is not supported.", file=sys.stderr)
@@ -236,7 +295,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(torch)
-    cfg, ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si)
+    cfg = si.CONFIGS[1]
+    inp = si.draw_prefill(cfg)
+    ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si, cfg, inp)
     by = prefill_bytes(cfg)
     fl = prefill_flops(cfg)
     tokens = cfg.batch * cfg.seqlen
@@ -263,7 +324,8 @@ def main():
                    "headdim": cfg.headdim, "ngroups": cfg.ngroups, "dstate": cfg.dstate,
                    "conv_width": cfg.conv_width, "chunk": cfg.chunk, "io": "bf16",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "ssd_prefill", "bound": "hbm", "achieved": ssd_gbs,
+        "roofline": {"kernel": "mamba2_ssd_prefill (ssd_prep_kernel + ssd_scan_kernel)",
+                     "bound": "hbm", "achieved": ssd_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ssd_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("ssd_prefill"),
                      "algorithmic_bytes": by["ssd"], "avg_launch_us": ssd_us},
@@ -284,7 +346,7 @@ def main():
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(si)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out))
 
 
