@@ -19,6 +19,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional
 
 import numpy as np
@@ -26,7 +28,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "config", "bf16_round", "bf16_bits", "bits_to_f32",
     "draw_params", "draw_xbc", "draw_z", "draw_dt_raw", "draw_h0",
-    "draw_conv_state", "draw_prefill", "draw_decode_step", "TOKEN_BLOCK",
+    "draw_conv_state", "draw_prefill", "draw_decode_step", "draw_decode_steps", "TOKEN_BLOCK",
 ]
 
 TOKEN_BLOCK = 256  # tokens per independently seeded block
@@ -144,16 +146,43 @@ def _blocks(t0: int, t1: int):
         blk += 1
 
 
-def _tokens(cfg: Config, tid: int, width: int, t0: int, t1: int, fill, step: int = -1) -> np.ndarray:
-    """Rows [t0, t1) of a [B][L][width] float32 tensor, each block drawn by ``fill``."""
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _tokens(cfg: Config, tid: int, width: int, t0: int, t1: int, fill, stream: int = 0,
+            io: str = "f32") -> np.ndarray:
+    """Rows [t0, t1) of a [B][T][width] float32 tensor, rounded to ``io``.
+
+    Rows are drawn in 256-row blocks: block k of batch row b comes from the stream
+    (seed, tid, b, k, stream), with stream 0 for prefill tokens and 1 for decode steps
+    (row = step index). Blocks are independent, so they are filled on a thread pool; the
+    result does not depend on the number of threads.
+    """
     out = np.empty((cfg.batch, t1 - t0, width), dtype=np.float32)
-    for b in range(cfg.batch):
-        for blk in _blocks(t0, t1):
-            b0 = blk * TOKEN_BLOCK
-            rows = fill(_rng(cfg.seed, tid, b, blk, step + 1), TOKEN_BLOCK, width)
-            lo, hi = max(t0, b0), min(t1, b0 + TOKEN_BLOCK)
-            out[b, lo - t0:hi - t0] = rows[lo - b0:hi - b0]
+
+    def one(job):
+        b, blk = job
+        b0 = blk * TOKEN_BLOCK
+        rows = fill(_rng(cfg.seed, tid, b, blk, stream), TOKEN_BLOCK, width)
+        lo, hi = max(t0, b0), min(t1, b0 + TOKEN_BLOCK)
+        out[b, lo - t0:hi - t0] = _io(rows[lo - b0:hi - b0], io)
+
+    jobs = [(b, blk) for b in range(cfg.batch) for blk in _blocks(t0, t1)]
+    if len(jobs) < 4:
+        for j in jobs:
+            one(j)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one, jobs))
     return out
+
+
+def _span(cfg: Config, t0: int, t1: Optional[int], step: int):
+    """(t0, t1, stream) of a prefill token range or of decode step ``step``."""
+    if step >= 0:
+        return step, step + 1, 1
+    return t0, cfg.seqlen if t1 is None else t1, 0
 
 
 def _xbc_fill(cfg: Config):
@@ -177,27 +206,31 @@ def draw_xbc(cfg: Config, t0: int = 0, t1: Optional[int] = None, step: int = -1)
     The same draw serves as the post-conv x/B/C operand of a stand-alone scan.
     Rounded to the config's I/O type.
     """
-    t1 = cfg.seqlen if t1 is None else t1
-    return _io(_tokens(cfg, _T_XBC, cfg.conv_channels, t0, t1, _xbc_fill(cfg), step), cfg.io)
+    t0, t1, stream = _span(cfg, t0, t1, step)
+    return _tokens(cfg, _T_XBC, cfg.conv_channels, t0, t1, _xbc_fill(cfg), stream, cfg.io)
 
 
 def draw_z(cfg: Config, t0: int = 0, t1: Optional[int] = None, step: int = -1) -> np.ndarray:
-    t1 = cfg.seqlen if t1 is None else t1
-    return _io(_tokens(cfg, _T_Z, cfg.d_inner, t0, t1, _normal_fill, step), cfg.io)
+    t0, t1, stream = _span(cfg, t0, t1, step)
+    return _tokens(cfg, _T_Z, cfg.d_inner, t0, t1, _normal_fill, stream, cfg.io)
+
+
+def _dt_rows(cfg: Config, t0: int, t1: int, stream: int, dt_bias: np.ndarray) -> np.ndarray:
+    if cfg.dt_mode == "normal":
+        raw = _tokens(cfg, _T_DT, cfg.nheads, t0, t1, _normal_fill, stream)
+    else:
+        lo, hi = math.log(1e-3), math.log(0.1)
+        u = _tokens(cfg, _T_DT, cfg.nheads, t0, t1,
+                    lambda rng, n, w: np.exp(rng.uniform(lo, hi, (n, w))).astype(np.float32), stream)
+        raw = (_inv_softplus(u.astype(np.float64)) - dt_bias.astype(np.float64)).astype(np.float32)
+    return _io(raw, cfg.io)
 
 
 def draw_dt_raw(cfg: Config, t0: int = 0, t1: Optional[int] = None, step: int = -1,
                 dt_bias: Optional[np.ndarray] = None) -> np.ndarray:
-    t1 = cfg.seqlen if t1 is None else t1
-    if cfg.dt_mode == "normal":
-        raw = _tokens(cfg, _T_DT, cfg.nheads, t0, t1, _normal_fill, step)
-    else:
-        lo, hi = math.log(1e-3), math.log(0.1)
-        u = _tokens(cfg, _T_DT, cfg.nheads, t0, t1,
-                    lambda rng, n, w: np.exp(rng.uniform(lo, hi, (n, w))).astype(np.float32), step)
-        bias = draw_params(cfg)["dt_bias"] if dt_bias is None else dt_bias
-        raw = (_inv_softplus(u.astype(np.float64)) - bias.astype(np.float64)).astype(np.float32)
-    return _io(raw, cfg.io)
+    t0, t1, stream = _span(cfg, t0, t1, step)
+    bias = draw_params(cfg)["dt_bias"] if dt_bias is None else dt_bias
+    return _dt_rows(cfg, t0, t1, stream, bias)
 
 
 def draw_h0(cfg: Config) -> np.ndarray:
@@ -229,6 +262,16 @@ def draw_prefill(cfg: Config, t0: int = 0, t1: Optional[int] = None) -> Dict[str
     d["dt_raw"] = draw_dt_raw(cfg, t0, t1, dt_bias=p["dt_bias"])
     d["h0"] = draw_h0(cfg)
     return d
+
+
+def draw_decode_steps(cfg: Config, k0: int, k1: int) -> Dict[str, np.ndarray]:
+    """Decode steps [k0, k1) at once, step-major ([k][B][...]); entry k equals row 0 of
+    what draw_decode_step(cfg, k) returns."""
+    bias = draw_params(cfg)["dt_bias"]
+    f = lambda a: np.ascontiguousarray(a.transpose(1, 0, 2))
+    return {"xbc": f(_tokens(cfg, _T_XBC, cfg.conv_channels, k0, k1, _xbc_fill(cfg), 1, cfg.io)),
+            "z": f(_tokens(cfg, _T_Z, cfg.d_inner, k0, k1, _normal_fill, 1, cfg.io)),
+            "dt_raw": f(_dt_rows(cfg, k0, k1, 1, bias))}
 
 
 def draw_decode_step(cfg: Config, step: int) -> Dict[str, np.ndarray]:

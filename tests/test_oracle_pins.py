@@ -376,3 +376,19 @@ def test_threads_do_not_change_results():
     y1, _ = scan(c, s, nthreads=1)
     y4, _ = scan(c, s, nthreads=4)
     np.testing.assert_array_equal(y1, y4)
+
+
+def test_one_head_per_group_sublayer_matches_full():
+    """The long-workload parity tests run the oracle on a sub-layer made of one head per
+    group (its x, z, dt columns and every group's B and C). The recurrence is per head, so
+    that sub-layer must reproduce the full layer's outputs for those heads exactly."""
+    c, s = rand_case(19, H=8, G=4)
+    y, hf = scan(c, s)
+    P, N, G = s["P"], s["N"], s["G"]
+    heads = [1, 2, 4, 7]
+    cols = np.concatenate([np.arange(h * P, (h + 1) * P) for h in heads])
+    sub = dict(c, x=c["x"][..., cols], z=c["z"][..., cols], dt_raw=c["dt_raw"][..., heads],
+               dt_bias=c["dt_bias"][heads], A=c["A"][heads], D=c["D"][heads], h0=c["h0"][:, heads])
+    ys, hs = scan(sub, dict(s, H=len(heads)))
+    np.testing.assert_array_equal(ys, y[..., cols])
+    np.testing.assert_array_equal(hs, hf[:, heads])
