@@ -102,10 +102,11 @@ int mamba2_conv1d(const mamba2_dims* dims, int32_t channels, const void* u, int6
  * needs for `dims` (0 if `dims` is invalid or the sequence is empty). The scan
  * first computes, once per (sequence, group, chunk), the causal Gram tiles
  * B_s . C_t of the chunk in fp32 and B^T and C laid out as MFMA operands, which
- * every head of the group then reads, and per (sequence, head, chunk) dt and
- * its prefix sums. With T = chunk / 32 and e = sizeof(io):
+ * every head of the group then reads, and per (sequence, head, chunk) dt, its
+ * prefix sums and per-token decay weights (3 fp32 per token). With T = chunk / 32
+ * and e = sizeof(io):
  *   nchunks * (batch * ngroups * (4096 T(T+1)/2 + 2 * 128 * chunk * e)
- *              + batch * nheads * 8 * chunk)            nchunks = ceil(seqlen / chunk)
+ *              + batch * nheads * 12 * chunk)           nchunks = ceil(seqlen / chunk)
  * The caller owns it; its contents are scratch (nothing is kept between calls).
  */
 size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);

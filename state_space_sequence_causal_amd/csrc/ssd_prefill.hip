@@ -16,8 +16,9 @@
 //    products of the bf16 inputs) in MFMA accumulator order, and B^T and C in MFMA operand
 //    order, so that each wave later reads every operand as 1 KiB contiguous per
 //    instruction; these are shared by all heads of the group. For each head of the group
-//    it writes dt = softplus(dt_raw + dt_bias) and the inclusive prefix of dt*A*log2(e)
-//    inside 32-token blocks.
+//    it writes dt = softplus(dt_raw + dt_bias), the inclusive prefix pi of dt*A*log2(e)
+//    inside 32-token blocks, and v_s = exp2(pi_end - pi_s) dt_s (decay from token s to the
+//    end of its block, times dt_s).
 //  * ssd_scan, one workgroup of 8 waves per (b, h). The fp32 state stays on chip for the
 //    whole sequence. Waves 0-3 ("Y waves") own 32-token blocks of the chunk: they build
 //    the masked decay matrix M from the Gram tiles and compute Y^T = X^T M^T + H^T C^T
@@ -65,8 +66,8 @@ struct Cfg {
   static constexpr size_t BT_BYTES = (size_t)(SN / 32) * KS_Q * 64 * FB;
   static constexpr size_t CF_BYTES = (size_t)NTB * KS_N * 64 * FB;
   static constexpr size_t REC_BYTES = G_BYTES + BT_BYTES + CF_BYTES;
-  // workspace record per (b, h, chunk): dt[Q] | pi[Q]
-  static constexpr size_t HREC_BYTES = 2 * Q * sizeof(float);
+  // workspace record per (b, h, chunk): dt[Q] | pi[Q] | v[Q]
+  static constexpr size_t HREC_BYTES = 3 * Q * sizeof(float);
   static constexpr int XV = Q * SP / VE / SCAN_THREADS;     // 16-byte x vectors per thread
   static constexpr bool PAIRS = XV % 2 == 0;                // two tokens per transposed write
   static constexpr int TPL = Q / 64;                        // decay tokens per lane (lane + 64 k)
@@ -85,9 +86,10 @@ __device__ __forceinline__ int xsw(int p, int s) {
   return s ^ (16 * ((p >> 3) & MASK));
 }
 
-__device__ __forceinline__ int tile_tb(int k) {  // column block of lower-triangle tile k
+__device__ __forceinline__ int tile_tb(int k) {  // column block of lower-triangle tile k < 36
   int tb = 0;
-  while ((tb + 1) * (tb + 2) / 2 <= k) ++tb;
+#pragma unroll
+  for (int t = 1; t < 8; ++t) tb += k >= t * (t + 1) / 2;
   return tb;
 }
 
@@ -165,9 +167,11 @@ __global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
         float o = __shfl_up(run, d, 32);
         if ((lane & 31) >= d) run += o;
       }
+      const float tot = __shfl(run, (lane & 32) + 31);   // the block's total
       float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
       hr[s] = dt;
       hr[Q + s] = run;
+      hr[2 * Q + s] = exp2_hw(tot - run) * dt;   // decay from s to the end of its block, times dt
     }
   }
   __syncthreads();
@@ -202,9 +206,12 @@ __global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------- scan kernel
+// ---------------------------------------------------------------------------- scan kernel, chunk 256
+// One role per wave for the whole chunk: 4 Y waves build the masked decay tiles M^T of their
+// token blocks in registers and compute Y^T, 4 H waves update the state (two barriers per
+// chunk). z is read straight from HBM (the chunk does not fit LDS alongside the rest).
 template <typename T, int Q>
-struct ScanSmem {
+struct WideSmem {
   using C = Cfg<T, Q>;
   T sXt[SP][C::LDQ];                       // x^T (k = s): A operand of Y_diag
   T sXW[SP][C::LDQ];                       // (w x)^T hi: B operand of the state update
@@ -277,7 +284,7 @@ __device__ __forceinline__ f32x16 load_tile16(const float* src) {
 
 template <typename T, int Q>
 __global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
+void ssd_scan_wide_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
                      const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
                      T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
                      int L, int H, int G) {
@@ -285,7 +292,7 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
   using YP = YPlan<Q>;
   constexpr int VE = C::VE;
   extern __shared__ __align__(16) unsigned char scan_smem[];
-  ScanSmem<T, Q>& S = *reinterpret_cast<ScanSmem<T, Q>*>(scan_smem);
+  WideSmem<T, Q>& S = *reinterpret_cast<WideSmem<T, Q>*>(scan_smem);
 
   const int id = xcd_local_order(blockIdx.x, gridDim.x);
   const int b = id / H, h = id % H;
@@ -339,7 +346,7 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
         if (zb) rZ[i] = ok ? ld16(zb + (row0 + t) * z_stride + cv * VE) : zero16<T>();
       }
     }
-    const float* hr = hrec + (size_t)c * (2 * Q);
+    const float* hr = hrec + (size_t)c * (3 * Q);
 #pragma unroll
     for (int k = 0; k < C::TPL; ++k) {
       rdt[k] = hr[lane + 64 * k];
@@ -706,6 +713,471 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
   }
 }
 
+// ---------------------------------------------------------------------------- scan kernel
+// Chunk sizes 64 and 128. Per chunk, three phases separated by barriers:
+//  S1 (all waves) stage the chunk: y of the previous chunk out of LDS (coalesced), raw z
+//     in, x^T and (w x)^T hi/lo, the chunk's dt / pi / v record; prefetch the next chunk.
+//  S2 Y waves: Y^T = H^T C^T for their tiles, scaled by exp2(lambda_t), and SiLU(z) into
+//     registers. H waves: the masked decay tiles M^T of the chunk (hi/lo) into LDS, each
+//     built once for all Y waves.
+//  S3 Y waves: Y^T += X^T M^T and the gated epilogue into LDS. H waves: H = exp2(lambda_end)
+//     H + B^T (w x), then the new state (bf16 hi/lo) into LDS for the next chunk.
+// Ownership: Y wave y holds two Y^T tiles (token blocks tb, one p-block) whose triangle
+// work adds up to the same amount on every wave; H wave w holds two state tiles of one
+// p-block. Each SIMD runs one Y wave and one H wave.
+//
+// Decay bookkeeping (log2 units, lambda_t = sum of dt*A*log2e from the chunk start through
+// t, blocks of 32 tokens with totals tot_k and in-block prefixes pi_t):
+//   exp2(lambda_t) = exp2(sum_{k<blk(t)} tot_k + pi_t)
+//   w_s = exp2(lambda_end - lambda_s) dt_s = v_s exp2(sum_{k>blk(s)} tot_k)
+//   decay s -> t across blocks si < tb = v_s exp2(sum_{si<k<tb} tot_k) exp2(pi_t)
+template <int Q> struct Own;
+template <> struct Own<64> {
+  static constexpr int NY = 1;
+  static constexpr int NB = 1;   // M tiles built per H wave (at most)
+  __device__ static int tb(int y, int) { return y >> 1; }
+  __device__ static int build(int w, int) { return w < 3 ? w : -1; }
+};
+template <> struct Own<128> {
+  static constexpr int NY = 2;
+  static constexpr int NB = 3;
+  __device__ static int tb(int y, int i) { return y < 2 ? (i ? 3 : 0) : (i ? 2 : 1); }
+  // lower-triangle tile k = tb (tb + 1) / 2 + si: H wave w builds diagonal tile w and one
+  // or two of the off-diagonal tiles 1, 3, 4, 6, 7, 8
+  __device__ static int build(int w, int i) {
+    if (i == 0) return w * (w + 3) / 2;
+    if (i == 1) return w == 0 ? 1 : w == 1 ? 3 : w == 2 ? 4 : 6;
+    return w == 0 ? 8 : w == 1 ? 7 : -1;
+  }
+};
+
+template <typename T, int Q>
+struct ScanSmem {
+  using C = Cfg<T, Q>;
+  T sXt[SP][C::LDQ];                        // x^T (k = s): A operand of Y^T += X^T M^T
+  T sXW[SP][C::LDQ];                        // (w x)^T hi: B operand of the state update
+  T sXWlo[C::SPLIT ? SP : 1][C::LDQ];       //        lo
+  T sHt[SP][C::LDN];                        // H^T hi: A operand of Y^T = H^T C^T
+  T sHtlo[C::SPLIT ? SP : 1][C::LDN];       //     lo
+  T sZ[Q][SP];                              // z of the chunk, then y (zpos layout)
+  Frag<T> sM[C::NTILES][2][64];             // M^T tiles in B-operand order [tile][k step][lane]
+  Frag<T> sMlo[C::SPLIT ? C::NTILES : 1][2][64];
+  float sRec[3 * Q];                        // dt | pi | v of the chunk
+};
+
+// Element (t, p) of the z / y tile sits at column zpos(t, p): 4-element groups XOR-ed with a
+// key of the token, so that the epilogue's 4-element accesses (32 tokens x one column group
+// per instruction) hit distinct banks. 16-byte staging vectors stay whole; with bf16 the two
+// halves of a vector trade places when bit 2 of the key is set.
+template <typename T>
+__device__ __forceinline__ int zkey(int t) {
+  return 4 * ((sizeof(T) == 2 ? t >> 1 : t) & 15);
+}
+template <typename T>
+__device__ __forceinline__ int zpos(int t, int p) { return p ^ zkey<T>(t); }
+
+template <typename T>
+__device__ __forceinline__ Vec<T> half_swap(const Vec<T>& v, bool swap) {
+  if constexpr (sizeof(T) == 2) {
+    Vec<T> r;
+    r.v = swap ? __builtin_shufflevector(v.v, v.v, 4, 5, 6, 7, 0, 1, 2, 3) : v.v;
+    return r;
+  } else {
+    return v;
+  }
+}
+
+template <typename T, int Q>
+__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
+                     const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
+                     T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
+                     int L, int H, int G) {
+  using C = Cfg<T, Q>;
+  using OW = Own<Q>;
+  constexpr int VE = C::VE;
+  constexpr int NTB = C::NTB;
+  extern __shared__ __align__(16) unsigned char scan_smem[];
+  ScanSmem<T, Q>& S = *reinterpret_cast<ScanSmem<T, Q>*>(scan_smem);
+  const float* sDt = S.sRec;
+  const float* sPi = S.sRec + Q;
+  const float* sV = S.sRec + 2 * Q;
+
+  const int id = xcd_local_order(blockIdx.x, gridDim.x);
+  const int b = id / H, h = id % H;
+  const int g = h / (H / G);
+  const int nC = (L + Q - 1) / Q;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g2 = lane >> 5;
+  const bool ywave = wave < 4;
+
+  const int64_t row0 = (int64_t)b * L;
+  const T* xb = x + h * SP;
+  const T* zb = z ? z + h * SP : nullptr;
+  T* yb = y + h * SP;
+  const float Dh = D ? D[h] : 0.f;
+  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
+  const float* hrec = reinterpret_cast<const float*>(
+      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
+      ((size_t)b * H + h) * nC * C::HREC_BYTES);
+
+  // ------------------------------------------------------------ staging registers
+  // x and z: XV 16-byte vectors per thread. With PAIRS, vectors 2i and 2i+1 are tokens
+  // 2sp and 2sp+1 of one 16-byte column, 8 lanes per token row (coalesced loads), so x^T
+  // and (w x)^T go to LDS as 32-bit token pairs.
+  Vec<T> rX[C::XV], rZ[C::XV];
+  float rV[C::XV];                  // v of each staged token
+  float rRec;                       // one word of the dt | pi | v record (threads < 3Q)
+  float tot[NTB];                   // block totals of the chunk (wave-uniform)
+  auto xcoord = [&](int i, int& s, int& cv) {
+    constexpr int VPR = SP / VE;  // vectors per token row
+    if constexpr (C::PAIRS) {
+      const int u = tid + SCAN_THREADS * (i >> 1);
+      s = 2 * (u / VPR) + (i & 1);
+      cv = u % VPR;
+    } else {
+      const int v = tid + SCAN_THREADS * i;
+      s = v / VPR;
+      cv = v % VPR;
+    }
+  };
+  auto load_chunk = [&](int c) {
+    const int t0 = c * Q;
+    const float* hr = hrec + (size_t)c * (3 * Q);
+#pragma unroll
+    for (int i = 0; i < C::XV; ++i) {
+      int s_, cv;
+      xcoord(i, s_, cv);
+      const int t = t0 + s_;
+      const bool ok = t < L;
+      rX[i] = ok ? ld16(xb + (row0 + t) * x_stride + cv * VE) : zero16<T>();
+      if (zb) rZ[i] = ok ? ld16(zb + (row0 + t) * z_stride + cv * VE) : zero16<T>();
+      rV[i] = hr[2 * Q + s_];
+    }
+    if (tid < 3 * Q) rRec = hr[tid];
+#pragma unroll
+    for (int k = 0; k < NTB; ++k) tot[k] = hr[Q + 32 * k + 31];
+  };
+  // y of chunk c-1 out of sZ, thread by thread over the same vectors it then refills
+  auto flush_y = [&](int c, int s_, int cv) {
+    const int t = (c - 1) * Q + s_;
+    const int key = zkey<T>(s_);
+    const Vec<T> v = ld16(&S.sZ[s_][(cv * VE) ^ (key & ~(VE - 1))]);
+    if (t < L) st16(yb + (row0 + t) * y_stride + cv * VE, half_swap<T>(v, (key & 4) && VE == 8));
+  };
+
+  // ------------------------------------------------------------ phase S1
+  // Leaves the chunk's block totals in `ctot` for the rest of the chunk.
+  float ctot[NTB];
+  auto stage = [&](int c) {
+#pragma unroll
+    for (int k = 0; k < NTB; ++k) ctot[k] = tot[k];
+#pragma unroll
+    for (int i = 0; i < C::XV; ++i) {
+      int s_, cv;
+      xcoord(i, s_, cv);
+      if (c > 0) flush_y(c, s_, cv);
+      if (zb) {
+        const int key = zkey<T>(s_);
+        st16(&S.sZ[s_][(cv * VE) ^ (key & ~(VE - 1))], half_swap<T>(rZ[i], (key & 4) && VE == 8));
+      }
+    }
+    if (tid < 3 * Q) S.sRec[tid] = rRec;
+    // exp2 of the decay from the end of block k to the end of the chunk
+    float esuf[NTB];
+    {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = NTB - 1; k >= 0; --k) {
+        esuf[k] = exp2_hw(acc);
+        acc += ctot[k];
+      }
+    }
+    auto w_of = [&](int i, int s_) {
+      float e = esuf[0];
+#pragma unroll
+      for (int k = 1; k < NTB; ++k)
+        if ((s_ >> 5) == k) e = esuf[k];
+      return rV[i] * e;
+    };
+    if constexpr (C::PAIRS) {
+#pragma unroll
+      for (int i = 0; i < C::XV; i += 2) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        const float w0 = w_of(i, s_), w1 = w_of(i + 1, s_ + 1);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const T x0 = rX[i].v[e], x1 = rX[i + 1].v[e];
+          const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
+          const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
+          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
+          st_pair(&S.sXt[p][sw], x0, x1);
+          st_pair(&S.sXW[p][sw], h0_, h1_);
+          if constexpr (C::SPLIT)
+            st_pair(&S.sXWlo[p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::XV; ++i) {
+        int s_, cv;
+        xcoord(i, s_, cv);
+        const float w0 = w_of(i, s_);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const T x0 = rX[i].v[e];
+          const float v0 = to_f(x0) * w0;
+          const T h0_ = from_f<T>(v0);
+          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
+          S.sXt[p][sw] = x0;
+          S.sXW[p][sw] = h0_;
+          if constexpr (C::SPLIT) S.sXWlo[p][sw] = from_f<T>(v0 - to_f(h0_));
+        }
+      }
+    }
+    if (c + 1 < nC) load_chunk(c + 1);
+  };
+
+  // The two roles run separate chunk loops with the same barrier sequence (three barriers
+  // per chunk), so each role's registers are allocated on their own.
+  if (ywave) {
+    // ========================================================== Y waves: outputs
+    const int pb = wave & 1;
+    const int prow = pb * 32 + col;
+    Frag<T> cf[OW::NY][C::KS_N];        // C operand frags of the owned token blocks
+    auto fetch = [&](int c) {
+      const unsigned char* cfp = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES;
+#pragma unroll
+      for (int i = 0; i < OW::NY; ++i)
+#pragma unroll
+        for (int j = 0; j < C::KS_N; ++j)
+          cf[i][j] = ld_frag<T>(cfp + ((size_t)(OW::tb(wave, i) * C::KS_N + j) * 64 + lane) * C::FB);
+    };
+    if (nC > 0) {
+      load_chunk(0);
+      fetch(0);
+    }
+    for (int c = 0; c < nC; ++c) {
+      stage(c);
+      __syncthreads();
+      // ---- S2: carried state, scaled by exp2(lambda_t); gate values
+      f32x16 acc[OW::NY];
+      float gz[OW::NY][16];
+#pragma unroll
+      for (int i = 0; i < OW::NY; ++i) {
+        acc[i] = (f32x16){};
+#pragma unroll
+        for (int j = 0; j < C::KS_N; ++j) {
+          mma(acc[i], frag_contig(&S.sHt[prow][16 * j], g2), cf[i][j]);
+          if constexpr (C::SPLIT) mma(acc[i], frag_contig(&S.sHtlo[prow][16 * j], g2), cf[i][j]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < OW::NY; ++i) {
+        const int tb = OW::tb(wave, i);
+        const int tl = tb * 32 + col;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          if (zb) {
+            const Raw4<T> zz = ld4(&S.sZ[tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gz[i][4 * r4 + q] = silu_fast(zz.get(q));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gz[i][4 * r4 + q] = 1.f;
+          }
+        }
+        float before = 0.f;
+#pragma unroll
+        for (int k = 0; k < NTB - 1; ++k)
+          if (k < tb) before += ctot[k];
+        const float et = exp2_hw(before + sPi[tl]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= et;
+      }
+      __syncthreads();
+      if (c + 1 < nC) fetch(c + 1);
+      // ---- S3: intra-chunk part from the M^T tiles, then y = acc * SiLU(z) into sZ
+#pragma unroll
+      for (int i = 0; i < OW::NY; ++i) {
+        const int tb = OW::tb(wave, i);
+        const int k0 = tb * (tb + 1) / 2;
+        for (int si = 0; si <= tb; ++si) {
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2) {
+            const Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, si * 32 + 16 * m2, g2);
+            mma(acc[i], xa, S.sM[k0 + si][m2][lane]);
+            if constexpr (C::SPLIT) mma(acc[i], xa, S.sMlo[k0 + si][m2][lane]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < OW::NY; ++i) {
+        const int tl = OW::tb(wave, i) * 32 + col;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * r4;
+          st4(&S.sZ[tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[i][r] * gz[i][r],
+              acc[i][r + 1] * gz[i][r + 1], acc[i][r + 2] * gz[i][r + 2], acc[i][r + 3] * gz[i][r + 3]);
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // ========================================================== H waves: M^T and state
+    const int hw = wave - 4;
+    const int pb = hw & 1;
+    const int prow = pb * 32 + col;
+    const int nb0 = hw >> 1;            // row blocks nb0 and nb0 + 2
+    f32x16 hacc[2];
+    Frag<T> af[2][C::KS_Q];             // B^T operand frags of the two row blocks
+    f32x16 gram[OW::NB];                // Gram tiles of the M^T tiles this wave builds
+    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
+        hacc[i][r] = h0 ? h0[sbase + n * SP + prow] : 0.f;
+      }
+    auto fetch_bt = [&](int c) {
+      const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < C::KS_Q; ++j)
+          af[i][j] = ld_frag<T>(btf + ((size_t)((nb0 + 2 * i) * C::KS_Q + j) * 64 + lane) * C::FB);
+    };
+    auto fetch_gram = [&](int c) {
+      const float* gt = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES);
+#pragma unroll
+      for (int s = 0; s < OW::NB; ++s) {
+        const int k = OW::build(hw, s);
+        if (k >= 0) gram[s] = load_tile16(gt + ((size_t)k * 64 + lane) * 16);
+      }
+    };
+    auto write_state = [&]() {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int n = (nb0 + 2 * i) * 32 + 8 * r4 + 4 * g2;
+          float v[4], lo[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[k] = hacc[i][4 * r4 + k];
+            lo[k] = v[k] - to_f(from_f<T>(v[k]));
+          }
+          st4(&S.sHt[prow][n], v[0], v[1], v[2], v[3]);
+          if constexpr (C::SPLIT) st4(&S.sHtlo[prow][n], lo[0], lo[1], lo[2], lo[3]);
+        }
+    };
+    // M^T tile k = (tb, si) in B-operand order: Gram tile G^T[s][t] times the decay from
+    // token s to token t and dt_s, zero above the diagonal, D on the diagonal.
+    auto build = [&](int k, const f32x16& gt) {
+      const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
+      const int tl = tb * 32 + col;
+      Frag<T> mh[2], ml[2];
+      if (si < tb) {
+        float mid = 0.f;
+#pragma unroll
+        for (int kk = 1; kk < NTB - 1; ++kk)
+          if (kk > si && kk < tb) mid += ctot[kk];
+        const float ut = exp2_hw(mid + sPi[tl]);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 vs = *reinterpret_cast<const f32x4*>(&sV[si * 32 + 8 * r4 + 4 * g2]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gt[r] * (vs[q] * ut));
+          }
+        }
+      } else {
+        const float pit = sPi[tl];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int s0 = tb * 32 + 8 * r4 + 4 * g2;
+          const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[s0]);
+          const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[s0]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            float v = (s0 + q <= tl) ? gt[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+            if (s0 + q == tl) v += Dh;
+            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
+          }
+        }
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        S.sM[k][m2][lane] = mh[m2];
+        if constexpr (C::SPLIT) S.sMlo[k][m2][lane] = ml[m2];
+      }
+    };
+    write_state();
+    if (nC > 0) load_chunk(0);
+    for (int c = 0; c < nC; ++c) {
+      fetch_gram(c);
+      stage(c);
+      __syncthreads();
+      // ---- S2: the chunk's M^T tiles
+#pragma unroll
+      for (int s = 0; s < OW::NB; ++s) {
+        const int k = OW::build(hw, s);
+        if (k >= 0) build(k, gram[s]);
+      }
+      fetch_bt(c);
+      __syncthreads();
+      // ---- S3: state update, then publish it for the next chunk
+      float lam = 0.f;
+#pragma unroll
+      for (int k = 0; k < NTB; ++k) lam += ctot[k];
+      const float eend = exp2_hw(lam);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
+#pragma unroll
+      for (int j = 0; j < C::KS_Q; ++j) {
+        const int k0 = xsw<Q>(prow, 16 * j + 8 * g2);
+        const Frag<T> bh = frag_contig(&S.sXW[prow][k0], 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) mma(hacc[i], af[i][j], bh);
+        if constexpr (C::SPLIT) {
+          const Frag<T> bl = frag_contig(&S.sXWlo[prow][k0], 0);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) mma(hacc[i], af[i][j], bl);
+        }
+      }
+      write_state();
+      __syncthreads();
+    }
+    if (h_final) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
+          h_final[sbase + n * SP + prow] = hacc[i][r];
+        }
+    }
+  }
+
+  // y of the last chunk out of sZ
+  if (nC > 0) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::XV; ++i) {
+      int s_, cv;
+      xcoord(i, s_, cv);
+      flush_y(nC, s_, cv);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- host side
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -715,11 +1187,23 @@ template <typename T, int Q>
 static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
   using C = Cfg<T, Q>;
   const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
-  const size_t scan_lds = sizeof(ScanSmem<T, Q>);
+  constexpr bool WIDE = Q > 128;
+  using ScanFn = void (*)(const T*, int64_t, const float*, const T*, int64_t, const float*, float*, T*,
+                          int64_t, const unsigned char*, int, int, int);
+  size_t scan_lds;
+  ScanFn scan;
+  if constexpr (WIDE) {
+    scan_lds = sizeof(WideSmem<T, Q>);
+    scan = &ssd_scan_wide_kernel<T, Q>;
+  } else {
+    scan_lds = sizeof(ScanSmem<T, Q>);
+    scan = &ssd_scan_kernel<T, Q>;
+  }
+  const void* scan_fn = reinterpret_cast<const void*>(scan);
   static bool configured = false;
   if (!configured) {
     hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q>), prep_lds);
-    if (e == hipSuccess) e = set_lds(reinterpret_cast<const void*>(&ssd_scan_kernel<T, Q>), scan_lds);
+    if (e == hipSuccess) e = set_lds(scan_fn, scan_lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -730,7 +1214,7 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC);
   }
-  hipLaunchKernelGGL((ssd_scan_kernel<T, Q>), dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
+  hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
                      static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
                      static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);

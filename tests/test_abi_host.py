@@ -134,14 +134,14 @@ def test_decode_needs_one_token():
 
 def test_workspace_size_formula():
     """Per (sequence, group, chunk): fp32 causal Gram tiles + B^T and C operand tiles;
-    per (sequence, head, chunk): dt and its prefix sums."""
+    per (sequence, head, chunk): dt, its prefix sums and per-token decay weights."""
     for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_BF16, 2, 256),
                           (m2.MAMBA2_F32, 4, 64)):
         d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
         t = chunk // 32
         rec = 4 * 1024 * t * (t + 1) // 2 + 2 * 128 * chunk * es
         nc = -(-1000 // chunk)
-        assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 8 * chunk)
+        assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 12 * chunk)
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(chunk=100)) == 0
     assert m2.lib.mamba2_ssd_prefill_workspace_bytes(None) == 0
