@@ -2,8 +2,10 @@
 // Mamba-2 block ("conv window 4": hyper.ai summary of arXiv 2508.14444, section
 // "方法"; neurohive article, section "Архитектура").
 //
-// HBM-bound: each io element is read once (plus a 3-token halo per tile) and
-// written once. A thread owns one 16-byte column of channels (8 bf16 or 4 f32)
+// HBM-bound: each io element is read once (plus a 3-token halo per 128-token
+// tile) and written once. SiLU uses the hardware exp2 and reciprocal (a few
+// fp32 ulps, far below the bf16 rounding of the output); with the accurate
+// library calls the kernel was bound by their instruction count. A thread owns one 16-byte column of channels (8 bf16 or 4 f32)
 // over a tile of tokens and slides the 4-tap window along time in registers,
 // so loads and stores are whole 16-byte vectors and a wave covers 1 KiB of
 // contiguous channels per row.
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
   }
   Vec<T> e0 = hist[0], e1 = hist[1], e2 = hist[2];
 
-  constexpr int U = 4;
+  constexpr int U = 16;   // loads in flight per thread
   int t = t0;
   for (; t + U <= t1; t += U) {
     Vec<T> cur[U];
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
       for (int i = 0; i < VE; ++i) {
         float v = bs[i] + wt[i][0] * e0.get(i) + wt[i][1] * e1.get(i) + wt[i][2] * e2.get(i) +
                   wt[i][3] * cur[k].get(i);
-        o.set(i, silu_f(v));
+        o.set(i, silu_fast(v));
       }
       st16(ob + (int64_t)(t + k) * out_stride, o);
       e0 = e1; e1 = e2; e2 = cur[k];
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
     for (int i = 0; i < VE; ++i) {
       float v = bs[i] + wt[i][0] * e0.get(i) + wt[i][1] * e1.get(i) + wt[i][2] * e2.get(i) +
                 wt[i][3] * cur.get(i);
-      o.set(i, silu_f(v));
+      o.set(i, silu_fast(v));
     }
     st16(ob + (int64_t)t * out_stride, o);
     e0 = e1; e1 = e2; e2 = cur;
@@ -103,7 +105,7 @@ template <typename T>
 static hipError_t launch_t(const void* u, int64_t u_stride, const float* w, const float* bias,
                            void* conv_state, void* out, int64_t out_stride, int B, int L, int Cc,
                            hipStream_t stream) {
-  constexpr int TT = 64;
+  constexpr int TT = 128;
   constexpr int VE = Vec<T>::VE;
   dim3 grid((Cc / VE + CONV_THREADS - 1) / CONV_THREADS, (L + TT - 1) / TT, B);
   hipLaunchKernelGGL((conv1d_kernel<T, TT>), grid, dim3(CONV_THREADS), 0, stream,
