@@ -164,6 +164,24 @@ __device__ __forceinline__ Frag<float> frag_accrows2(const float* a, const float
   return f;
 }
 
+// hi + lo split of 8 fp32 values into two operand fragments: hi = bf16(v), lo = bf16(v - hi)
+// (for fp32 io the fragment is v itself and lo is unused)
+__device__ __forceinline__ void frag_split(const f32x8& v, Frag<bf16>& hi, Frag<bf16>& lo) {
+  hi.v = __builtin_convertvector(v, bf16x8);
+  lo.v = __builtin_convertvector(v - __builtin_convertvector(hi.v, f32x8), bf16x8);
+}
+__device__ __forceinline__ void frag_split(const f32x8& v, Frag<float>& hi, Frag<float>&) { hi.v = v; }
+
+// the same for 4 values stored as io elements
+__device__ __forceinline__ void split4_store(bf16* hi_p, bf16* lo_p, const f32x4& v) {
+  const bf16x4 hi = __builtin_convertvector(v, bf16x4);
+  *reinterpret_cast<bf16x4*>(hi_p) = hi;
+  *reinterpret_cast<bf16x4*>(lo_p) = __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
+}
+__device__ __forceinline__ void split4_store(float* hi_p, float*, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(hi_p) = v;
+}
+
 template <typename T> __device__ __forceinline__ Frag<T> frag_zero() {
   Frag<T> f;
   for (int e = 0; e < 8; ++e) f.v[e] = from_f<T>(0.f);

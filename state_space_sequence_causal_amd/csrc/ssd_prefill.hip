@@ -884,22 +884,15 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
       }
     }
     if (tid < 3 * Q) S.sRec[tid] = rRec;
-    // exp2 of the decay from the end of block k to the end of the chunk
-    float esuf[NTB];
-    {
-      float acc = 0.f;
-#pragma unroll
-      for (int k = NTB - 1; k >= 0; --k) {
-        esuf[k] = exp2_hw(acc);
-        acc += ctot[k];
-      }
-    }
+    // w_s = v_s exp2(decay from the end of s's block to the end of the chunk); written as
+    // a sum of selects (a table of the per-block factors indexed by the lane's block would
+    // go through scratch memory)
     auto w_of = [&](int i, int s_) {
-      float e = esuf[0];
+      const int blk = s_ >> 5;
+      float after = 0.f;
 #pragma unroll
-      for (int k = 1; k < NTB; ++k)
-        if ((s_ >> 5) == k) e = esuf[k];
-      return rV[i] * e;
+      for (int k = 1; k < NTB; ++k) after += k > blk ? ctot[k] : 0.f;
+      return rV[i] * exp2_hw(after);
     };
     if constexpr (C::PAIRS) {
 #pragma unroll
