@@ -26,6 +26,9 @@
 //    H = exp(l_end) H + B^T (w x). Each SIMD hosts one wave of each kind; the state tiles
 //    are dealt so that the MFMA work per SIMD is balanced. Per chunk: stage (x, z, decay
 //    vectors) | barrier | compute | barrier | publish the new state.
+//    For bf16 io at chunk 64 a software-pipelined form of the same kernel (further down)
+//    overlaps the Y waves' chunk c with the H waves' chunk c and with the staging and tile
+//    builds of chunk c+1, at one barrier per chunk.
 //
 // Decay factors are formed in log2 units from prefix sums taken inside 32-token blocks, so
 // no factor is the difference of two large prefix sums: inside a block exp2(pi_t - pi_s);
@@ -845,14 +848,16 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
   auto load_chunk = [&](int c) {
     const int t0 = c * Q;
     const float* hr = hrec + (size_t)c * (3 * Q);
+    // Rows past the end of the sequence load the last row instead (finite values; their
+    // dt and v are zero, so they add nothing), which keeps the loads unconditional: a
+    // guarded load makes the compiler wait for it on the spot.
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
       int s_, cv;
       xcoord(i, s_, cv);
-      const int t = t0 + s_;
-      const bool ok = t < L;
-      rX[i] = ok ? ld16(xb + (row0 + t) * x_stride + cv * VE) : zero16<T>();
-      if (zb) rZ[i] = ok ? ld16(zb + (row0 + t) * z_stride + cv * VE) : zero16<T>();
+      const int t = min(t0 + s_, L - 1);
+      rX[i] = ld16(xb + (row0 + t) * x_stride + cv * VE);
+      if (zb) rZ[i] = ld16(zb + (row0 + t) * z_stride + cv * VE);
       rV[i] = hr[2 * Q + s_];
     }
     if (tid < 3 * Q) rRec = hr[tid];
@@ -1171,6 +1176,362 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
   }
 }
 
+// ---------------------------------------------------------------------------- pipelined scan, chunk 64
+// bf16 io, chunk 64. One barrier per chunk: in iteration c the Y waves compute chunk c's
+// outputs and the H waves advance the state to H_c, while every wave also stages chunk c+1
+// (x^T, (w x)^T hi/lo, z, flush of y(c-1)) and three Y waves build chunk c+1's masked decay
+// tiles. Everything chunk c+1 needs is written into the other half of double-buffered LDS
+// tiles, and the state is published into the other half of a double-buffered H^T, so the
+// only synchronisation is the barrier that ends the iteration. The dt / pi / v records are
+// staged two chunks ahead (three buffers) so that tile builds never wait for staging of
+// the same iteration.
+//   Y wave y (0..3): Y^T tile (token block y >> 1, p-block y & 1).
+//                    Y waves 0, 1, 2 also build chunk c+1's M^T tiles 0 (diagonal 0),
+//                    2 (diagonal 1) and 1 (block 1 from block 0).
+//   H wave w (0..3): state tiles (row blocks w >> 1 and (w >> 1) + 2, p-block w & 1).
+// LDS tiles are unpadded with XOR swizzles chosen so that the MFMA operand reads (16 bytes
+// per lane, 32 rows per instruction) and the state writes are bank-conflict free.
+constexpr int P64 = 64;
+__device__ __forceinline__ int xs64(int p, int s) { return s ^ (8 * ((p ^ (p >> 2)) & 7)); }
+__device__ __forceinline__ int hsw(int p, int n) { return n ^ (8 * (p & 15)); }
+
+struct Pipe64Smem {
+  bf16 sXt[2][SP][P64];                     // x^T by chunk parity (xs64)
+  bf16 sXW[2][SP][P64];                     // (w x)^T hi (xs64)
+  bf16 sXWlo[2][SP][P64];                   //         lo
+  bf16 sZ[2][P64][SP];                      // z, then y (zpos)
+  Frag<bf16> sM[2][3][2][64];               // M^T tiles [parity][tile][k step][lane]
+  Frag<bf16> sMlo[2][3][2][64];
+  bf16 sHt[2][SP][SN];                      // H^T hi by chunk parity (hsw)
+  bf16 sHtlo[2][SP][SN];                    //     lo
+  float sRec[3][3 * P64];                   // dt | pi | v, chunk c in slot c % 3
+};
+
+__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
+                       const bf16* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
+                       bf16* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
+                       int L, int H, int G) {
+  using T = bf16;
+  using C = Cfg<T, P64>;
+  constexpr int Q = P64;
+  extern __shared__ __align__(16) unsigned char scan_smem[];
+  Pipe64Smem& S = *reinterpret_cast<Pipe64Smem*>(scan_smem);
+
+  const int id = xcd_local_order(blockIdx.x, gridDim.x);
+  const int b = id / H, h = id % H;
+  const int g = h / (H / G);
+  const int nC = (L + Q - 1) / Q;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g2 = lane >> 5;
+  const bool ywave = wave < 4;
+
+  const int64_t row0 = (int64_t)b * L;
+  const T* xb = x + h * SP;
+  const T* zb = z ? z + h * SP : nullptr;
+  T* yb = y + h * SP;
+  const float Dh = D ? D[h] : 0.f;
+  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
+  const float* hrec = reinterpret_cast<const float*>(
+      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
+      ((size_t)b * H + h) * nC * C::HREC_BYTES);
+
+  // ------------------------------------------------------------ staging (all threads)
+  // thread: token pair (s0, s0 + 1) = 2 (tid / 16), columns p0 .. p0 + 3 = 4 (tid % 16)
+  const int s0 = 2 * (tid >> 4), p0 = 4 * (tid & 15);
+  Raw4<T> rX[2], rZ[2];
+  float rV[2], rRec, tot[2];
+  auto load_set = [&](int c) {       // x, z, v of this thread's tokens and the block totals
+    const float* hr = hrec + (size_t)c * (3 * Q);
+    // Rows past the end of the sequence load the last row instead (finite values; their
+    // dt and v are zero, so they add nothing), which keeps the loads unconditional: a
+    // guarded load makes the compiler wait for it on the spot.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = min(c * Q + s0 + k, L - 1);
+      rX[k] = ld4(xb + (row0 + t) * x_stride + p0);
+      if (zb) rZ[k] = ld4(zb + (row0 + t) * z_stride + p0);
+      rV[k] = hr[2 * Q + s0 + k];
+    }
+    tot[0] = hr[Q + 31];
+    tot[1] = hr[Q + 63];
+  };
+  auto load_rec = [&](int c) {       // every thread loads (a clamped word) so the load is unconditional
+    rRec = hrec[(size_t)c * (3 * Q) + min(tid, 3 * Q - 1)];
+  };
+  auto put_rec = [&](int c) {
+    if (tid < 3 * Q) S.sRec[c % 3][tid] = rRec;
+  };
+  auto flush_y = [&](int c, bool full) {   // y of chunk c out of sZ[c & 1]
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int s = s0 + k, t = c * Q + s;
+      const Raw4<T> v = ld4(&S.sZ[c & 1][s][zpos<T>(s, p0)]);
+      if (full || t < L) *reinterpret_cast<bf16x4*>(yb + (row0 + t) * y_stride + p0) = v.v;
+    }
+  };
+  // x^T, (w x)^T and z of chunk c (its set in registers, block totals ct) into buffers c & 1
+  auto stage = [&](int c, const float* ct) {
+    const int buf = c & 1;
+    if (zb) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos<T>(s0 + k, p0)]) = rZ[k].v;
+    }
+    // w_s = v_s exp2(decay from the end of s's block to the chunk end): block 0 -> tot_1
+    const float w0 = rV[0] * (s0 < 32 ? exp2_hw(ct[1]) : 1.f);
+    const float w1 = rV[1] * (s0 < 32 ? exp2_hw(ct[1]) : 1.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const T x0 = rX[0].v[e], x1 = rX[1].v[e];
+      const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
+      const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
+      const int p = p0 + e, sw = xs64(p, s0);
+      st_pair(&S.sXt[buf][p][sw], x0, x1);
+      st_pair(&S.sXW[buf][p][sw], h0_, h1_);
+      st_pair(&S.sXWlo[buf][p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
+    }
+  };
+
+  // block totals: ctot_cur of chunk c; `tot` (from the set in flight) of chunk c + 1
+  float ctot_cur[2] = {0.f, 0.f};
+
+  if (ywave) {
+    // ========================================================== Y waves
+    const int tb = wave >> 1, pb = wave & 1;
+    const int prow = pb * 32 + col, tl = tb * 32 + col;
+    Frag<T> cf[C::KS_N];
+    f32x16 gram;
+    const int kb = wave == 0 ? 0 : wave == 1 ? 2 : wave == 2 ? 1 : -1;   // M^T tile built here
+    auto fetch_gram = [&](int c) {    // unconditional: wave 3 (no tile) loads tile 0
+      gram = load_tile16(reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
+                         ((size_t)max(kb, 0) * 64 + lane) * 16);
+    };
+    // M^T tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t and dt_s,
+    // zero above the diagonal, D on the diagonal; record and block totals of chunk c
+    auto build = [&](int c) {
+      if (kb < 0) return;
+      const float* rec = S.sRec[c % 3];
+      const float* sDt = rec;
+      const float* sPi = rec + Q;
+      const float* sV = rec + 2 * Q;
+      const int tb = kb == 0 ? 0 : 1, si = kb == 2 ? 1 : 0;
+      const int tl = tb * 32 + col;
+      Frag<T> mh[2], ml[2];
+      if (si < tb) {
+        // block 0 -> block 1: v_s exp2(pi_t)
+        const float ut = exp2_hw(sPi[tl]);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 vs = *reinterpret_cast<const f32x4*>(&sV[8 * r4 + 4 * g2]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gram[r] * (vs[q] * ut));
+          }
+        }
+      } else {
+        const float pit = sPi[tl];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int sr = tb * 32 + 8 * r4 + 4 * g2;
+          const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
+          const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            float v = (sr + q <= tl) ? gram[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+            if (sr + q == tl) v += Dh;
+            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
+          }
+        }
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        S.sM[c & 1][kb][m2][lane] = mh[m2];
+        S.sMlo[c & 1][kb][m2][lane] = ml[m2];
+      }
+    };
+    auto fetch_c = [&](int c) {
+      const unsigned char* cfp = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES;
+#pragma unroll
+      for (int j = 0; j < C::KS_N; ++j)
+        cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
+    };
+    // prologue: chunk 0 staged, records 0 and 1, chunk 1's set in flight
+    if (nC > 0) {
+      load_set(0);
+      load_rec(0);
+      put_rec(0);
+      load_rec(min(1, nC - 1));
+      put_rec(1);
+      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
+      stage(0, ctot_cur);
+      fetch_c(0);
+      fetch_gram(0);
+      load_set(min(1, nC - 1));
+      load_rec(min(2, nC - 1));
+    }
+    __syncthreads();
+    if (nC > 0) {
+      build(0);
+      fetch_gram(min(1, nC - 1));
+    }
+    __syncthreads();
+    for (int c = 0; c < nC; ++c) {
+      const int cur = c & 1, prv = cur ^ 1;
+      // ---- chunk c: carried state, scaled by exp2(lambda_t)
+      f32x16 acc = {};
+#pragma unroll
+      for (int j = 0; j < C::KS_N; ++j) {
+        const int n = hsw(prow, 16 * j + 8 * g2);
+        mma(acc, frag_contig(&S.sHt[prv][prow][n], 0), cf[j]);
+        mma(acc, frag_contig(&S.sHtlo[prv][prow][n], 0), cf[j]);
+      }
+      const float et = exp2_hw((tb ? ctot_cur[0] : 0.f) + S.sRec[c % 3][Q + tl]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] *= et;
+      fetch_c(min(c + 1, nC - 1));
+      // ---- intra-chunk part: Y^T += X^T M^T over source blocks si <= tb
+#pragma unroll
+      for (int si = 0; si < 2; ++si) {
+        if (si <= tb) {
+          const int k = tb * (tb + 1) / 2 + si;
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2) {
+            const int sa = si * 32 + 16 * m2 + 4 * g2;
+            const Frag<T> xa = frag_accrows2(&S.sXt[cur][prow][xs64(prow, sa)],
+                                             &S.sXt[cur][prow][xs64(prow, sa + 8)]);
+            mma(acc, xa, S.sM[cur][k][m2][lane]);
+            mma(acc, xa, S.sMlo[cur][k][m2][lane]);
+          }
+        }
+      }
+      // ---- gate and y into sZ[cur] (in place of z)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int r = 4 * r4;
+        T* zp = &S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)];
+        float gq[4] = {1.f, 1.f, 1.f, 1.f};
+        if (zb) {
+          const Raw4<T> zz = ld4(zp);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gq[q] = silu_fast(zz.get(q));
+        }
+        st4(zp, acc[r] * gq[0], acc[r + 1] * gq[1], acc[r + 2] * gq[2], acc[r + 3] * gq[3]);
+      }
+      // ---- chunk c + 1: tiles and staging. Memory operations are unconditional (chunk
+      // indices clamped; the last iteration stages a copy nobody reads), which keeps the
+      // compiler's count of outstanding loads exact across iterations.
+      build(c + 1);
+      fetch_gram(min(c + 2, nC - 1));
+      if (c >= 1) flush_y(c - 1, true);   // chunk c - 1 < nC - 1 is full
+      stage(c + 1, tot);
+      put_rec(c + 2);
+      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
+      load_set(min(c + 2, nC - 1));
+      load_rec(min(c + 3, nC - 1));
+      __syncthreads();
+    }
+  } else {
+    // ========================================================== H waves
+    const int hw = wave - 4;
+    const int pb = hw & 1, nb0 = hw >> 1;
+    const int prow = pb * 32 + col;
+    f32x16 hacc[2];
+    Frag<T> af[2][C::KS_Q];
+    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
+        hacc[i][r] = h0 ? h0[sbase + n * SP + prow] : 0.f;
+      }
+    auto fetch_bt = [&](int c) {
+      const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < C::KS_Q; ++j)
+          af[i][j] = ld_frag<T>(btf + ((size_t)((nb0 + 2 * i) * C::KS_Q + j) * 64 + lane) * C::FB);
+    };
+    auto publish = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int n = hsw(prow, (nb0 + 2 * i) * 32 + 8 * r4 + 4 * g2);
+          float v[4], lo[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[k] = hacc[i][4 * r4 + k];
+            lo[k] = v[k] - to_f(from_f<T>(v[k]));
+          }
+          st4(&S.sHt[buf][prow][n], v[0], v[1], v[2], v[3]);
+          st4(&S.sHtlo[buf][prow][n], lo[0], lo[1], lo[2], lo[3]);
+        }
+    };
+    publish(1);          // h0 is the state chunk 0 reads
+    if (nC > 0) {
+      load_set(0);
+      load_rec(0);
+      put_rec(0);
+      load_rec(min(1, nC - 1));
+      put_rec(1);
+      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
+      stage(0, ctot_cur);
+      fetch_bt(0);
+      load_set(min(1, nC - 1));
+      load_rec(min(2, nC - 1));
+    }
+    __syncthreads();
+    __syncthreads();   // the Y waves build chunk 0's tiles in between
+    for (int c = 0; c < nC; ++c) {
+      const int cur = c & 1;
+      // ---- state update to H_c, published into sHt[cur]
+      const float eend = exp2_hw(ctot_cur[0] + ctot_cur[1]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
+#pragma unroll
+      for (int j = 0; j < C::KS_Q; ++j) {
+        const int k0 = xs64(prow, 16 * j + 8 * g2);
+        const Frag<T> bh = frag_contig(&S.sXW[cur][prow][k0], 0);
+        const Frag<T> bl = frag_contig(&S.sXWlo[cur][prow][k0], 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          mma(hacc[i], af[i][j], bh);
+          mma(hacc[i], af[i][j], bl);
+        }
+      }
+      publish(cur);
+      fetch_bt(min(c + 1, nC - 1));
+      // ---- staging of chunk c + 1 (unconditional, as in the Y waves)
+      if (c >= 1) flush_y(c - 1, true);
+      stage(c + 1, tot);
+      put_rec(c + 2);
+      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
+      load_set(min(c + 2, nC - 1));
+      load_rec(min(c + 3, nC - 1));
+      __syncthreads();
+    }
+    if (h_final) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
+          h_final[sbase + n * SP + prow] = hacc[i][r];
+        }
+    }
+  }
+  // y of the last chunk
+  if (nC > 0) flush_y(nC - 1, false);
+}
+
 // ---------------------------------------------------------------------------- host side
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -1188,6 +1549,9 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (WIDE) {
     scan_lds = sizeof(WideSmem<T, Q>);
     scan = &ssd_scan_wide_kernel<T, Q>;
+  } else if constexpr (Q == 64 && sizeof(T) == 2) {
+    scan_lds = sizeof(Pipe64Smem);
+    scan = &ssd_scan64_kernel;
   } else {
     scan_lds = sizeof(ScanSmem<T, Q>);
     scan = &ssd_scan_kernel<T, Q>;
