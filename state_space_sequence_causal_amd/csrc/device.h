@@ -164,22 +164,35 @@ __device__ __forceinline__ Frag<float> frag_accrows2(const float* a, const float
   return f;
 }
 
-// hi + lo split of 8 fp32 values into two operand fragments: hi = bf16(v), lo = bf16(v - hi)
-// (for fp32 io the fragment is v itself and lo is unused)
-__device__ __forceinline__ void frag_split(const f32x8& v, Frag<bf16>& hi, Frag<bf16>& lo) {
-  hi.v = __builtin_convertvector(v, bf16x8);
-  lo.v = __builtin_convertvector(v - __builtin_convertvector(hi.v, f32x8), bf16x8);
+// ---------------------------------------------------------------- hi + lo splits
+// A computed fp32 operand v enters a bf16 MFMA as two bf16 values, hi = bf16(v) (RNE) and
+// lo = bf16(v - hi), which together hold v to about 2^-16. For a pair of values this costs
+// one pair conversion, two exact unpacks, two subtractions and a second pair conversion.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
-__device__ __forceinline__ void frag_split(const f32x8& v, Frag<float>& hi, Frag<float>&) { hi.v = v; }
-
-// the same for 4 values stored as io elements
-__device__ __forceinline__ void split4_store(bf16* hi_p, bf16* lo_p, const f32x4& v) {
-  const bf16x4 hi = __builtin_convertvector(v, bf16x4);
-  *reinterpret_cast<bf16x4*>(hi_p) = hi;
-  *reinterpret_cast<bf16x4*>(lo_p) = __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), bf16x4);
+struct Split2 {
+  uint32_t hi, lo;  // packed bf16 pairs, first value in the low half
+};
+__device__ __forceinline__ Split2 split2(float a, float b) {
+  const uint32_t h = pack_bf16(a, b);
+  const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+  return {h, pack_bf16(a - ha, b - hb)};
 }
-__device__ __forceinline__ void split4_store(float* hi_p, float*, const f32x4& v) {
-  *reinterpret_cast<f32x4*>(hi_p) = v;
+// 8 values into hi and lo operand fragments (element e of the fragment is v[e])
+__device__ __forceinline__ void frag_split(const float* v, Frag<bf16>& hi, Frag<bf16>& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const Split2 s = split2(v[2 * k], v[2 * k + 1]);
+    h[k] = s.hi;
+    l[k] = s.lo;
+  }
+  hi.v = __builtin_bit_cast(bf16x8, h);
+  lo.v = __builtin_bit_cast(bf16x8, l);
 }
 
 template <typename T> __device__ __forceinline__ Frag<T> frag_zero() {

@@ -26,9 +26,6 @@
 //    H = exp(l_end) H + B^T (w x). Each SIMD hosts one wave of each kind; the state tiles
 //    are dealt so that the MFMA work per SIMD is balanced. Per chunk: stage (x, z, decay
 //    vectors) | barrier | compute | barrier | publish the new state.
-//    For bf16 io at chunk 64 a software-pipelined form of the same kernel (further down)
-//    overlaps the Y waves' chunk c with the H waves' chunk c and with the staging and tile
-//    builds of chunk c+1, at one barrier per chunk.
 //
 // Decay factors are formed in log2 units from prefix sums taken inside 32-token blocks, so
 // no factor is the difference of two large prefix sums: inside a block exp2(pi_t - pi_s);
@@ -42,6 +39,8 @@
 // relative. With a single bf16 rounding the error of outputs dominated by one term reaches
 // 4e-2 to 2e-1 of rms(y) on these heavy-tailed outputs, outside the 2e-2 bar; with the
 // split it stays below 1e-4. The fp32 io mode uses fp32 MFMAs and needs no split.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -1177,21 +1176,21 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 }
 
 // ---------------------------------------------------------------------------- pipelined scan, chunk 64
-// bf16 io, chunk 64. One barrier per chunk: in iteration c the Y waves compute chunk c's
-// outputs and the H waves advance the state to H_c, while every wave also stages chunk c+1
-// (x^T, (w x)^T hi/lo, z, flush of y(c-1)) and three Y waves build chunk c+1's masked decay
-// tiles. Everything chunk c+1 needs is written into the other half of double-buffered LDS
-// tiles, and the state is published into the other half of a double-buffered H^T, so the
-// only synchronisation is the barrier that ends the iteration. The dt / pi / v records are
-// staged two chunks ahead (three buffers) so that tile builds never wait for staging of
-// the same iteration.
-//   Y wave y (0..3): Y^T tile (token block y >> 1, p-block y & 1).
-//                    Y waves 0, 1, 2 also build chunk c+1's M^T tiles 0 (diagonal 0),
-//                    2 (diagonal 1) and 1 (block 1 from block 0).
-//   H wave w (0..3): state tiles (row blocks w >> 1 and (w >> 1) + 2, p-block w & 1).
-// LDS tiles are unpadded with XOR swizzles chosen so that the MFMA operand reads (16 bytes
-// per lane, 32 rows per instruction) and the state writes are bank-conflict free.
+// bf16 io, chunk 64, 16 waves. One barrier per chunk. In iteration c:
+//   Y waves 0..3:   chunk c's outputs, Y^T tile (token block y >> 1, p-block y & 1):
+//                   H^T C^T scaled by exp2(lambda_t), plus X^T M^T, gated, into sZ.
+//   H waves 4..7:   the state to H_c (tiles: row blocks w >> 1 and (w >> 1) + 2, p-block w & 1),
+//                   published into the other half of a double-buffered H^T.
+//   helper waves 8..15: chunk c+1's staging (flush of y(c-1), z, x^T, (w x)^T hi/lo), its
+//                   masked decay tiles M^T (waves 8, 9, 10: tiles 0, 2, 1), the dt / pi / v
+//                   record of chunk c+2, and the loads for the chunks after.
+// Everything chunk c+1 needs goes to the other half of double-buffered LDS tiles, so the
+// barrier that ends the iteration is the only synchronisation; records are staged two chunks
+// ahead (three buffers). Four waves per SIMD (one of each kind plus two helpers) hide each
+// other's latencies. LDS tiles are unpadded, with XOR swizzles that make the MFMA operand
+// reads (16 bytes per lane, 32 rows per instruction) and the state writes conflict free.
 constexpr int P64 = 64;
+constexpr int P64_THREADS = 1024;
 __device__ __forceinline__ int xs64(int p, int s) { return s ^ (8 * ((p ^ (p >> 2)) & 7)); }
 __device__ __forceinline__ int hsw(int p, int n) { return n ^ (8 * (p & 15)); }
 
@@ -1207,7 +1206,7 @@ struct Pipe64Smem {
   float sRec[3][3 * P64];                   // dt | pi | v, chunk c in slot c % 3
 };
 
-__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
                        const bf16* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
                        bf16* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
@@ -1225,163 +1224,32 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g2 = lane >> 5;
-  const bool ywave = wave < 4;
 
   const int64_t row0 = (int64_t)b * L;
-  const T* xb = x + h * SP;
-  const T* zb = z ? z + h * SP : nullptr;
-  T* yb = y + h * SP;
-  const float Dh = D ? D[h] : 0.f;
   const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
   const float* hrec = reinterpret_cast<const float*>(
       ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
       ((size_t)b * H + h) * nC * C::HREC_BYTES);
+  // block totals of chunk c (pi at the ends of its two 32-token blocks), from LDS
+  auto tot_of = [&](int c, int k) { return S.sRec[c % 3][Q + 32 * k + 31]; };
 
-  // ------------------------------------------------------------ staging (all threads)
-  // thread: token pair (s0, s0 + 1) = 2 (tid / 16), columns p0 .. p0 + 3 = 4 (tid % 16)
-  const int s0 = 2 * (tid >> 4), p0 = 4 * (tid & 15);
-  Raw4<T> rX[2], rZ[2];
-  float rV[2], rRec, tot[2];
-  auto load_set = [&](int c) {       // x, z, v of this thread's tokens and the block totals
-    const float* hr = hrec + (size_t)c * (3 * Q);
-    // Rows past the end of the sequence load the last row instead (finite values; their
-    // dt and v are zero, so they add nothing), which keeps the loads unconditional: a
-    // guarded load makes the compiler wait for it on the spot.
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int t = min(c * Q + s0 + k, L - 1);
-      rX[k] = ld4(xb + (row0 + t) * x_stride + p0);
-      if (zb) rZ[k] = ld4(zb + (row0 + t) * z_stride + p0);
-      rV[k] = hr[2 * Q + s0 + k];
-    }
-    tot[0] = hr[Q + 31];
-    tot[1] = hr[Q + 63];
-  };
-  auto load_rec = [&](int c) {       // every thread loads (a clamped word) so the load is unconditional
-    rRec = hrec[(size_t)c * (3 * Q) + min(tid, 3 * Q - 1)];
-  };
-  auto put_rec = [&](int c) {
-    if (tid < 3 * Q) S.sRec[c % 3][tid] = rRec;
-  };
-  auto flush_y = [&](int c, bool full) {   // y of chunk c out of sZ[c & 1]
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int s = s0 + k, t = c * Q + s;
-      const Raw4<T> v = ld4(&S.sZ[c & 1][s][zpos<T>(s, p0)]);
-      if (full || t < L) *reinterpret_cast<bf16x4*>(yb + (row0 + t) * y_stride + p0) = v.v;
-    }
-  };
-  // x^T, (w x)^T and z of chunk c (its set in registers, block totals ct) into buffers c & 1
-  auto stage = [&](int c, const float* ct) {
-    const int buf = c & 1;
-    if (zb) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos<T>(s0 + k, p0)]) = rZ[k].v;
-    }
-    // w_s = v_s exp2(decay from the end of s's block to the chunk end): block 0 -> tot_1
-    const float w0 = rV[0] * (s0 < 32 ? exp2_hw(ct[1]) : 1.f);
-    const float w1 = rV[1] * (s0 < 32 ? exp2_hw(ct[1]) : 1.f);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const T x0 = rX[0].v[e], x1 = rX[1].v[e];
-      const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
-      const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
-      const int p = p0 + e, sw = xs64(p, s0);
-      st_pair(&S.sXt[buf][p][sw], x0, x1);
-      st_pair(&S.sXW[buf][p][sw], h0_, h1_);
-      st_pair(&S.sXWlo[buf][p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
-    }
-  };
-
-  // block totals: ctot_cur of chunk c; `tot` (from the set in flight) of chunk c + 1
-  float ctot_cur[2] = {0.f, 0.f};
-
-  if (ywave) {
+  if (wave < 4) {
     // ========================================================== Y waves
     const int tb = wave >> 1, pb = wave & 1;
     const int prow = pb * 32 + col, tl = tb * 32 + col;
     Frag<T> cf[C::KS_N];
-    f32x16 gram;
-    const int kb = wave == 0 ? 0 : wave == 1 ? 2 : wave == 2 ? 1 : -1;   // M^T tile built here
-    auto fetch_gram = [&](int c) {    // unconditional: wave 3 (no tile) loads tile 0
-      gram = load_tile16(reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
-                         ((size_t)max(kb, 0) * 64 + lane) * 16);
-    };
-    // M^T tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t and dt_s,
-    // zero above the diagonal, D on the diagonal; record and block totals of chunk c
-    auto build = [&](int c) {
-      if (kb < 0) return;
-      const float* rec = S.sRec[c % 3];
-      const float* sDt = rec;
-      const float* sPi = rec + Q;
-      const float* sV = rec + 2 * Q;
-      const int tb = kb == 0 ? 0 : 1, si = kb == 2 ? 1 : 0;
-      const int tl = tb * 32 + col;
-      Frag<T> mh[2], ml[2];
-      if (si < tb) {
-        // block 0 -> block 1: v_s exp2(pi_t)
-        const float ut = exp2_hw(sPi[tl]);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 vs = *reinterpret_cast<const f32x4*>(&sV[8 * r4 + 4 * g2]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gram[r] * (vs[q] * ut));
-          }
-        }
-      } else {
-        const float pit = sPi[tl];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int sr = tb * 32 + 8 * r4 + 4 * g2;
-          const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
-          const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            float v = (sr + q <= tl) ? gram[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
-            if (sr + q == tl) v += Dh;
-            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
-          }
-        }
-      }
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        S.sM[c & 1][kb][m2][lane] = mh[m2];
-        S.sMlo[c & 1][kb][m2][lane] = ml[m2];
-      }
-    };
     auto fetch_c = [&](int c) {
       const unsigned char* cfp = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES;
 #pragma unroll
       for (int j = 0; j < C::KS_N; ++j)
         cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
     };
-    // prologue: chunk 0 staged, records 0 and 1, chunk 1's set in flight
-    if (nC > 0) {
-      load_set(0);
-      load_rec(0);
-      put_rec(0);
-      load_rec(min(1, nC - 1));
-      put_rec(1);
-      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
-      stage(0, ctot_cur);
-      fetch_c(0);
-      fetch_gram(0);
-      load_set(min(1, nC - 1));
-      load_rec(min(2, nC - 1));
-    }
+    if (nC > 0) fetch_c(0);
     __syncthreads();
-    if (nC > 0) {
-      build(0);
-      fetch_gram(min(1, nC - 1));
-    }
     __syncthreads();
     for (int c = 0; c < nC; ++c) {
       const int cur = c & 1, prv = cur ^ 1;
-      // ---- chunk c: carried state, scaled by exp2(lambda_t)
+      // ---- carried state, scaled by exp2(lambda_t)
       f32x16 acc = {};
 #pragma unroll
       for (int j = 0; j < C::KS_N; ++j) {
@@ -1389,7 +1257,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         mma(acc, frag_contig(&S.sHt[prv][prow][n], 0), cf[j]);
         mma(acc, frag_contig(&S.sHtlo[prv][prow][n], 0), cf[j]);
       }
-      const float et = exp2_hw((tb ? ctot_cur[0] : 0.f) + S.sRec[c % 3][Q + tl]);
+      const float et = exp2_hw((tb ? tot_of(c, 0) : 0.f) + S.sRec[c % 3][Q + tl]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] *= et;
       fetch_c(min(c + 1, nC - 1));
@@ -1414,27 +1282,16 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         const int r = 4 * r4;
         T* zp = &S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)];
         float gq[4] = {1.f, 1.f, 1.f, 1.f};
-        if (zb) {
+        if (z) {
           const Raw4<T> zz = ld4(zp);
 #pragma unroll
           for (int q = 0; q < 4; ++q) gq[q] = silu_fast(zz.get(q));
         }
         st4(zp, acc[r] * gq[0], acc[r + 1] * gq[1], acc[r + 2] * gq[2], acc[r + 3] * gq[3]);
       }
-      // ---- chunk c + 1: tiles and staging. Memory operations are unconditional (chunk
-      // indices clamped; the last iteration stages a copy nobody reads), which keeps the
-      // compiler's count of outstanding loads exact across iterations.
-      build(c + 1);
-      fetch_gram(min(c + 2, nC - 1));
-      if (c >= 1) flush_y(c - 1, true);   // chunk c - 1 < nC - 1 is full
-      stage(c + 1, tot);
-      put_rec(c + 2);
-      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
-      load_set(min(c + 2, nC - 1));
-      load_rec(min(c + 3, nC - 1));
       __syncthreads();
     }
-  } else {
+  } else if (wave < 8) {
     // ========================================================== H waves
     const int hw = wave - 4;
     const int pb = hw & 1, nb0 = hw >> 1;
@@ -1463,35 +1320,20 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int n = hsw(prow, (nb0 + 2 * i) * 32 + 8 * r4 + 4 * g2);
-          float v[4], lo[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k] = hacc[i][4 * r4 + k];
-            lo[k] = v[k] - to_f(from_f<T>(v[k]));
-          }
-          st4(&S.sHt[buf][prow][n], v[0], v[1], v[2], v[3]);
-          st4(&S.sHtlo[buf][prow][n], lo[0], lo[1], lo[2], lo[3]);
+          const Split2 a = split2(hacc[i][4 * r4], hacc[i][4 * r4 + 1]);
+          const Split2 d = split2(hacc[i][4 * r4 + 2], hacc[i][4 * r4 + 3]);
+          *reinterpret_cast<uint2*>(&S.sHt[buf][prow][n]) = make_uint2(a.hi, d.hi);
+          *reinterpret_cast<uint2*>(&S.sHtlo[buf][prow][n]) = make_uint2(a.lo, d.lo);
         }
     };
     publish(1);          // h0 is the state chunk 0 reads
-    if (nC > 0) {
-      load_set(0);
-      load_rec(0);
-      put_rec(0);
-      load_rec(min(1, nC - 1));
-      put_rec(1);
-      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
-      stage(0, ctot_cur);
-      fetch_bt(0);
-      load_set(min(1, nC - 1));
-      load_rec(min(2, nC - 1));
-    }
+    if (nC > 0) fetch_bt(0);
     __syncthreads();
-    __syncthreads();   // the Y waves build chunk 0's tiles in between
+    __syncthreads();
     for (int c = 0; c < nC; ++c) {
       const int cur = c & 1;
       // ---- state update to H_c, published into sHt[cur]
-      const float eend = exp2_hw(ctot_cur[0] + ctot_cur[1]);
+      const float eend = exp2_hw(tot_of(c, 0) + tot_of(c, 1));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1509,13 +1351,6 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       }
       publish(cur);
       fetch_bt(min(c + 1, nC - 1));
-      // ---- staging of chunk c + 1 (unconditional, as in the Y waves)
-      if (c >= 1) flush_y(c - 1, true);
-      stage(c + 1, tot);
-      put_rec(c + 2);
-      ctot_cur[0] = tot[0]; ctot_cur[1] = tot[1];
-      load_set(min(c + 2, nC - 1));
-      load_rec(min(c + 3, nC - 1));
       __syncthreads();
     }
     if (h_final) {
@@ -1527,9 +1362,172 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           h_final[sbase + n * SP + prow] = hacc[i][r];
         }
     }
+  } else {
+    // ========================================================== helper waves
+    const int htid = tid - 512, hv = wave - 8;
+    const T* xb = x + h * SP;
+    T* yb = y + h * SP;
+    const float Dh = D ? D[h] : 0.f;
+    // thread: token pair (s0, s0 + 1) = 2 (htid / 16), columns p0 .. p0 + 3 = 4 (htid % 16)
+    const int s0 = 2 * (htid >> 4), p0 = 4 * (htid & 15);
+    // per-thread element offsets inside a chunk's rows fit 32 bits; chunk bases are uniform
+    const uint32_t xs = (uint32_t)x_stride, zs = (uint32_t)z_stride, ys = (uint32_t)y_stride;
+    // M^T tiles: helper waves 0, 1, 2 build tiles 0 (diagonal 0), 2 (diagonal 1), 1 (block 1
+    // from block 0) and carry the dt / pi / v records (3Q words, a word a thread); the other
+    // helpers only stage.
+    const int kb = hv == 0 ? 0 : hv == 1 ? 2 : hv == 2 ? 1 : -1;
+    // Each role (builder or not, with or without z) runs its own copy of the loop, so that
+    // every copy issues a fixed sequence of memory operations and the compiler's count of
+    // outstanding loads stays exact: a merged count would wait for loads just issued.
+    auto helpers = [&](auto builder_tag, auto z_tag) {
+      constexpr bool BUILDER = decltype(builder_tag)::value;
+      constexpr bool HAS_Z = decltype(z_tag)::value;
+      const T* zb = HAS_Z ? z + h * SP : nullptr;
+      Raw4<T> rX[2], rZ[2];
+      float rRec = 0.f;
+      f32x16 gram;
+      auto load_set = [&](int c) {       // x and z of this thread's tokens
+        const int64_t r0 = row0 + (int64_t)c * Q;
+        const T* xc = xb + r0 * x_stride;
+        // Rows past the end of the sequence load the last row instead (finite values; their
+        // dt and v are zero, so they add nothing), which keeps the loads unconditional.
+        const int lim = L - 1 - c * Q;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t s = (uint32_t)min(s0 + k, lim);
+          rX[k] = ld4(xc + (s * xs + p0));
+          if constexpr (HAS_Z) rZ[k] = ld4(zb + r0 * z_stride + (s * zs + p0));
+        }
+      };
+      auto load_rec = [&](int c) {
+        if constexpr (BUILDER) rRec = hrec[(size_t)c * (3 * Q) + htid];
+      };
+      auto put_rec = [&](int c) {
+        if constexpr (BUILDER) S.sRec[c % 3][htid] = rRec;
+      };
+      auto flush_y = [&](int c, bool full) {   // y of chunk c out of sZ[c & 1]
+        T* yc = yb + (row0 + (int64_t)c * Q) * y_stride;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int s = s0 + k;
+          const Raw4<T> v = ld4(&S.sZ[c & 1][s][zpos<T>(s, p0)]);
+          if (full || c * Q + s < L) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
+        }
+      };
+      // x^T, (w x)^T and z of chunk c (its set in registers) into buffers c & 1
+      auto stage = [&](int c) {
+        const int buf = c & 1;
+        if constexpr (HAS_Z) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos<T>(s0 + k, p0)]) = rZ[k].v;
+        }
+        // w_s = v_s exp2(decay from the end of s's block to the chunk end): block 0 -> tot_1
+        const float* rec = S.sRec[c % 3];
+        const float2 vs = *reinterpret_cast<const float2*>(&rec[2 * Q + s0]);
+        const float wb = s0 < 32 ? exp2_hw(rec[Q + 63]) : 1.f;
+        const float w0 = vs.x * wb, w1 = vs.y * wb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const T x0 = rX[0].v[e], x1 = rX[1].v[e];
+          const Split2 v = split2(to_f(x0) * w0, to_f(x1) * w1);
+          const int p = p0 + e, sw = xs64(p, s0);
+          st_pair(&S.sXt[buf][p][sw], x0, x1);
+          *reinterpret_cast<uint32_t*>(&S.sXW[buf][p][sw]) = v.hi;
+          *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
+        }
+      };
+      auto fetch_gram = [&](int c) {
+        if constexpr (BUILDER)
+          gram = load_tile16(reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
+                             ((size_t)kb * 64 + lane) * 16);
+      };
+      // tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t and dt_s, zero
+      // above the diagonal, D on the diagonal
+      auto build = [&](int c) {
+        if constexpr (BUILDER) {
+          const float* rec = S.sRec[c % 3];
+          const float* sDt = rec;
+          const float* sPi = rec + Q;
+          const float* sV = rec + 2 * Q;
+          const int tb = kb == 0 ? 0 : 1, si = kb == 2 ? 1 : 0;
+          const int tl = tb * 32 + col;
+          float mv[16];
+          if (si < tb) {
+            // block 0 -> block 1: v_s exp2(pi_t)
+            const float ut = exp2_hw(sPi[tl]);
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 vq = *reinterpret_cast<const f32x4*>(&sV[8 * r4 + 4 * g2]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) mv[4 * r4 + q] = gram[4 * r4 + q] * (vq[q] * ut);
+            }
+          } else {
+            const float pit = sPi[tl];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int sr = tb * 32 + 8 * r4 + 4 * g2;
+              const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
+              const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int r = 4 * r4 + q;
+                float v = (sr + q <= tl) ? gram[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+                if (sr + q == tl) v += Dh;
+                mv[r] = v;
+              }
+            }
+          }
+#pragma unroll
+          for (int m2 = 0; m2 < 2; ++m2) {
+            Frag<T> mh, ml;
+            frag_split(mv + 8 * m2, mh, ml);
+            S.sM[c & 1][kb][m2][lane] = mh;
+            S.sMlo[c & 1][kb][m2][lane] = ml;
+          }
+        }
+      };
+      // prologue: records 0 and 1 into LDS; then chunk 0 staged and its tiles built, chunk 1's
+      // set in flight
+      if (nC > 0) {
+        load_set(0);
+        load_rec(0);
+        put_rec(0);
+        load_rec(min(1, nC - 1));
+        put_rec(1);
+        fetch_gram(0);
+        load_rec(min(2, nC - 1));
+      }
+      __syncthreads();
+      if (nC > 0) {
+        stage(0);
+        load_set(min(1, nC - 1));
+        build(0);
+        fetch_gram(min(1, nC - 1));
+      }
+      __syncthreads();
+      for (int c = 0; c < nC; ++c) {
+        // ---- chunk c + 1: tiles and staging. Chunk indices are clamped, so every iteration
+        // issues the same memory operations (the last stages a copy nobody reads).
+        build(c + 1);
+        fetch_gram(min(c + 2, nC - 1));
+        if (c >= 1) flush_y(c - 1, true);   // chunk c - 1 < nC - 1 is full
+        stage(c + 1);
+        put_rec(c + 2);
+        load_set(min(c + 2, nC - 1));
+        load_rec(min(c + 3, nC - 1));
+        __syncthreads();
+      }
+      if (nC > 0) flush_y(nC - 1, false);   // y of the last chunk
+    };
+    if (kb >= 0) {
+      if (z) helpers(std::true_type{}, std::true_type{});
+      else helpers(std::true_type{}, std::false_type{});
+    } else {
+      if (z) helpers(std::false_type{}, std::true_type{});
+      else helpers(std::false_type{}, std::false_type{});
+    }
   }
-  // y of the last chunk
-  if (nC > 0) flush_y(nC - 1, false);
 }
 
 // ---------------------------------------------------------------------------- host side
@@ -1571,7 +1569,8 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC);
   }
-  hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
+  constexpr int threads = (Q == 64 && sizeof(T) == 2) ? P64_THREADS : SCAN_THREADS;
+  hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(threads), scan_lds, stream,
                      static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
                      static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);

@@ -103,19 +103,22 @@ def test_prefill_bf16_ragged_multichunk(chunk):
     check_prefill(small(102, chunk=chunk, seqlen=600))
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("opts", [dict(z=False), dict(D=False), dict(h0=False),
                                   dict(z=False, D=False, h0=False)])
-def test_prefill_optional_operands(opts):
-    check_prefill(small(103, seqlen=160), **opts)
+def test_prefill_optional_operands(opts, chunk):
+    check_prefill(small(103, seqlen=160, chunk=chunk), **opts)
 
 
-def test_prefill_inplace_state():
-    check_prefill(small(104, seqlen=129), inplace=True)
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_inplace_state(chunk):
+    check_prefill(small(104, seqlen=129, chunk=chunk), inplace=True)
 
 
-@pytest.mark.parametrize("L", [1, 2, 31, 128, 129])
-def test_prefill_short_and_boundary_lengths(L):
-    check_prefill(small(105, seqlen=L, batch=3, nheads=8, ngroups=2))
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("L", [1, 2, 31, 63, 64, 65, 128, 129])
+def test_prefill_short_and_boundary_lengths(L, chunk):
+    check_prefill(small(105, seqlen=L, batch=3, nheads=8, ngroups=2, chunk=chunk))
 
 
 def test_prefill_len0_passes_state_through():
@@ -145,18 +148,23 @@ def test_prefill_chunk_invariance_and_determinism():
     y128, h128 = gpu_prefill(cfg, inp, chunk=128)
     y256, h256 = gpu_prefill(cfg, inp, chunk=256)
     y128b, h128b = gpu_prefill(cfg, inp, chunk=128)
+    y64b, h64b = gpu_prefill(cfg, inp, chunk=64)
     for yg, hg, q in ((y64, h64, 64), (y128, h128, 128), (y256, h256, 256)):
         assert_close(yg, yr, "bf16", f"chunk {q} y")
         assert_close(hg, hr, "bf16", f"chunk {q} h_final", rounded=False)
     assert compute_err(y64, y128, "bf16") <= 2 * TOL["bf16"]
     np.testing.assert_array_equal(y128, y128b)
     np.testing.assert_array_equal(h128, h128b)
+    np.testing.assert_array_equal(y64, y64b)
+    np.testing.assert_array_equal(h64, h64b)
 
 
-def test_prefill_12b_8k_full_size_head_subset():
-    """The 12B-shape 8k prefill as the benchmark runs it, checked on 9 heads spanning all 8 groups."""
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_12b_8k_full_size_head_subset(chunk):
+    """The 12B-shape 8k prefill at full size, with the benchmark's chunk of 64 and with 128,
+    checked on 9 heads spanning all 8 groups."""
     cfg = si.CONFIGS[1]
-    check_prefill(cfg, heads=[0, 21, 40, 63, 77, 99, 118, 139, 159])
+    check_prefill(dataclasses.replace(cfg, chunk=chunk), heads=[0, 21, 40, 63, 77, 99, 118, 139, 159])
 
 
 # --------------------------------------------------------------------------- conv1d
