@@ -184,10 +184,12 @@ __global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
 #pragma unroll
     for (int j = 0; j < C::KS_N; ++j)
       mma(acc, frag_contig(&sB[si * 32 + col][16 * j], g2), frag_contig(&sC[tb * 32 + col][16 * j], g2));
-    float* dst = gout + ((size_t)k * 64 + lane) * 16;
+    // stored as [q][lane][4]: accumulator registers 4q .. 4q+3 of every lane, so that each
+    // of the reader's four 16-byte loads covers 1 KiB contiguously
+    float* dst = gout + (size_t)k * 1024 + 4 * lane;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(dst + 4 * q) =
+      *reinterpret_cast<f32x4*>(dst + 256 * q) =
           (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
   }
   // B^T operand frags (row n = nb*32 + col, k = s): record (nb, j), lane
@@ -271,11 +273,12 @@ __device__ __forceinline__ void split_set(Frag<T>& hi, Frag<T>& lo, int e, float
   if constexpr (sizeof(T) == 2) frag_set<T>(lo, e, v - frag_get(hi, e));
 }
 
-__device__ __forceinline__ f32x16 load_tile16(const float* src) {
+// one Gram tile (1024 floats, [q][lane][4]) into this lane's accumulator-order registers
+__device__ __forceinline__ f32x16 load_tile16(const float* tile, int lane) {
   f32x16 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
+    f32x4 v = *reinterpret_cast<const f32x4*>(tile + 256 * q + 4 * lane);
     r[4 * q] = v[0];
     r[4 * q + 1] = v[1];
     r[4 * q + 2] = v[2];
@@ -482,8 +485,8 @@ void ssd_scan_wide_kernel(const T* __restrict__ x, int64_t x_stride, const float
         cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
       const float* gt = reinterpret_cast<const float*>(rec);
       const int k0 = tb * (tb + 1) / 2;
-      gq0 = load_tile16(gt + ((size_t)k0 * 64 + lane) * 16);
-      if (tb > 0) gq1 = load_tile16(gt + ((size_t)(k0 + 1) * 64 + lane) * 16);
+      gq0 = load_tile16(gt + (size_t)k0 * 1024, lane);
+      if (tb > 0) gq1 = load_tile16(gt + (size_t)(k0 + 1) * 1024, lane);
       if constexpr (!C::STAGE_Z) {
         const int t = c * Q + tb * 32 + col;
         if (zb && t < L) {
@@ -526,7 +529,7 @@ void ssd_scan_wide_kernel(const T* __restrict__ x, int64_t x_stride, const float
         for (int si = 0; si < tb; ++si) {
           const f32x16 gcur = gq0;
           gq0 = gq1;
-          if (si + 2 <= tb) gq1 = load_tile16(gt + ((size_t)(k0 + si + 2) * 64 + lane) * 16);
+          if (si + 2 <= tb) gq1 = load_tile16(gt + (size_t)(k0 + si + 2) * 1024, lane);
           Frag<T> mh[2], ml[2];
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -1052,7 +1055,7 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 #pragma unroll
       for (int s = 0; s < OW::NB; ++s) {
         const int k = OW::build(hw, s);
-        if (k >= 0) gram[s] = load_tile16(gt + ((size_t)k * 64 + lane) * 16);
+        if (k >= 0) gram[s] = load_tile16(gt + (size_t)k * 1024, lane);
       }
     };
     auto write_state = [&]() {
@@ -1179,7 +1182,7 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 // bf16 io, chunk 64, 16 waves. One barrier per chunk. In iteration c:
 //   Y waves 0..3:   chunk c's outputs, Y^T tile (token block y >> 1, p-block y & 1):
 //                   H^T C^T scaled by exp2(lambda_t), plus X^T M^T, gated, into sZ.
-//   H waves 4..7:   the state to H_c (tiles: row blocks w >> 1 and (w >> 1) + 2, p-block w & 1),
+//   H waves 4..7:   the state to H_c (H wave w: state rows 32 w .. 32 w + 31, both p-blocks),
 //                   published into the other half of a double-buffered H^T.
 //   helper waves 8..15: chunk c+1's staging (flush of y(c-1), z, x^T, (w x)^T hi/lo), its
 //                   masked decay tiles M^T (waves 8, 9, 10: tiles 0, 2, 1), the dt / pi / v
@@ -1293,38 +1296,38 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     }
   } else if (wave < 8) {
     // ========================================================== H waves
+    // H wave hw owns state rows n = 32 hw .. 32 hw + 31 for both p-blocks, so that no two waves
+    // load the same B^T fragments
     const int hw = wave - 4;
-    const int pb = hw & 1, nb0 = hw >> 1;
-    const int prow = pb * 32 + col;
-    f32x16 hacc[2];
-    Frag<T> af[2][C::KS_Q];
+    f32x16 hacc[2];                     // [p-block]
+    Frag<T> af[C::KS_Q];
     const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
-        hacc[i][r] = h0 ? h0[sbase + n * SP + prow] : 0.f;
+        const int n = hw * 32 + acc_row(r, lane);
+        hacc[i][r] = h0 ? h0[sbase + n * SP + i * 32 + col] : 0.f;
       }
     auto fetch_bt = [&](int c) {
       const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < C::KS_Q; ++j)
-          af[i][j] = ld_frag<T>(btf + ((size_t)((nb0 + 2 * i) * C::KS_Q + j) * 64 + lane) * C::FB);
+      for (int j = 0; j < C::KS_Q; ++j)
+        af[j] = ld_frag<T>(btf + ((size_t)(hw * C::KS_Q + j) * 64 + lane) * C::FB);
     };
     auto publish = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        const int prow = i * 32 + col;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = hsw(prow, (nb0 + 2 * i) * 32 + 8 * r4 + 4 * g2);
+          const int n = hsw(prow, hw * 32 + 8 * r4 + 4 * g2);
           const Split2 a = split2(hacc[i][4 * r4], hacc[i][4 * r4 + 1]);
           const Split2 d = split2(hacc[i][4 * r4 + 2], hacc[i][4 * r4 + 3]);
           *reinterpret_cast<uint2*>(&S.sHt[buf][prow][n]) = make_uint2(a.hi, d.hi);
           *reinterpret_cast<uint2*>(&S.sHtlo[buf][prow][n]) = make_uint2(a.lo, d.lo);
         }
+      }
     };
     publish(1);          // h0 is the state chunk 0 reads
     if (nC > 0) fetch_bt(0);
@@ -1340,13 +1343,12 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
 #pragma unroll
       for (int j = 0; j < C::KS_Q; ++j) {
-        const int k0 = xs64(prow, 16 * j + 8 * g2);
-        const Frag<T> bh = frag_contig(&S.sXW[cur][prow][k0], 0);
-        const Frag<T> bl = frag_contig(&S.sXWlo[cur][prow][k0], 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          mma(hacc[i], af[i][j], bh);
-          mma(hacc[i], af[i][j], bl);
+          const int prow = i * 32 + col;
+          const int k0 = xs64(prow, 16 * j + 8 * g2);
+          mma(hacc[i], af[j], frag_contig(&S.sXW[cur][prow][k0], 0));
+          mma(hacc[i], af[j], frag_contig(&S.sXWlo[cur][prow][k0], 0));
         }
       }
       publish(cur);
@@ -1358,8 +1360,8 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
-          h_final[sbase + n * SP + prow] = hacc[i][r];
+          const int n = hw * 32 + acc_row(r, lane);
+          h_final[sbase + n * SP + i * 32 + col] = hacc[i][r];
         }
     }
   } else {
@@ -1440,7 +1442,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       auto fetch_gram = [&](int c) {
         if constexpr (BUILDER)
           gram = load_tile16(reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
-                             ((size_t)kb * 64 + lane) * 16);
+                                 (size_t)kb * 1024, lane);
       };
       // tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t and dt_s, zero
       // above the diagonal, D on the diagonal
