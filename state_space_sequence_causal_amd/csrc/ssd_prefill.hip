@@ -1185,7 +1185,7 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 //   H waves 4..7:   the state to H_c (H wave w: state rows 32 w .. 32 w + 31, both p-blocks),
 //                   published into the other half of a double-buffered H^T.
 //   helper waves 8..15: chunk c+1's staging (flush of y(c-1), z, x^T, (w x)^T hi/lo), its
-//                   masked decay tiles M^T (waves 8, 9, 10: tiles 0, 2, 1), the dt / pi / v
+//                   masked decay tiles M^T (in halves, by helper waves 0..5), the dt / pi / v
 //                   record of chunk c+2, and the loads for the chunks after.
 // Everything chunk c+1 needs goes to the other half of double-buffered LDS tiles, so the
 // barrier that ends the iteration is the only synchronisation; records are staged two chunks
@@ -1254,16 +1254,36 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       const int cur = c & 1, prv = cur ^ 1;
       // ---- carried state, scaled by exp2(lambda_t)
       f32x16 acc = {};
+      {
+        // four k steps of H^T hi / lo in flight
+        Frag<T> ha[4], la[4];
 #pragma unroll
-      for (int j = 0; j < C::KS_N; ++j) {
-        const int n = hsw(prow, 16 * j + 8 * g2);
-        mma(acc, frag_contig(&S.sHt[prv][prow][n], 0), cf[j]);
-        mma(acc, frag_contig(&S.sHtlo[prv][prow][n], 0), cf[j]);
+        for (int j = 0; j < 4; ++j) {
+          const int n = hsw(prow, 16 * j + 8 * g2);
+          ha[j] = frag_contig(&S.sHt[prv][prow][n], 0);
+          la[j] = frag_contig(&S.sHtlo[prv][prow][n], 0);
+        }
+#pragma unroll
+        for (int j = 0; j < C::KS_N; ++j) {
+          mma(acc, ha[j & 3], cf[j]);
+          mma(acc, la[j & 3], cf[j]);
+          if (j + 4 < C::KS_N) {
+            const int n = hsw(prow, 16 * (j + 4) + 8 * g2);
+            ha[j & 3] = frag_contig(&S.sHt[prv][prow][n], 0);
+            la[j & 3] = frag_contig(&S.sHtlo[prv][prow][n], 0);
+          }
+        }
       }
       const float et = exp2_hw((tb ? tot_of(c, 0) : 0.f) + S.sRec[c % 3][Q + tl]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] *= et;
       fetch_c(min(c + 1, nC - 1));
+      // z of this wave's outputs, read ahead of the intra-chunk MFMAs
+      Raw4<T> zz[4];
+      if (z) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) zz[r4] = ld4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)]);
+      }
       // ---- intra-chunk part: Y^T += X^T M^T over source blocks si <= tb
 #pragma unroll
       for (int si = 0; si < 2; ++si) {
@@ -1280,17 +1300,21 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         }
       }
       // ---- gate and y into sZ[cur] (in place of z)
+      if (z) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int r = 4 * r4;
-        T* zp = &S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)];
-        float gq[4] = {1.f, 1.f, 1.f, 1.f};
-        if (z) {
-          const Raw4<T> zz = ld4(zp);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) gq[q] = silu_fast(zz.get(q));
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * r4;
+          st4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[r] * silu_fast(zz[r4].get(0)),
+              acc[r + 1] * silu_fast(zz[r4].get(1)), acc[r + 2] * silu_fast(zz[r4].get(2)),
+              acc[r + 3] * silu_fast(zz[r4].get(3)));
         }
-        st4(zp, acc[r] * gq[0], acc[r + 1] * gq[1], acc[r + 2] * gq[2], acc[r + 3] * gq[3]);
+      } else {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * r4;
+          st4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[r], acc[r + 1], acc[r + 2],
+              acc[r + 3]);
+        }
       }
       __syncthreads();
     }
@@ -1368,29 +1392,33 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     // ========================================================== helper waves
     const int htid = tid - 512, hv = wave - 8;
     const T* xb = x + h * SP;
+    const T* zb = z ? z + h * SP : xb;   // without z, x is loaded in its place and not used
     T* yb = y + h * SP;
     const float Dh = D ? D[h] : 0.f;
     // thread: token pair (s0, s0 + 1) = 2 (htid / 16), columns p0 .. p0 + 3 = 4 (htid % 16)
     const int s0 = 2 * (htid >> 4), p0 = 4 * (htid & 15);
     // per-thread element offsets inside a chunk's rows fit 32 bits; chunk bases are uniform
     const uint32_t xs = (uint32_t)x_stride, zs = (uint32_t)z_stride, ys = (uint32_t)y_stride;
-    // M^T tiles: helper waves 0, 1, 2 build tiles 0 (diagonal 0), 2 (diagonal 1), 1 (block 1
-    // from block 0) and carry the dt / pi / v records (3Q words, a word a thread); the other
-    // helpers only stage.
-    const int kb = hv == 0 ? 0 : hv == 1 ? 2 : hv == 2 ? 1 : -1;
-    // Each role (builder or not, with or without z) runs its own copy of the loop, so that
-    // every copy issues a fixed sequence of memory operations and the compiler's count of
+    // M^T tiles, built in halves (k steps hm of 16 source tokens): helper waves 0, 1 build
+    // tile 0 (diagonal 0), waves 2, 3 tile 2 (diagonal 1), waves 4, 5 tile 1 (block 1 from
+    // block 0); waves 6, 7 build nothing. Helper wave v runs on SIMD v % 4, so the two
+    // diagonal tiles, the costly ones, are spread over all four SIMDs. Waves 0..2 also carry
+    // the dt / pi / v records (3Q words, a word a thread).
+    const int kb = hv < 2 ? 0 : hv < 4 ? 2 : hv < 6 ? 1 : -1;
+    const int hm = hv & 1;
+    // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
+    // copy issues a fixed sequence of memory operations and the compiler's count of
     // outstanding loads stays exact: a merged count would wait for loads just issued.
-    auto helpers = [&](auto builder_tag, auto z_tag) {
-      constexpr bool BUILDER = decltype(builder_tag)::value;
-      constexpr bool HAS_Z = decltype(z_tag)::value;
-      const T* zb = HAS_Z ? z + h * SP : nullptr;
+    auto helpers = [&](auto gram_tag, auto rec_tag) {
+      constexpr bool GRAM = decltype(gram_tag)::value;
+      constexpr bool REC = decltype(rec_tag)::value;
       Raw4<T> rX[2], rZ[2];
       float rRec = 0.f;
-      f32x16 gram;
+      f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7
       auto load_set = [&](int c) {       // x and z of this thread's tokens
         const int64_t r0 = row0 + (int64_t)c * Q;
         const T* xc = xb + r0 * x_stride;
+        const T* zc = zb + r0 * z_stride;
         // Rows past the end of the sequence load the last row instead (finite values; their
         // dt and v are zero, so they add nothing), which keeps the loads unconditional.
         const int lim = L - 1 - c * Q;
@@ -1398,14 +1426,14 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         for (int k = 0; k < 2; ++k) {
           const uint32_t s = (uint32_t)min(s0 + k, lim);
           rX[k] = ld4(xc + (s * xs + p0));
-          if constexpr (HAS_Z) rZ[k] = ld4(zb + r0 * z_stride + (s * zs + p0));
+          rZ[k] = ld4(zc + (s * zs + p0));
         }
       };
       auto load_rec = [&](int c) {
-        if constexpr (BUILDER) rRec = hrec[(size_t)c * (3 * Q) + htid];
+        if constexpr (REC) rRec = hrec[(size_t)c * (3 * Q) + htid];
       };
       auto put_rec = [&](int c) {
-        if constexpr (BUILDER) S.sRec[c % 3][htid] = rRec;
+        if constexpr (REC) S.sRec[c % 3][htid] = rRec;
       };
       auto flush_y = [&](int c, bool full) {   // y of chunk c out of sZ[c & 1]
         T* yc = yb + (row0 + (int64_t)c * Q) * y_stride;
@@ -1419,7 +1447,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       // x^T, (w x)^T and z of chunk c (its set in registers) into buffers c & 1
       auto stage = [&](int c) {
         const int buf = c & 1;
-        if constexpr (HAS_Z) {
+        if (z) {
 #pragma unroll
           for (int k = 0; k < 2; ++k)
             *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos<T>(s0 + k, p0)]) = rZ[k].v;
@@ -1439,54 +1467,54 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
         }
       };
-      auto fetch_gram = [&](int c) {
-        if constexpr (BUILDER)
-          gram = load_tile16(reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
-                                 (size_t)kb * 1024, lane);
+      auto fetch_gram = [&](int c) {   // quads 2 hm, 2 hm + 1 of the stored tile
+        if constexpr (GRAM) {
+          const float* tile = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
+                              (size_t)kb * 1024 + 512 * hm + 4 * lane;
+          gram[0] = *reinterpret_cast<const f32x4*>(tile);
+          gram[1] = *reinterpret_cast<const f32x4*>(tile + 256);
+        }
       };
-      // tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t and dt_s, zero
-      // above the diagonal, D on the diagonal
+      // half hm of tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t
+      // and dt_s, zero above the diagonal, D on the diagonal. Register 4 j + q of the half is
+      // source token 16 hm + 8 j + 4 g2 + q of the tile's source block.
       auto build = [&](int c) {
-        if constexpr (BUILDER) {
+        if constexpr (GRAM) {
           const float* rec = S.sRec[c % 3];
           const float* sDt = rec;
           const float* sPi = rec + Q;
           const float* sV = rec + 2 * Q;
           const int tb = kb == 0 ? 0 : 1, si = kb == 2 ? 1 : 0;
           const int tl = tb * 32 + col;
-          float mv[16];
+          float mv[8];
           if (si < tb) {
             // block 0 -> block 1: v_s exp2(pi_t)
             const float ut = exp2_hw(sPi[tl]);
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4 vq = *reinterpret_cast<const f32x4*>(&sV[8 * r4 + 4 * g2]);
+            for (int j = 0; j < 2; ++j) {
+              const f32x4 vq = *reinterpret_cast<const f32x4*>(&sV[16 * hm + 8 * j + 4 * g2]);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) mv[4 * r4 + q] = gram[4 * r4 + q] * (vq[q] * ut);
+              for (int q = 0; q < 4; ++q) mv[4 * j + q] = gram[j][q] * (vq[q] * ut);
             }
           } else {
             const float pit = sPi[tl];
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const int sr = tb * 32 + 8 * r4 + 4 * g2;
+            for (int j = 0; j < 2; ++j) {
+              const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
               const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
               const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int r = 4 * r4 + q;
-                float v = (sr + q <= tl) ? gram[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+                float v = (sr + q <= tl) ? gram[j][q] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
                 if (sr + q == tl) v += Dh;
-                mv[r] = v;
+                mv[4 * j + q] = v;
               }
             }
           }
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2) {
-            Frag<T> mh, ml;
-            frag_split(mv + 8 * m2, mh, ml);
-            S.sM[c & 1][kb][m2][lane] = mh;
-            S.sMlo[c & 1][kb][m2][lane] = ml;
-          }
+          Frag<T> mh, ml;
+          frag_split(mv, mh, ml);
+          S.sM[c & 1][kb][hm][lane] = mh;
+          S.sMlo[c & 1][kb][hm][lane] = ml;
         }
       };
       // prologue: records 0 and 1 into LDS; then chunk 0 staged and its tiles built, chunk 1's
@@ -1522,13 +1550,9 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       }
       if (nC > 0) flush_y(nC - 1, false);   // y of the last chunk
     };
-    if (kb >= 0) {
-      if (z) helpers(std::true_type{}, std::true_type{});
-      else helpers(std::true_type{}, std::false_type{});
-    } else {
-      if (z) helpers(std::false_type{}, std::true_type{});
-      else helpers(std::false_type{}, std::false_type{});
-    }
+    if (hv < 3) helpers(std::true_type{}, std::true_type{});
+    else if (kb >= 0) helpers(std::true_type{}, std::false_type{});
+    else helpers(std::false_type{}, std::false_type{});
   }
 }
 
