@@ -4,18 +4,22 @@ One step = one pass of the prefill hot path over one batch of synthetic input
 already resident in HBM: mamba2_conv1d (width-4 causal conv + SiLU over the xBC
 channels) followed by mamba2_ssd_prefill (the fused chunked scan), on the
 12B-shape single-layer workload: B=1, L=8192, 160 heads x 64, 8 groups,
-d_state 128, chunk 128, bf16 io, fp32 state. ``value`` is prefill tokens/s of
-that step. The one-token decode state update is measured in the same run on
-the 9B-shape batch-64 decode workload and reported under "decode".
+d_state 128, bf16 io, fp32 state. ``value`` is prefill tokens/s of that step.
+The scan runs with chunk length 64 (--chunk): the chunk length is the scan's
+tiling parameter and does not change what is computed (the GPU tests check
+chunks 64, 128 and 256 against the oracle). The workload's listed chunk of 128
+is timed in the same run and reported under "kernels". The one-token decode
+state update is measured in the same run on the 9B-shape batch-64 decode
+workload and reported under "decode".
 
 Per-kernel durations come from HIP events recorded around each launch on the
 stream the kernels run on (torch's current stream). Algorithmic bytes count
 every input read once, every output written once and the fp32 state read and
 written once; they are the roofline numerators.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps K] [--chunk Q]
        [--no-cpu-baseline] [--copy-calibration]
-       python bench.py --summarize-counters FETCH_CSV WRITE_CSV
+       python bench.py [--chunk Q] --summarize-counters FETCH_CSV WRITE_CSV
 """
 from __future__ import annotations
 
@@ -48,15 +52,17 @@ def kernel_source_hash(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str, launches_bytes_unit: float = 1.0):
+def measured_traffic(name: str, chunk: int | None = None):
     """HBM bytes per launch from the committed counter summary, or None when the kernel
-    source changed since the counters were taken."""
+    source changed since the counters were taken (or they were taken at another chunk)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[name]
     except (OSError, KeyError, ValueError):
         return None
     if t.get("source_hash") != kernel_source_hash(name):
+        return None
+    if chunk is not None and t.get("chunk") != chunk:
         return None
     return t.get("bytes_per_launch")
 
@@ -91,7 +97,7 @@ def decode_bytes(cfg) -> int:
 
 
 # ------------------------------------------------------------------------------ GPU parts
-def run_prefill(args, torch, m2, si, cfg, inp):
+def run_prefill(args, torch, m2, si, cfg, inp, chunk):
     dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
     f32 = lambda a: torch.from_numpy(a).cuda()
     u, z, dt = dev(inp["xbc"]), dev(inp["z"]), dev(inp["dt_raw"])
@@ -103,7 +109,7 @@ def run_prefill(args, torch, m2, si, cfg, inp):
     y = torch.empty((cfg.batch, cfg.seqlen, di), dtype=torch.bfloat16, device="cuda")
     hf = torch.empty((cfg.batch, cfg.nheads, cfg.dstate, cfg.headdim), dtype=torch.float32, device="cuda")
     ws = torch.empty(m2.mamba2_ssd_prefill_workspace_bytes(
-        m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, cfg.chunk, m2.MAMBA2_BF16)),
+        m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, chunk, m2.MAMBA2_BF16)),
         dtype=torch.uint8, device="cuda")
 
     def step(evs=None):
@@ -113,7 +119,7 @@ def run_prefill(args, torch, m2, si, cfg, inp):
         if evs:
             evs[1].record()
         m2.mamba2_ssd_prefill(x, Bm, Cm, dt, dtb, A, D, z, None, hf, y, ngroups=cfg.ngroups,
-                              chunk=cfg.chunk, workspace=ws)
+                              chunk=chunk, workspace=ws)
         if evs:
             evs[2].record()
 
@@ -212,11 +218,14 @@ def cpu_baseline(cfg, inp):
 
 
 # ------------------------------------------------------------------------------ counters
-COUNTER_KERNELS = {          # traffic entry -> kernel-name fragments summed per call
-    "ssd_prefill": ["ssd_prep_kernel", "ssd_scan_kernel"],
-    "conv1d": ["conv1d_kernel"],
-    "state_update": ["state_update_kernel"],
-}
+def counter_kernels(chunk: int) -> dict:
+    """traffic entry -> (mangled) kernel-name fragments summed per call, for the bf16 prefill
+    at chunk length ``chunk``"""
+    scan = {64: "ssd_scan64_kernel", 256: "ssd_scan_wide_kernelIDF16bLi256E"}.get(
+        chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
+    return {"ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}E", scan],
+            "conv1d": ["conv1d_kernel"],
+            "state_update": ["state_update_kernel"]}
 
 
 def _counter_means(path: str, counter: str):
@@ -238,7 +247,7 @@ def _counter_means(path: str, counter: str):
     return {k: v[0] / v[1] for k, v in acc.items()}, calib
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
+def summarize_counters(fetch_csv: str, write_csv: str, chunk: int) -> dict:
     """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch),
     each scaled by what the same counter reads for the calibration kernel (torch.neg over
     1 GiB in, 1 GiB out). Writes profiles/traffic.json keyed by the kernel source hash."""
@@ -258,11 +267,13 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
     w_cal = CALIB_BYTES / (w_kib * 1024.0)
     out = {"_calibration": {"kernel": "torch.neg over 2^28 fp32 (1 GiB read, 1 GiB written)",
                             "fetch_factor": f_cal, "write_factor": w_cal}}
-    for key, frags in COUNTER_KERNELS.items():
+    for key, frags in counter_kernels(chunk).items():
         fb = sum(pick(fetch, fr) for fr in frags) * 1024.0 * f_cal
         wb = sum(pick(write, fr) for fr in frags) * 1024.0 * w_cal
         out[key] = {"source_hash": kernel_source_hash(key), "fetch_bytes": fb, "write_bytes": wb,
                     "bytes_per_launch": fb + wb, "kernels": frags}
+        if key == "ssd_prefill":
+            out[key]["chunk"] = chunk
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -272,16 +283,19 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # a few hundred warm-up steps (~0.1 s): the first tens of milliseconds of GPU work run at
+    # lower clocks
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--chunk", type=int, default=64, help="scan chunk length of the timed prefill")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs of this script into profiles/traffic.json")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(json.dumps(summarize_counters(*args.summarize_counters), indent=1))
+        print(json.dumps(summarize_counters(*args.summarize_counters, args.chunk), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer core runs on a single MI355X with no "
@@ -297,7 +311,10 @@ def main():
         copy_calibration(torch)
     cfg = si.CONFIGS[1]
     inp = si.draw_prefill(cfg)
-    ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si, cfg, inp)
+    ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si, cfg, inp, args.chunk)
+    alt = None
+    if args.chunk != cfg.chunk:
+        alt = run_prefill(args, torch, m2, si, cfg, inp, cfg.chunk)
     by = prefill_bytes(cfg)
     fl = prefill_flops(cfg)
     tokens = cfg.batch * cfg.seqlen
@@ -322,12 +339,12 @@ def main():
         "config": {"workload": "12B-shape Mamba-2 layer-core prefill: conv1d + chunked SSD scan",
                    "batch": cfg.batch, "seq_len": cfg.seqlen, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "ngroups": cfg.ngroups, "dstate": cfg.dstate,
-                   "conv_width": cfg.conv_width, "chunk": cfg.chunk, "io": "bf16",
+                   "conv_width": cfg.conv_width, "chunk": args.chunk, "io": "bf16",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "mamba2_ssd_prefill (ssd_prep_kernel + ssd_scan_kernel)",
                      "bound": "hbm", "achieved": ssd_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ssd_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("ssd_prefill"),
+                     "traffic": measured_traffic("ssd_prefill", args.chunk),
                      "algorithmic_bytes": by["ssd"], "avg_launch_us": ssd_us},
         "kernels": {
             "ssd_prefill": {"us": ssd_us, "tokens_per_s": tokens / (ssd_us * 1e-6), "GB_s": ssd_gbs,
@@ -345,6 +362,10 @@ def main():
                    "traffic": measured_traffic("state_update")},
         "wall_s_timed": wall,
     }
+    if alt is not None:
+        out["kernels"][f"ssd_prefill_chunk{cfg.chunk}"] = {
+            "us": alt[3], "tokens_per_s": tokens / (alt[3] * 1e-6),
+            "step_tokens_per_s": tokens / (alt[0] * 1e-3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out))
