@@ -9,13 +9,17 @@
 // One workgroup per (sequence b, group g): it owns the x channels of the
 // group's heads and the group's B and C channels, so every conv-cache column
 // has exactly one reader-writer (no cross-workgroup ordering is needed). Each of
-// its 16 waves streams one head (two for wider groups) in parts of 8 rows: lane
-// (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of rows n = rg + 4k, so one
-// wave instruction touches 1 KiB of contiguous state. Two parts are in flight
-// while one is updated, and the first two are requested before the conv step,
-// which they do not need. y is reduced over the four row groups with cross-lane
-// shuffles. Small parts and many waves per CU measured best on MI355X (about
-// 5.4 TB/s at batch 64, against about 6.0 TB/s for a plain in-place stream).
+// its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
+// (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of row n = 4m + rg, so one wave
+// instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
+// buffers with 3 in flight; every load is unconditional (loads past the wave's
+// last part re-read it), so the compiler's count of outstanding memory
+// operations is exact and each wait is for the one part it needs. The first
+// three parts are requested before the conv step, which they do not need. y is
+// reduced over the four row groups with cross-lane shuffles. At batch 64 the
+// kernel streams about 5.3 TB/s, against about 5.8 TB/s for a plain in-place
+// stream of the same size on this part; the conv step before the stream costs
+// about 4.5 us of the ~104 us.
 #include "device.h"
 #include "launch.h"
 
@@ -26,7 +30,8 @@ constexpr int DEC_THREADS = DEC_WAVES * 64;
 constexpr int DEC_P = 64;
 constexpr int DEC_N = 128;
 constexpr int DEC_W = 4;
-constexpr int DEC_K = 2;            // state rows per lane in one work item
+constexpr int DEC_K = 1;            // state rows per lane in one work item
+constexpr int DEC_NB = 4;           // item buffers
 constexpr int DEC_IPH = 32 / DEC_K;  // work items per head
 
 template <typename T>
@@ -49,7 +54,7 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
@@ -75,25 +80,38 @@ void state_update_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int q = lane & 15, rg = lane >> 4;
 
-  // Work items of this wave: (head j, part) for j = wave, wave + 8, ...; part m holds the
-  // 4 DEC_K state rows n = 4 DEC_K m + rg + 4k, k < DEC_K.
-  const int nitems = ((hpg - wave + DEC_WAVES - 1) / DEC_WAVES) * DEC_IPH;
-  auto item_ptr = [&](int it) {
-    const int j = wave + DEC_WAVES * (it / DEC_IPH);
-    const int h = g * hpg + j;
-    return ssm_state + ((int64_t)b * H + h) * DEC_N * DEC_P + (4 * DEC_K * (it % DEC_IPH) + rg) * DEC_P +
-           4 * q;
+  // Work items of this wave: (head j, part) for j = wave, wave + DEC_WAVES, ...; part m holds
+  // the 4 DEC_K state rows n = 4 DEC_K m + rg + 4k, k < DEC_K. Item it of the wave is part
+  // it % DEC_IPH of its head it / DEC_IPH.
+  const int nheads_w = (hpg - wave + DEC_WAVES - 1) / DEC_WAVES;
+  const int nitems = nheads_w * DEC_IPH;
+  // the wave's state base is uniform; an item is a 32-bit byte offset from it (heads of a
+  // wave are DEC_WAVES apart, parts of a head 4 DEC_K rows apart)
+  const char* wbase = reinterpret_cast<const char*>(
+      ssm_state + ((int64_t)b * H + g * hpg + wave) * DEC_N * DEC_P);
+  const uint32_t lane_off = (uint32_t)(rg * DEC_P + 4 * q) * 4u;
+  auto item_off = [&](int it) -> uint32_t {
+    return (uint32_t)((it / DEC_IPH) * DEC_WAVES * DEC_N * DEC_P + (it % DEC_IPH) * 4 * DEC_K * DEC_P) * 4u;
   };
-  f32x4 buf[3][DEC_K];
+  auto item_ptr = [&](int it) {
+    return const_cast<float*>(reinterpret_cast<const float*>(wbase + (item_off(it) + lane_off)));
+  };
+  // DEC_NB buffers, item it in buffer it % DEC_NB, DEC_NB - 1 items in flight. Loads past the
+  // wave's last item re-read the last item (never used): every load is unconditional, so the
+  // compiler's count of outstanding memory operations stays exact and each wait is for the
+  // one item it needs.
+  f32x4 buf[DEC_NB][DEC_K];
   auto load_item = [&](int it, f32x4 (&dst)[DEC_K]) {
-    const float* st = item_ptr(it);
+    const float* st = item_ptr(min(it, nitems - 1));
 #pragma unroll
     for (int k = 0; k < DEC_K; ++k)
       dst[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + 4 * k * DEC_P));
   };
-  // the state does not depend on the conv: the first two parts are requested first
-  if (nitems > 0) load_item(0, buf[0]);
-  if (nitems > 1) load_item(1, buf[1]);
+  // the state does not depend on the conv: the first parts are requested first
+  if (nitems > 0) {
+#pragma unroll
+    for (int k = 0; k < DEC_NB - 1; ++k) load_item(k, buf[k]);
+  }
 
   // conv step on the owned channels; the cache shifts by one token
   const T* ub = u_t + (int64_t)b * Cc;
@@ -123,62 +141,58 @@ void state_update_kernel(
   }
   __syncthreads();
 
-  // stream the items: load item it+1 while item it is updated and stored
-  f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
-  auto process = [&](int it, const f32x4 (&hv)[DEC_K]) {
-    const int j = wave + DEC_WAVES * (it / DEC_IPH);
+  // stream the heads: per part, request part it + DEC_NB - 1, then update part it in place
+  const T* zsrc = z_t ? z_t : u_t;     // without z a valid row is read and not used
+  for (int hj = 0; hj < nheads_w; ++hj) {
+    const int j = wave + DEC_WAVES * hj;
     const int h = g * hpg + j;
     const float a = das[j], dt = dts[j];
     const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + j * DEC_P + 4 * q);
     const f32x4 dx = dt * x4;
-    float* st = item_ptr(it);
-    const int n0 = 4 * DEC_K * (it % DEC_IPH) + rg;
+    f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int m0 = 0; m0 < DEC_IPH; m0 += DEC_NB) {
 #pragma unroll
-    for (int k = 0; k < DEC_K; ++k) {
-      const float bn = bsm[n0 + 4 * k], cn = csm[n0 + 4 * k];
-      f32x4 nv;
-      nv[0] = a * hv[k][0] + bn * dx[0];
-      nv[1] = a * hv[k][1] + bn * dx[1];
-      nv[2] = a * hv[k][2] + bn * dx[2];
-      nv[3] = a * hv[k][3] + bn * dx[3];
-      yacc[0] += cn * nv[0];
-      yacc[1] += cn * nv[1];
-      yacc[2] += cn * nv[2];
-      yacc[3] += cn * nv[3];
-      __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(st + 4 * k * DEC_P));
-    }
-    if (it % DEC_IPH == DEC_IPH - 1) {
-      // head done: reduce y over the four row groups, add the skip term, gate, store
+    for (int mm = 0; mm < DEC_NB; ++mm) {
+      const int m = m0 + mm;
+      const int it = hj * DEC_IPH + m;
+      load_item(it + DEC_NB - 1, buf[(mm + DEC_NB - 1) % DEC_NB]);
+      // keep the request here: the scheduler would otherwise sink it below the update
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 (&hv)[DEC_K] = buf[mm];
+      float* st = item_ptr(it);
+      const int n0 = 4 * DEC_K * m + rg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        yacc[i] += __shfl_xor(yacc[i], 16);
-        yacc[i] += __shfl_xor(yacc[i], 32);
+      for (int k = 0; k < DEC_K; ++k) {
+        const float bn = bsm[n0 + 4 * k], cn = csm[n0 + 4 * k];
+        f32x4 nv;
+        nv[0] = a * hv[k][0] + bn * dx[0];
+        nv[1] = a * hv[k][1] + bn * dx[1];
+        nv[2] = a * hv[k][2] + bn * dx[2];
+        nv[3] = a * hv[k][3] + bn * dx[3];
+        yacc[0] += cn * nv[0];
+        yacc[1] += cn * nv[1];
+        yacc[2] += cn * nv[2];
+        yacc[3] += cn * nv[3];
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(st + 4 * k * DEC_P));
       }
-      if (rg == 0) {
-        const float dh = D ? D[h] : 0.f;
-        f32x4 o = yacc + dh * x4;
-        if (z_t) {
-          f32x4 zz = load4(z_t + (int64_t)b * di + h * DEC_P + 4 * q);
+    }
+    }
+    // head done: reduce y over the four row groups (every lane ends with the sum), add the
+    // skip term, gate, store (the four row groups write the same values)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz[i]);
-        }
-        store4(y_t + (int64_t)b * di + h * DEC_P + 4 * q, o[0], o[1], o[2], o[3]);
-      }
-      yacc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      yacc[i] += __shfl_xor(yacc[i], 16);
+      yacc[i] += __shfl_xor(yacc[i], 32);
     }
-  };
-  // three buffers in rotation: part it+2 is requested while part it is updated
-  for (int it = 0; it < nitems; it += 3) {
-    if (it + 2 < nitems) load_item(it + 2, buf[2]);
-    process(it, buf[0]);
-    if (it + 1 < nitems) {
-      if (it + 3 < nitems) load_item(it + 3, buf[0]);
-      process(it + 1, buf[1]);
+    const float dh = D ? D[h] : 0.f;
+    f32x4 o = yacc + dh * x4;
+    const f32x4 zz = load4(zsrc + (int64_t)b * (z_t ? di : Cc) + h * DEC_P + 4 * q);
+    if (z_t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz[i]);
     }
-    if (it + 2 < nitems) {
-      if (it + 4 < nitems) load_item(it + 4, buf[1]);
-      process(it + 2, buf[2]);
-    }
+    store4(y_t + (int64_t)b * di + h * DEC_P + 4 * q, o[0], o[1], o[2], o[3]);
   }
 }
 
