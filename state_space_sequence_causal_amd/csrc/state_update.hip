@@ -14,12 +14,13 @@
 // instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
 // buffers with 3 in flight; every load is unconditional (loads past the wave's
 // last part re-read it), so the compiler's count of outstanding memory
-// operations is exact and each wait is for the one part it needs. The first
-// three parts are requested before the conv step, which they do not need. y is
+// operations is exact and each wait is for the one part it needs. At start-up the
+// conv and dt inputs are requested first and the first three state parts right
+// after, so the conv that gates the stream does not wait behind the state. A
+// head's z is requested when its stream starts and used when it ends. y is
 // reduced over the four row groups with cross-lane shuffles. At batch 64 the
-// kernel streams about 5.3 TB/s, against about 5.8 TB/s for a plain in-place
-// stream of the same size on this part; the conv step before the stream costs
-// about 4.5 us of the ~104 us.
+// kernel streams about 5.35 TB/s, against about 5.8 TB/s for a plain in-place
+// stream of the same size on this part.
 #include "device.h"
 #include "launch.h"
 
@@ -107,37 +108,81 @@ void state_update_kernel(
     for (int k = 0; k < DEC_K; ++k)
       dst[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + 4 * k * DEC_P));
   };
-  // the state does not depend on the conv: the first parts are requested first
+  // Start-up. The conv and dt inputs are requested first, then the first state parts: a wait
+  // for a load also waits for every load issued before it, so the conv, which gates the
+  // stream, must not queue behind the state. Each conv thread owns 4 channels.
+  constexpr int CV = 4;
+  const T* ub = u_t + (int64_t)b * Cc;
+  T* csb = conv_state + (int64_t)b * (DEC_W - 1) * Cc;
+  const int lc = tid * CV;
+  const bool conv_thread = lc < nch;
+  const int c = lc < nx ? g * nx + lc
+                        : (lc < nx + DEC_N ? di + g * DEC_N + (lc - nx) : di + G * DEC_N + g * DEC_N + (lc - nx - DEC_N));
+  Raw4<T> s0, s1, s2, cur;
+  f32x4 wv[CV], bv = {0.f, 0.f, 0.f, 0.f};
+  if (conv_thread) {
+    s0 = ld4(csb + c);
+    s1 = ld4(csb + Cc + c);
+    s2 = ld4(csb + 2 * Cc + c);
+    cur = ld4(ub + c);
+#pragma unroll
+    for (int i = 0; i < CV; ++i) wv[i] = *reinterpret_cast<const f32x4*>(w + (int64_t)(c + i) * DEC_W);
+    if (bias) {
+#pragma unroll
+      for (int i = 0; i < CV; ++i) bv[i] = bias[c + i];
+    }
+  }
+  float dtr = 0.f, dtb = 0.f, av = 0.f;
+  const bool dt_thread = tid < hpg;
+  if (dt_thread) {
+    const int h = g * hpg + tid;
+    dtr = to_f(dt_raw_t[(int64_t)b * H + h]);
+    dtb = dt_bias[h];
+    av = A[h];
+  }
+  // the state does not depend on the conv: its first parts are in flight during the conv
   if (nitems > 0) {
 #pragma unroll
     for (int k = 0; k < DEC_NB - 1; ++k) load_item(k, buf[k]);
   }
-
   // conv step on the owned channels; the cache shifts by one token
-  const T* ub = u_t + (int64_t)b * Cc;
-  T* csb = conv_state + (int64_t)b * (DEC_W - 1) * Cc;
-  for (int v = tid; v < nch / VE; v += DEC_THREADS) {
-    int lc = v * VE;
-    int c = lc < nx ? g * nx + lc
-                    : (lc < nx + DEC_N ? di + g * DEC_N + (lc - nx) : di + G * DEC_N + g * DEC_N + (lc - nx - DEC_N));
-    Vec<T> s0 = ld16(csb + c), s1 = ld16(csb + Cc + c), s2 = ld16(csb + 2 * Cc + c);
-    Vec<T> cur = ld16(ub + c);
+  if (conv_thread) {
 #pragma unroll
-    for (int i = 0; i < VE; ++i) {
-      f32x4 wv = *reinterpret_cast<const f32x4*>(w + (int64_t)(c + i) * DEC_W);
-      float acc = (bias ? bias[c + i] : 0.f) + wv[0] * s0.get(i) + wv[1] * s1.get(i) +
-                  wv[2] * s2.get(i) + wv[3] * cur.get(i);
+    for (int i = 0; i < CV; ++i) {
+      const float acc = bv[i] + wv[i][0] * s0.get(i) + wv[i][1] * s1.get(i) + wv[i][2] * s2.get(i) +
+                        wv[i][3] * cur.get(i);
       smem[lc + i] = silu_fast(acc);
     }
-    st16(csb + c, s1);
-    st16(csb + Cc + c, s2);
-    st16(csb + 2 * Cc + c, cur);
+    *reinterpret_cast<decltype(s1.v)*>(csb + c) = s1.v;
+    *reinterpret_cast<decltype(s2.v)*>(csb + Cc + c) = s2.v;
+    *reinterpret_cast<decltype(cur.v)*>(csb + 2 * Cc + c) = cur.v;
   }
-  for (int j = tid; j < hpg; j += DEC_THREADS) {
-    int h = g * hpg + j;
-    float dt = softplus_f(to_f(dt_raw_t[(int64_t)b * H + h]) + dt_bias[h]);
+  // groups wider than DEC_THREADS * CV channels: the rest, plainly
+  for (int l2 = lc + DEC_THREADS * CV; l2 < nch; l2 += DEC_THREADS * CV) {
+    const int c2 = l2 < nx ? g * nx + l2
+                           : (l2 < nx + DEC_N ? di + g * DEC_N + (l2 - nx) : di + G * DEC_N + g * DEC_N + (l2 - nx - DEC_N));
+    const Raw4<T> a0 = ld4(csb + c2), a1 = ld4(csb + Cc + c2), a2 = ld4(csb + 2 * Cc + c2), a3 = ld4(ub + c2);
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const f32x4 wq = *reinterpret_cast<const f32x4*>(w + (int64_t)(c2 + i) * DEC_W);
+      const float acc = (bias ? bias[c2 + i] : 0.f) + wq[0] * a0.get(i) + wq[1] * a1.get(i) +
+                        wq[2] * a2.get(i) + wq[3] * a3.get(i);
+      smem[l2 + i] = silu_fast(acc);
+    }
+    *reinterpret_cast<decltype(a1.v)*>(csb + c2) = a1.v;
+    *reinterpret_cast<decltype(a2.v)*>(csb + Cc + c2) = a2.v;
+    *reinterpret_cast<decltype(a3.v)*>(csb + 2 * Cc + c2) = a3.v;
+  }
+  for (int j = DEC_THREADS + tid; j < hpg; j += DEC_THREADS) {   // more heads than threads
+    const int h = g * hpg + j;
+    const float dt = softplus_f(to_f(dt_raw_t[(int64_t)b * H + h]) + dt_bias[h]);
     dts[j] = dt;
     das[j] = expf(dt * A[h]);
+  }
+  if (dt_thread) {
+    const float dt = softplus_f(dtr + dtb);
+    dts[tid] = dt;
+    das[tid] = expf(dt * av);
   }
   __syncthreads();
 
@@ -150,6 +195,9 @@ void state_update_kernel(
     const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + j * DEC_P + 4 * q);
     const f32x4 dx = dt * x4;
     f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
+    // the gate's z is requested now and used after the head's stream, so its latency is hidden
+    const f32x4 zz = load4(zsrc + (int64_t)b * (z_t ? di : Cc) + h * DEC_P + 4 * q);
+    const float dh = D ? D[h] : 0.f;
 #pragma unroll 1
     for (int m0 = 0; m0 < DEC_IPH; m0 += DEC_NB) {
 #pragma unroll
@@ -185,9 +233,7 @@ void state_update_kernel(
       yacc[i] += __shfl_xor(yacc[i], 16);
       yacc[i] += __shfl_xor(yacc[i], 32);
     }
-    const float dh = D ? D[h] : 0.f;
     f32x4 o = yacc + dh * x4;
-    const f32x4 zz = load4(zsrc + (int64_t)b * (z_t ? di : Cc) + h * DEC_P + 4 * q);
     if (z_t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz[i]);

@@ -128,8 +128,9 @@ def test_prefill_len0_passes_state_through():
     np.testing.assert_array_equal(hg, inp["h0"].astype(np.float64))
 
 
-def test_prefill_one_group_many_heads():
-    check_prefill(small(107, nheads=12, ngroups=1, seqlen=140))
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_prefill_one_group_many_heads(chunk):
+    check_prefill(small(107, nheads=12, ngroups=1, seqlen=140, chunk=chunk))
 
 
 def test_prefill_no_write_past_y():
@@ -203,35 +204,35 @@ def test_conv1d_12b_channels_no_bias():
 
 
 # --------------------------------------------------------------------------- decode
-def gpu_decode(cfg, params, step_inp, conv_state, ssm_state):
+def gpu_decode(cfg, params, step_inp, conv_state, ssm_state, z=True, D=True, bias=True):
     t = torch()
     io = cfg.io
     u = dev(step_inp["xbc"][:, 0], io)
-    z = dev(step_inp["z"][:, 0], io)
+    zt = dev(step_inp["z"][:, 0], io) if z else None
     dt = dev(step_inp["dt_raw"][:, 0], io)
     cs = dev(conv_state, io)
     ss = dev32(ssm_state)
     y = empty((cfg.batch, cfg.d_inner), io)
-    m2.mamba2_state_update(u, dev32(params["conv_w"]), dev32(params["conv_b"]), cs, dt,
-                           dev32(params["dt_bias"]), dev32(params["A"]), dev32(params["D"]), z,
-                           ss, y, ngroups=cfg.ngroups)
+    m2.mamba2_state_update(u, dev32(params["conv_w"]), dev32(params["conv_b"]) if bias else None, cs, dt,
+                           dev32(params["dt_bias"]), dev32(params["A"]), dev32(params["D"]) if D else None,
+                           zt, ss, y, ngroups=cfg.ngroups)
     t.cuda.synchronize()
     return host(y), host(cs), host(ss)
 
 
-def oracle_decode(cfg, params, step_inp, conv_state, ssm_state):
-    return oracle.state_update(step_inp["xbc"][:, 0], params["conv_w"], params["conv_b"], conv_state,
-                               step_inp["dt_raw"][:, 0], params["dt_bias"], params["A"], params["D"],
-                               step_inp["z"][:, 0], ssm_state, nheads=cfg.nheads,
-                               ngroups=cfg.ngroups)
+def oracle_decode(cfg, params, step_inp, conv_state, ssm_state, z=True, D=True, bias=True):
+    return oracle.state_update(step_inp["xbc"][:, 0], params["conv_w"], params["conv_b"] if bias else None,
+                               conv_state, step_inp["dt_raw"][:, 0], params["dt_bias"], params["A"],
+                               params["D"] if D else None, step_inp["z"][:, 0] if z else None,
+                               ssm_state, nheads=cfg.nheads, ngroups=cfg.ngroups)
 
 
-def check_decode(cfg):
+def check_decode(cfg, **opts):
     params = si.draw_params(cfg)
     step = si.draw_decode_step(cfg, 0)
     cs0, ss0 = si.draw_conv_state(cfg), si.draw_h0(cfg)
-    yg, csg, ssg = gpu_decode(cfg, params, step, cs0, ss0)
-    yr, csr, ssr = oracle_decode(cfg, params, step, cs0, ss0)
+    yg, csg, ssg = gpu_decode(cfg, params, step, cs0, ss0, **opts)
+    yr, csr, ssr = oracle_decode(cfg, params, step, cs0, ss0, **opts)
     np.testing.assert_array_equal(csg, csr)
     ey = assert_close(yg, yr, cfg.io, f"{cfg.name} y")
     es = assert_close(ssg, ssr, cfg.io, f"{cfg.name} state", rounded=False)
@@ -250,6 +251,19 @@ def test_decode_small(io):
 
 def test_decode_12b_shape_20_heads_per_group():
     check_decode(small(112, seqlen=1, batch=2, nheads=160, ngroups=8))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_one_group_80_heads(io):
+    """80 heads in one group: the group's conv channels exceed one pass of the workgroup's
+    threads and each wave streams five heads."""
+    check_decode(small(114, io=io, seqlen=1, batch=2, nheads=80, ngroups=1))
+
+
+@pytest.mark.parametrize("opts", [dict(z=False), dict(D=False), dict(bias=False),
+                                  dict(z=False, D=False, bias=False)])
+def test_decode_optional_operands(opts):
+    check_decode(small(115, seqlen=1, batch=3, nheads=16, ngroups=2), **opts)
 
 
 # --------------------------------------------------------------------------- chained paths
