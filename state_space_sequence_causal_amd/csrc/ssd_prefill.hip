@@ -1399,22 +1399,22 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     const int s0 = 2 * (htid >> 4), p0 = 4 * (htid & 15);
     // per-thread element offsets inside a chunk's rows fit 32 bits; chunk bases are uniform
     const uint32_t xs = (uint32_t)x_stride, zs = (uint32_t)z_stride, ys = (uint32_t)y_stride;
-    // M^T tiles, built in halves (k steps hm of 16 source tokens): helper waves 0, 1 build
-    // tile 0 (diagonal 0), waves 2, 3 tile 2 (diagonal 1), waves 4, 5 tile 1 (block 1 from
-    // block 0); waves 6, 7 build nothing. Helper wave v runs on SIMD v % 4, so the two
-    // diagonal tiles, the costly ones, are spread over all four SIMDs. Waves 0..2 also carry
-    // the dt / pi / v records (3Q words, a word a thread).
-    const int kb = hv < 2 ? 0 : hv < 4 ? 2 : hv < 6 ? 1 : -1;
-    const int hm = hv & 1;
+    // M^T tiles: helper waves 0, 1 build tile 0 (diagonal 0) in halves (k steps hm of 16
+    // source tokens), waves 2, 3 tile 2 (diagonal 1); waves 4..7 build tile 1 (block 1 from
+    // block 0, no exponentials) in quarters of 8 source tokens. Helper wave v runs on SIMD
+    // v % 4, so every SIMD gets half a diagonal tile and a quarter of the other. Waves 0..2
+    // also carry the dt / pi / v records (3Q words, a word a thread).
+    const int kb = hv < 2 ? 0 : hv < 4 ? 2 : 1;
+    const int hm = hv & 1, hq = hv & 3;
     // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
     // copy issues a fixed sequence of memory operations and the compiler's count of
     // outstanding loads stays exact: a merged count would wait for loads just issued.
-    auto helpers = [&](auto gram_tag, auto rec_tag) {
-      constexpr bool GRAM = decltype(gram_tag)::value;
+    auto helpers = [&](auto part_tag, auto rec_tag) {
+      constexpr int PART = decltype(part_tag)::value;   // 2: a diagonal half, 4: an off quarter
       constexpr bool REC = decltype(rec_tag)::value;
       Raw4<T> rX[2], rZ[2];
       float rRec = 0.f;
-      f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7
+      f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7 (4 hq .. 4 hq + 3)
       auto load_set = [&](int c) {       // x and z of this thread's tokens
         const int64_t r0 = row0 + (int64_t)c * Q;
         const T* xc = xb + r0 * x_stride;
@@ -1467,48 +1467,51 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
         }
       };
-      auto fetch_gram = [&](int c) {   // quads 2 hm, 2 hm + 1 of the stored tile
-        if constexpr (GRAM) {
-          const float* tile = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
-                              (size_t)kb * 1024 + 512 * hm + 4 * lane;
-          gram[0] = *reinterpret_cast<const f32x4*>(tile);
-          gram[1] = *reinterpret_cast<const f32x4*>(tile + 256);
+      auto fetch_gram = [&](int c) {   // quads 2 hm, 2 hm + 1 (or quad hq) of the stored tile
+        const float* tile = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
+                            (size_t)kb * 1024 + 4 * lane;
+        if constexpr (PART == 2) {
+          gram[0] = *reinterpret_cast<const f32x4*>(tile + 512 * hm);
+          gram[1] = *reinterpret_cast<const f32x4*>(tile + 512 * hm + 256);
+        } else {
+          gram[0] = *reinterpret_cast<const f32x4*>(tile + 256 * hq);
         }
       };
       // half hm of tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t
       // and dt_s, zero above the diagonal, D on the diagonal. Register 4 j + q of the half is
       // source token 16 hm + 8 j + 4 g2 + q of the tile's source block.
       auto build = [&](int c) {
-        if constexpr (GRAM) {
+        if constexpr (PART == 4) {
+          // quarter hq of tile 1 (block 1 from block 0): v_s exp2(pi_t); registers 4 hq + q
+          // are source tokens 8 hq + 4 g2 + q, elements 4 (hq & 1) + q of k step hq >> 1
+          const float* rec = S.sRec[c % 3];
+          const float ut = exp2_hw(rec[Q + 32 + col]);
+          const f32x4 vq = *reinterpret_cast<const f32x4*>(&rec[2 * Q + 8 * hq + 4 * g2]);
+          const Split2 a = split2(gram[0][0] * (vq[0] * ut), gram[0][1] * (vq[1] * ut));
+          const Split2 d = split2(gram[0][2] * (vq[2] * ut), gram[0][3] * (vq[3] * ut));
+          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sM[c & 1][1][hq >> 1][lane]) +
+                                    8 * (hq & 1)) = make_uint2(a.hi, d.hi);
+          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sMlo[c & 1][1][hq >> 1][lane]) +
+                                    8 * (hq & 1)) = make_uint2(a.lo, d.lo);
+        } else {
           const float* rec = S.sRec[c % 3];
           const float* sDt = rec;
           const float* sPi = rec + Q;
-          const float* sV = rec + 2 * Q;
-          const int tb = kb == 0 ? 0 : 1, si = kb == 2 ? 1 : 0;
+          // half hm of a diagonal tile (token block tb onto itself)
+          const int tb = kb == 0 ? 0 : 1;
           const int tl = tb * 32 + col;
           float mv[8];
-          if (si < tb) {
-            // block 0 -> block 1: v_s exp2(pi_t)
-            const float ut = exp2_hw(sPi[tl]);
+          const float pit = sPi[tl];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const f32x4 vq = *reinterpret_cast<const f32x4*>(&sV[16 * hm + 8 * j + 4 * g2]);
+          for (int j = 0; j < 2; ++j) {
+            const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
+            const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
+            const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) mv[4 * j + q] = gram[j][q] * (vq[q] * ut);
-            }
-          } else {
-            const float pit = sPi[tl];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
-              const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
-              const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float v = (sr + q <= tl) ? gram[j][q] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
-                if (sr + q == tl) v += Dh;
-                mv[4 * j + q] = v;
-              }
+            for (int q = 0; q < 4; ++q) {
+              float v = (sr + q <= tl) ? gram[j][q] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+              if (sr + q == tl) v += Dh;
+              mv[4 * j + q] = v;
             }
           }
           Frag<T> mh, ml;
@@ -1550,9 +1553,11 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       }
       if (nC > 0) flush_y(nC - 1, false);   // y of the last chunk
     };
-    if (hv < 3) helpers(std::true_type{}, std::true_type{});
-    else if (kb >= 0) helpers(std::true_type{}, std::false_type{});
-    else helpers(std::false_type{}, std::false_type{});
+    using Half = std::integral_constant<int, 2>;
+    using Quarter = std::integral_constant<int, 4>;
+    if (hv < 3) helpers(Half{}, std::true_type{});
+    else if (hv < 4) helpers(Half{}, std::false_type{});
+    else helpers(Quarter{}, std::false_type{});
   }
 }
 
