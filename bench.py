@@ -341,7 +341,8 @@ def main():
                    "headdim": cfg.headdim, "ngroups": cfg.ngroups, "dstate": cfg.dstate,
                    "conv_width": cfg.conv_width, "chunk": args.chunk, "io": "bf16",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "mamba2_ssd_prefill (ssd_prep_kernel + ssd_scan_kernel)",
+        "roofline": {"kernel": "mamba2_ssd_prefill (" + " + ".join(
+                         k.split("IDF16b")[0] for k in counter_kernels(args.chunk)["ssd_prefill"]) + ")",
                      "bound": "hbm", "achieved": ssd_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ssd_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("ssd_prefill", args.chunk),
