@@ -1185,13 +1185,14 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 //   H waves 4..7:   the state to H_c (H wave w: state rows 32 w .. 32 w + 31, both p-blocks),
 //                   published into the other half of a double-buffered H^T.
 //   helper waves 8..15: chunk c+1's staging (flush of y(c-1), z, x^T, (w x)^T hi/lo), its
-//                   masked decay tiles M^T (in halves, by helper waves 0..5), the dt / pi / v
-//                   record of chunk c+2, and the loads for the chunks after.
+//                   masked decay tiles M^T (the diagonal ones in halves by helper waves 0..3,
+//                   the other in quarters by helper waves 4..7), the dt / pi / v record of
+//                   chunk c+2, and the loads for the chunks after.
 // Everything chunk c+1 needs goes to the other half of double-buffered LDS tiles, so the
 // barrier that ends the iteration is the only synchronisation; records are staged two chunks
 // ahead (three buffers). Four waves per SIMD (one of each kind plus two helpers) hide each
-// other's latencies. LDS tiles are unpadded, with XOR swizzles that make the MFMA operand
-// reads (16 bytes per lane, 32 rows per instruction) and the state writes conflict free.
+// other's latencies. LDS tiles are unpadded, with XOR swizzles that keep the 16-byte MFMA
+// operand reads of H^T and (w x)^T (32 rows per instruction) free of bank conflicts.
 constexpr int P64 = 64;
 constexpr int P64_THREADS = 1024;
 __device__ __forceinline__ int xs64(int p, int s) { return s ^ (8 * ((p ^ (p >> 2)) & 7)); }
