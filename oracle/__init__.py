@@ -54,7 +54,9 @@ def _load():
         lib.oracle_ssd_scan.argtypes = scan
         lib.oracle_ssd_chunked.argtypes = [_L] * 7 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
         lib.oracle_state_update.argtypes = [_L] * 6 + [_dp] * 3 + [_dp] + [_dp] * 4 + [_dp, _dp, _dp, ctypes.c_int]
-        for f in ("oracle_conv1d", "oracle_ssd_scan", "oracle_ssd_chunked", "oracle_state_update"):
+        lib.oracle_group_rmsnorm.argtypes = [_L, _L, _L, _dp, _dp, ctypes.c_double, _dp]
+        for f in ("oracle_conv1d", "oracle_ssd_scan", "oracle_ssd_chunked", "oracle_state_update",
+                  "oracle_group_rmsnorm"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -146,6 +148,19 @@ def state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_sta
                                 _p(bias), _p(cs), _p(dt_raw_t), _p(dt_bias), _p(A), _p(D),
                                 _p(z_t), _p(ss), _p(y), int(nthreads))
     return y, cs, ss
+
+
+def group_rmsnorm(g, weight=None, *, ngroups: int, eps: float = 1e-5):
+    """Group RMSNorm of the gated output g [..][width]: each row is cut into ngroups
+    contiguous groups, each scaled by 1 / sqrt(mean of squares + eps), then by weight."""
+    g = _d(g)
+    width = g.shape[-1]
+    if width % ngroups:
+        raise ValueError("width must be a multiple of ngroups")
+    rows = g.size // width
+    out = np.empty_like(g)
+    _load().oracle_group_rmsnorm(rows, width, ngroups, _p(g), _p(_d(weight)), float(eps), _p(out))
+    return out
 
 
 def split_xbc(xbc, nheads: int, ngroups: int, headdim: int = 64, dstate: int = 128):

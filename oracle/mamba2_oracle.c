@@ -21,7 +21,13 @@
  *
  * Readings where the pages are silent: conv taps are a cross-correlation with
  * w[c][W-1] on the current token; SiLU follows the conv bias on every channel;
- * dt * B x^T is taken literally (no zero-order-hold factor); no RMSNorm.
+ * dt * B x^T is taken literally (no zero-order-hold factor); the scan's output
+ * carries no RMSNorm.
+ *
+ * Group RMSNorm of the gated output (the block's RMSNorm, hyper.ai summary,
+ * section "方法", applied after the SiLU(z) gate): each row of width channels
+ * is cut into G contiguous groups; within a group,
+ *   out[k] = g[k] / sqrt(mean_group(g^2) + eps) * weight[k].
  *
  * Three forms are provided so that they pin one another:
  *   O1 oracle_ssd_scan     -- the plain recurrence above, token by token;
@@ -241,4 +247,22 @@ void oracle_state_update(long B, long H, long P, long G, long N, long W, const d
   free(bs);
   free(xs);
   free(xbc);
+}
+
+/* Group RMSNorm of rows of the gated output g (rows x width, width divisible by G):
+ * out[r][k] = g[r][k] / sqrt(mean over k' in k's group of g[r][k']^2 + eps) * weight[k]
+ * (weight NULL means ones). */
+void oracle_group_rmsnorm(long rows, long width, long G, const double* g, const double* weight,
+                          double eps, double* out) {
+  const long gs = width / G;
+  for (long r = 0; r < rows; ++r) {
+    for (long q = 0; q < G; ++q) {
+      const double* gr = g + r * width + q * gs;
+      double ss = 0.0;
+      for (long k = 0; k < gs; ++k) ss += gr[k] * gr[k];
+      const double inv = 1.0 / sqrt(ss / (double)gs + eps);
+      for (long k = 0; k < gs; ++k)
+        out[r * width + q * gs + k] = gr[k] * inv * (weight ? weight[q * gs + k] : 1.0);
+    }
+  }
 }
