@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 1
+#define MAMBA2_ABI_VERSION 2
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -158,6 +158,27 @@ int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w
                         const float* bias, void* conv_state, const void* dt_raw_t,
                         const float* dt_bias, const float* A, const float* D, const void* z_t,
                         float* ssm_state, void* y_t, void* stream);
+
+/*
+ * mamba2_group_rmsnorm -- the block's RMSNorm of the gated output (hyper.ai summary,
+ * section "方法"), taken after the SiLU(z) gate over each of the G groups of
+ * d_inner / G contiguous channels (d_inner = H * P):
+ *     out[k] = g[k] / sqrt(mean over k's group of g^2 + eps) * weight[k]
+ * It applies to the y of mamba2_ssd_prefill (B * L rows) or of mamba2_state_update
+ * (dims->seqlen = 1, B rows).
+ *
+ *   g       [B][L][H*P] io, row stride g_stride (elements): the gated output
+ *   weight  [H*P] f32, or NULL for ones
+ *   eps     finite and >= 0 (the Mamba-2 block uses 1e-5)
+ *   out     [B][L][H*P] io, row stride out_stride; may be g itself (same stride: in
+ *           place), must not otherwise overlap g or weight
+ * Each group's sum of squares is formed in fp32 in a fixed order, so results are
+ * identical from run to run. d_inner / G must be a multiple of 8 (bf16) or 4 (f32),
+ * which headdim 64 guarantees. With seqlen 0 the call does nothing.
+ */
+int mamba2_group_rmsnorm(const mamba2_dims* dims, const void* g, int64_t g_stride,
+                         const float* weight, float eps, void* out, int64_t out_stride,
+                         void* stream);
 
 /* Description of the last failure on the calling thread ("" after success). */
 const char* mamba2_last_error(void);

@@ -29,12 +29,14 @@ __all__ = [
     "Config", "CONFIGS", "config", "bf16_round", "bf16_bits", "bits_to_f32",
     "draw_params", "draw_xbc", "draw_z", "draw_dt_raw", "draw_h0",
     "draw_conv_state", "draw_prefill", "draw_decode_step", "draw_decode_steps", "TOKEN_BLOCK",
+    "draw_gated", "draw_norm_weight",
 ]
 
 TOKEN_BLOCK = 256  # tokens per independently seeded block
 
 # tensor ids (part of the stream key; never renumber)
 _T_ALOG, _T_DTB, _T_D, _T_CW, _T_CB, _T_XBC, _T_Z, _T_DT, _T_H0, _T_CS = range(10)
+_T_GATED, _T_NW = 10, 11
 
 
 @dataclasses.dataclass(frozen=True)
@@ -281,3 +283,21 @@ def draw_decode_step(cfg: Config, step: int) -> Dict[str, np.ndarray]:
         "z": draw_z(cfg, 0, 1, step=step),
         "dt_raw": draw_dt_raw(cfg, 0, 1, step=step),
     }
+
+
+def _gated_fill(rng, n, width):
+    a = rng.standard_normal((n, width), dtype=np.float32)
+    return a * np.exp(np.float32(0.5) * rng.standard_normal((n, width), dtype=np.float32))
+
+
+def draw_gated(cfg: Config, t0: int = 0, t1: Optional[int] = None) -> np.ndarray:
+    """Stand-in for the gated layer output y * SiLU(z), rows [B][t1-t0][d_inner]: N(0,1) times
+    a log-normal scale exp(N(0, 1/4)), which gives the heavy tails the gated output has.
+    Rounded to the config's I/O type."""
+    t0, t1, stream = _span(cfg, t0, t1, -1)
+    return _tokens(cfg, _T_GATED, cfg.d_inner, t0, t1, _gated_fill, stream, cfg.io)
+
+
+def draw_norm_weight(cfg: Config) -> np.ndarray:
+    """Per-channel RMSNorm weight [d_inner] ~ U(0.5, 1.5), fp32."""
+    return _rng(cfg.seed, _T_NW).uniform(0.5, 1.5, cfg.d_inner).astype(np.float32)

@@ -61,7 +61,8 @@ lib.mamba2_ssd_prefill_workspace_bytes.restype = _sz
 lib.mamba2_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                    _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
 lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update"):
+lib.mamba2_group_rmsnorm.argtypes = [_dims, _vp, _i64, _vp, ctypes.c_float, _vp, _i64, _vp]
+for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -147,3 +148,19 @@ def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, 
     _check(lib.mamba2_state_update(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_state),
                                    _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
                                    _ptr(ssm_state), _ptr(y_t), _stream()))
+
+
+def mamba2_group_rmsnorm(g, weight, out, *, ngroups: int, eps: float = 1e-5) -> None:
+    """Group RMSNorm of the gated output g ([B, L, H*P] or [B, H*P]) into out (may be g)."""
+    if g.dim() == 2:
+        B, W = g.shape
+        L, gs, os_ = 1, W, out.shape[-1]
+        gs, os_ = (g.stride(0) if g.numel() else W), (out.stride(0) if out.numel() else W)
+        if g.stride(-1) != 1 or out.stride(-1) != 1:
+            raise Mamba2Error(2, "the last dimension must be contiguous")
+    else:
+        B, L, W = g.shape
+        gs, os_ = _row_stride(g), _row_stride(out)
+    d = make_dims(B, L, W // 64, ngroups, 64, io_dtype_of(g))
+    _check(lib.mamba2_group_rmsnorm(ctypes.byref(d), _ptr(g), gs, _ptr(weight), float(eps), _ptr(out),
+                                    os_, _stream()))

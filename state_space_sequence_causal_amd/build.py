@@ -1,6 +1,6 @@
 """Build libmamba2.so in-tree with hipcc for gfx950.
 
-    python -m state_space_sequence_causal_amd.build
+    python state_space_sequence_causal_amd/build.py
 
 Every HIP source is compiled with packed-FP32 instructions disabled (the code
 never relies on them), objects in parallel, then linked into one shared
@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmamba2.so")
-SOURCES = ["conv1d.hip", "ssd_prefill.hip", "state_update.hip", "mamba2_api.cpp"]
+SOURCES = ["conv1d.hip", "ssd_prefill.hip", "state_update.hip", "rmsnorm.hip", "mamba2_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

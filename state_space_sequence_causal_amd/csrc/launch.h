@@ -42,4 +42,9 @@ struct DecodeArgs {
 };
 hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream);
 
+// rows x width io elements (row strides in elements), width = G contiguous groups
+hipError_t launch_group_rmsnorm(int io_bf16, const void* g, int64_t g_stride, const float* weight,
+                                float eps, void* out, int64_t out_stride, int64_t rows, int G,
+                                int width, hipStream_t stream);
+
 }  // namespace m2

@@ -213,3 +213,26 @@ M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const f
   return hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, static_cast<hipStream_t>(stream)),
                     "state_update launch");
 }
+
+M2_EXPORT int mamba2_group_rmsnorm(const mamba2_dims* d, const void* g, int64_t g_stride,
+                                   const float* weight, float eps, void* out, int64_t out_stride,
+                                   void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return fail(MAMBA2_ERR_SHAPE, "eps must be finite and >= 0");
+  if (d->seqlen == 0) return ok();
+  if (!g || !out) return fail(MAMBA2_ERR_NULL, "g and out must not be NULL");
+  const int io = d->io_dtype, es = esize_of(io);
+  const int64_t width = (int64_t)d->nheads * d->headdim, rows = (int64_t)d->batch * d->seqlen;
+  if ((st = check_stride("g", g, g_stride, width, io))) return st;
+  if ((st = check_stride("out", out, out_stride, width, io))) return st;
+  if (weight && !aligned16(weight)) return fail(MAMBA2_ERR_ALIGN, "weight is not 16-byte aligned");
+  Range ro = span(out, rows, out_stride, width, es), rg = span(g, rows, g_stride, width, es);
+  Range rw = span(weight, 1, 0, width, 4);
+  const bool in_place = out == g && out_stride == g_stride;
+  if (overlap(ro, rw) || (!in_place && overlap(ro, rg)))
+    return fail(MAMBA2_ERR_ALIAS, "out overlaps g (other than exactly in place) or weight");
+  return hip_status(m2::launch_group_rmsnorm(io == MAMBA2_BF16, g, g_stride, weight, eps, out, out_stride,
+                                             rows, d->ngroups, (int)width, static_cast<hipStream_t>(stream)),
+                    "group_rmsnorm launch");
+}

@@ -25,7 +25,7 @@ def declared():
 
 def test_header_declares_the_calls():
     names = declared()
-    for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update",
+    for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm",
               "mamba2_ssd_prefill_workspace_bytes", "mamba2_last_error", "mamba2_abi_version"):
         assert n in names
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 1
+    assert m2.mamba2_abi_version() == 2
 
 
 def dims(**kw):
@@ -153,3 +153,25 @@ def test_workspace_size_formula():
 ])
 def test_prefill_rejects_workspace(kw, code):
     assert prefill(dims(), **kw) == code, m2.mamba2_last_error()
+
+
+def rmsnorm(d, **kw):
+    a = dict(g=BASE, gs=d.nheads * 64, w=BASE + 8 * MB, eps=1e-5, out=BASE + 16 * MB, os=d.nheads * 64)
+    a.update(kw)
+    return m2.lib.mamba2_group_rmsnorm(ctypes.byref(d), a["g"], a["gs"], a["w"], a["eps"], a["out"],
+                                       a["os"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=None), ENULL), (dict(out=None), ENULL), (dict(gs=200), ESHAPE), (dict(eps=-1.0), ESHAPE),
+    (dict(eps=float("nan")), ESHAPE), (dict(eps=float("inf")), ESHAPE), (dict(gs=258), EALIGN),
+    (dict(g=BASE + 4), EALIGN), (dict(w=BASE + 8 * MB + 4), EALIGN),
+    (dict(out=BASE + 1024), EALIAS), (dict(out=BASE, os=512), EALIAS), (dict(w=BASE + 16 * MB), EALIAS),
+])
+def test_rmsnorm_rejects(kw, code):
+    assert rmsnorm(dims(), **kw) == code, m2.mamba2_last_error()
+
+
+def test_rmsnorm_rejects_model_shape():
+    assert rmsnorm(dims(nheads=6, ngroups=4)) == ESHAPE
+    assert rmsnorm(dims(seqlen=0), g=None, out=None) == OK
