@@ -10,7 +10,8 @@ tiling parameter and does not change what is computed (the GPU tests check
 chunks 64, 128 and 256 against the oracle). The workload's listed chunk of 128
 is timed in the same run and reported under "kernels". The one-token decode
 state update is measured in the same run on the 9B-shape batch-64 decode
-workload and reported under "decode".
+workload and reported under "decode"; the group RMSNorm of the gated output
+(not part of the step) under "kernels" as well.
 
 Per-kernel durations come from HIP events recorded around each launch on the
 stream the kernels run on (torch's current stream). Algorithmic bytes count
@@ -41,6 +42,7 @@ KERNEL_SOURCES = {
     "ssd_prefill": ["ssd_prefill.hip", "device.h"],
     "state_update": ["state_update.hip", "device.h"],
     "conv1d": ["conv1d.hip", "device.h"],
+    "group_rmsnorm": ["rmsnorm.hip", "device.h"],
 }
 
 
@@ -176,6 +178,30 @@ def run_decode(args, torch, m2, si):
     return cfg, sum(times) / n, times[n // 2]
 
 
+def run_rmsnorm(args, torch, m2, si, cfg):
+    """The group RMSNorm over the prefill's gated output shape (seeded stand-in input)."""
+    g = torch.from_numpy(si.bf16_bits(si.draw_gated(cfg)).view("int16")).view(torch.bfloat16).cuda()
+    w = torch.from_numpy(si.draw_norm_weight(cfg)).cuda()
+    out = torch.empty_like(g)
+
+    def step():
+        m2.mamba2_group_rmsnorm(g, w, out, ngroups=cfg.ngroups)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / args.steps
+    nbytes = 2 * g.numel() * g.element_size() + w.numel() * 4
+    return us, nbytes
+
+
 CALIB_BYTES = 1 << 30
 
 
@@ -225,7 +251,8 @@ def counter_kernels(chunk: int) -> dict:
         chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
     return {"ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}E", scan],
             "conv1d": ["conv1d_kernel"],
-            "state_update": ["state_update_kernel"]}
+            "state_update": ["state_update_kernel"],
+            "group_rmsnorm": ["group_rmsnorm_kernel"]}
 
 
 def _counter_means(path: str, counter: str):
@@ -320,6 +347,7 @@ def main():
     tokens = cfg.batch * cfg.seqlen
     ssd_gbs = by["ssd"] / (ssd_us * 1e-6) / 1e9
     dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
+    rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -363,6 +391,11 @@ def main():
                    "traffic": measured_traffic("state_update")},
         "wall_s_timed": wall,
     }
+    out["kernels"]["group_rmsnorm"] = {
+        "us": rms_us, "GB_s": rms_bytes / (rms_us * 1e-6) / 1e9,
+        "frac": rms_bytes / (rms_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": rms_bytes,
+        "traffic": measured_traffic("group_rmsnorm"),
+        "note": "block RMSNorm of the gated output over 8 groups of 1280 channels (not in the step)"}
     if alt is not None:
         out["kernels"][f"ssd_prefill_chunk{cfg.chunk}"] = {
             "us": alt[3], "tokens_per_s": tokens / (alt[3] * 1e-6),

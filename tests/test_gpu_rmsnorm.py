@@ -71,7 +71,7 @@ def test_rmsnorm_in_place_no_weight_strided():
     assert_close(og, ref, "bf16", "strided")
 
 
-@pytest.mark.parametrize("heads,groups", [(16, 1), (8, 8), (20, 4)])
+@pytest.mark.parametrize("heads,groups", [(16, 1), (8, 8), (20, 4), (64, 1)])
 def test_rmsnorm_group_widths(heads, groups):
     og, ref = run(small(205, nheads=heads, ngroups=groups, io="f32"))
     assert_close(og, ref, "f32", f"{heads} heads / {groups} groups")
