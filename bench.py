@@ -1,17 +1,18 @@
 """Benchmark of the Mamba-2 layer core on one MI355X.
 
 One step = one pass of the prefill hot path over one batch of synthetic input
-already resident in HBM: mamba2_conv1d (width-4 causal conv + SiLU over the xBC
-channels) followed by mamba2_ssd_prefill (the fused chunked scan), on the
-12B-shape single-layer workload: B=1, L=8192, 160 heads x 64, 8 groups,
-d_state 128, bf16 io, fp32 state. ``value`` is prefill tokens/s of that step.
-The scan runs with chunk length 64 (--chunk): the chunk length is the scan's
-tiling parameter and does not change what is computed (the GPU tests check
-chunks 64, 128 and 256 against the oracle). The workload's listed chunk of 128
-is timed in the same run and reported under "kernels". The one-token decode
-state update is measured in the same run on the 9B-shape batch-64 decode
-workload and reported under "decode"; the group RMSNorm of the gated output
-(not part of the step) under "kernels" as well.
+already resident in HBM: mamba2_conv_ssd_prefill, the width-4 causal conv + SiLU
+over the raw xBC channels and the chunked scan in one call (at chunk 64 the conv
+runs inside the scan's kernels), on the 12B-shape single-layer workload: B=1,
+L=8192, 160 heads x 64, 8 groups, d_state 128, bf16 io, fp32 state. ``value`` is
+prefill tokens/s of that step. The chunk length (--chunk, 64) is the scan's tiling
+parameter and does not change what is computed (the GPU tests check chunks 64, 128
+and 256 against the oracle). The same run reports under "kernels": the two-call
+path (mamba2_conv1d, then mamba2_ssd_prefill) at the same chunk, and the one call at
+the workload's listed chunk of 128. The one-token decode state update is measured
+in the same run on the 9B-shape batch-64 decode workload and reported under
+"decode"; the group RMSNorm of the gated output (not part of the step) under
+"kernels" as well.
 
 Per-kernel durations come from HIP events recorded around each launch on the
 stream the kernels run on (torch's current stream). Algorithmic bytes count
@@ -39,6 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "SSD prefill tokens/s @12B-shape L=8k; decode state-update GB/s % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
+    "conv_ssd_prefill": ["ssd_prefill.hip", "device.h"],
     "ssd_prefill": ["ssd_prefill.hip", "device.h"],
     "state_update": ["state_update.hip", "device.h"],
     "conv1d": ["conv1d.hip", "device.h"],
@@ -80,7 +82,10 @@ def prefill_bytes(cfg) -> dict:
     ssd += B * H * N * P * 4                                     # h_final (h0 = 0 is not read)
     ssd += 3 * H * 4                                             # dt_bias, A, D
     conv = tok * 2 * Cc * e + Cc * 5 * 4 + 2 * B * 3 * Cc * e    # u, out; w, bias; conv cache
-    return {"ssd": ssd, "conv": conv}
+    # the one call reads the raw xBC in place of the conv output: the scan's bytes plus the
+    # conv parameters and the conv cache in and out
+    fused = ssd + Cc * 5 * 4 + 2 * B * 3 * Cc * e
+    return {"ssd": ssd, "conv": conv, "fused": fused}
 
 
 def prefill_flops(cfg) -> float:
@@ -99,36 +104,45 @@ def decode_bytes(cfg) -> int:
 
 
 # ------------------------------------------------------------------------------ GPU parts
-def run_prefill(args, torch, m2, si, cfg, inp, chunk):
+def run_prefill(args, torch, m2, si, cfg, inp, chunk, fused=True):
+    """Times the prefill step at ``chunk``: the one call (fused=True) or mamba2_conv1d then
+    mamba2_ssd_prefill. Returns ms per step, wall seconds and the per-call microseconds."""
     dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
     f32 = lambda a: torch.from_numpy(a).cuda()
     u, z, dt = dev(inp["xbc"]), dev(inp["z"]), dev(inp["dt_raw"])
     w, bias, dtb, A, D = (f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
     di, gn = cfg.d_inner, cfg.ngroups * cfg.dstate
-    xbc = torch.empty_like(u)
-    x, Bm, Cm = xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:]
     cs = torch.zeros((cfg.batch, 3, cfg.conv_channels), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((cfg.batch, cfg.seqlen, di), dtype=torch.bfloat16, device="cuda")
     hf = torch.empty((cfg.batch, cfg.nheads, cfg.dstate, cfg.headdim), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m2.mamba2_ssd_prefill_workspace_bytes(
-        m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, chunk, m2.MAMBA2_BF16)),
-        dtype=torch.uint8, device="cuda")
+    dims = m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, chunk, m2.MAMBA2_BF16)
+    if fused:
+        ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+
+        def calls():
+            m2.mamba2_conv_ssd_prefill(u, w, bias, cs, dt, dtb, A, D, z, None, hf, y,
+                                       ngroups=cfg.ngroups, chunk=chunk, workspace=ws)
+        calls = [calls]
+    else:
+        ws = torch.empty(m2.mamba2_ssd_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+        xbc = torch.empty_like(u)
+        x, Bm, Cm = xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:]
+        calls = [lambda: m2.mamba2_conv1d(u, w, bias, cs, xbc),
+                 lambda: m2.mamba2_ssd_prefill(x, Bm, Cm, dt, dtb, A, D, z, None, hf, y,
+                                               ngroups=cfg.ngroups, chunk=chunk, workspace=ws)]
 
     def step(evs=None):
+        for i, f in enumerate(calls):
+            if evs:
+                evs[i].record()
+            f()
         if evs:
-            evs[0].record()
-        m2.mamba2_conv1d(u, w, bias, cs, xbc)
-        if evs:
-            evs[1].record()
-        m2.mamba2_ssd_prefill(x, Bm, Cm, dt, dtb, A, D, z, None, hf, y, ngroups=cfg.ngroups,
-                              chunk=chunk, workspace=ws)
-        if evs:
-            evs[2].record()
+            evs[-1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -139,9 +153,8 @@ def run_prefill(args, torch, m2, si, cfg, inp, chunk):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_start.elapsed_time(t_end)
-    conv_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / args.steps
-    ssd_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1e3 / args.steps
-    return total_ms / args.steps, wall, conv_us, ssd_us
+    per_call = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / args.steps for i in range(len(calls))]
+    return total_ms / args.steps, wall, per_call
 
 
 def run_decode(args, torch, m2, si):
@@ -252,9 +265,11 @@ def cpu_baseline(cfg, inp):
 def counter_kernels(chunk: int) -> dict:
     """traffic entry -> (mangled) kernel-name fragments summed per call, for the bf16 prefill
     at chunk length ``chunk``"""
-    scan = {64: "ssd_scan64_kernel", 256: "ssd_scan_wide_kernelIDF16bLi256E"}.get(
-        chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
-    return {"ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}E", scan],
+    scan = {64: ("ssd_scan64_kernelILb0E", "ssd_scan64_kernel<false>"),
+            256: "ssd_scan_wide_kernelIDF16bLi256E"}.get(chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
+    return {"conv_ssd_prefill": ["ssd_prep_kernelIDF16bLi64ELb1E",
+                                 ("ssd_scan64_kernelILb1E", "ssd_scan64_kernel<true>")],
+            "ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}ELb0E", scan],
             "conv1d": ["conv1d_kernel"],
             "state_update": ["state_update_kernel"],
             "group_rmsnorm": ["group_rmsnorm_kernel"]}
@@ -289,7 +304,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, chunk: int) -> dict:
         raise SystemExit("no calibration dispatch found: run the counter passes with --copy-calibration")
 
     def pick(table, frag):
-        hits = [v for k, v in table.items() if frag in k]
+        alts = frag if isinstance(frag, tuple) else (frag,)   # mangled or demangled name
+        hits = [v for k, v in table.items() if any(a in k for a in alts)]
         if len(hits) != 1:
             raise SystemExit(f"expected one kernel matching {frag!r}, found {len(hits)}: "
                              f"{sorted(table)}")
@@ -306,6 +322,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, chunk: int) -> dict:
                     "bytes_per_launch": fb + wb, "kernels": frags}
         if key == "ssd_prefill":
             out[key]["chunk"] = chunk
+        if key == "conv_ssd_prefill":
+            out[key]["chunk"] = 64
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -343,7 +361,8 @@ def main():
         copy_calibration(torch)
     cfg = si.CONFIGS[1]
     inp = si.draw_prefill(cfg)
-    ms_step, wall, conv_us, ssd_us = run_prefill(args, torch, m2, si, cfg, inp, args.chunk)
+    ms_step, wall, (step_us,) = run_prefill(args, torch, m2, si, cfg, inp, args.chunk)
+    _, _, (conv_us, ssd_us) = run_prefill(args, torch, m2, si, cfg, inp, args.chunk, fused=False)
     alt = None
     if args.chunk != cfg.chunk:
         alt = run_prefill(args, torch, m2, si, cfg, inp, cfg.chunk)
@@ -351,6 +370,9 @@ def main():
     fl = prefill_flops(cfg)
     tokens = cfg.batch * cfg.seqlen
     ssd_gbs = by["ssd"] / (ssd_us * 1e-6) / 1e9
+    step_gbs = by["fused"] / (step_us * 1e-6) / 1e9
+    fused_kernels = counter_kernels(64)["conv_ssd_prefill"] if args.chunk == 64 else \
+        ["conv1d_kernel"] + counter_kernels(args.chunk)["ssd_prefill"]
     dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
     rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
     dby = decode_bytes(dcfg)
@@ -369,24 +391,32 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "12B-shape Mamba-2 layer-core prefill: conv1d + chunked SSD scan",
+        "config": {"workload": "12B-shape Mamba-2 layer-core prefill: conv1d + chunked SSD scan (one call)",
                    "batch": cfg.batch, "seq_len": cfg.seqlen, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "ngroups": cfg.ngroups, "dstate": cfg.dstate,
                    "conv_width": cfg.conv_width, "chunk": args.chunk, "io": "bf16",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "mamba2_ssd_prefill (" + " + ".join(
-                         k.split("IDF16b")[0] for k in counter_kernels(args.chunk)["ssd_prefill"]) + ")",
-                     "bound": "hbm", "achieved": ssd_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ssd_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("ssd_prefill", args.chunk),
-                     "algorithmic_bytes": by["ssd"], "avg_launch_us": ssd_us},
+        "roofline": {"kernel": "mamba2_conv_ssd_prefill (" + (
+                         "ssd_prep_kernel<bf16, 64, conv> + ssd_scan64_kernel<conv>" if args.chunk == 64 else
+                         " + ".join(k.split("IDF16b")[0] for k in fused_kernels)) + ")",
+                     "bound": "hbm", "achieved": step_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("conv_ssd_prefill", 64) if args.chunk == 64 else None,
+                     "algorithmic_bytes": by["fused"], "avg_launch_us": step_us},
         "kernels": {
+            "conv_ssd_prefill": {"us": step_us, "tokens_per_s": tokens / (step_us * 1e-6), "GB_s": step_gbs,
+                                 "algorithmic_TFLOP_s": fl / (step_us * 1e-6) / 1e12},
             "ssd_prefill": {"us": ssd_us, "tokens_per_s": tokens / (ssd_us * 1e-6), "GB_s": ssd_gbs,
+                            "frac": ssd_gbs / HBM_PEAK_GBS, "algorithmic_bytes": by["ssd"],
                             "algorithmic_TFLOP_s": fl / (ssd_us * 1e-6) / 1e12,
-                            "mfma_frac_algorithmic": fl / (ssd_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+                            "mfma_frac_algorithmic": fl / (ssd_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                            "traffic": measured_traffic("ssd_prefill", args.chunk),
+                            "note": "two-call path: the scan after mamba2_conv1d"},
             "conv1d": {"us": conv_us, "GB_s": by["conv"] / (conv_us * 1e-6) / 1e9,
                        "frac": by["conv"] / (conv_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                       "traffic": measured_traffic("conv1d")},
+                       "traffic": measured_traffic("conv1d"),
+                       "note": "two-call path: the conv over all xBC channels"},
+            "two_call_step_us": conv_us + ssd_us,
         },
         "decode": {"workload": "9B-shape decode state update: B=64, 128 heads x 64, 8 groups, "
                                "d_state 128, bf16 io, fp32 state (256 MiB), in place",
@@ -402,9 +432,10 @@ def main():
         "traffic": measured_traffic("group_rmsnorm"),
         "note": "block RMSNorm of the gated output over 8 groups of 1280 channels (not in the step)"}
     if alt is not None:
-        out["kernels"][f"ssd_prefill_chunk{cfg.chunk}"] = {
-            "us": alt[3], "tokens_per_s": tokens / (alt[3] * 1e-6),
-            "step_tokens_per_s": tokens / (alt[0] * 1e-3)}
+        out["kernels"][f"conv_ssd_prefill_chunk{cfg.chunk}"] = {
+            "us": alt[2][0], "tokens_per_s": tokens / (alt[2][0] * 1e-6),
+            "note": "the one call at the listed chunk runs mamba2_conv1d into the workspace, "
+                    "then the chunk-128 scan"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(out))

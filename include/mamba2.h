@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 2
+#define MAMBA2_ABI_VERSION 3
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -132,13 +132,51 @@ size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
  *           MAMBA2_ERR_WORKSPACE if missing or too small
  * x/B/C may be views into one xBC tensor (row stride = its channel count).
  * With seqlen 0 nothing per-token is read or written (those pointers may be
- * NULL) and h_final receives h0 (or zeros).
+ * NULL) and h_final receives h0 (or zeros). Row strides above 2^25 elements are
+ * rejected (MAMBA2_ERR_SHAPE).
  */
 int mamba2_ssd_prefill(const mamba2_dims* dims, const void* x, int64_t x_stride, const void* Bm,
                        int64_t b_stride, const void* Cm, int64_t c_stride, const void* dt_raw,
                        const float* dt_bias, const float* A, const float* D, const void* z,
                        int64_t z_stride, const float* h0, float* h_final, void* y,
                        int64_t y_stride, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mamba2_conv_ssd_prefill_workspace_bytes -- device workspace mamba2_conv_ssd_prefill
+ * needs for `dims` (0 if `dims` is invalid). For bf16 io at chunk 64 it equals
+ * mamba2_ssd_prefill_workspace_bytes(dims); for the other supported settings it adds
+ * batch * seqlen * Cc io elements (after rounding the former up to 256 bytes), where
+ * the conv output is kept between the two steps.
+ */
+size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
+
+/*
+ * mamba2_conv_ssd_prefill -- the prefill of the layer core from the raw xBC
+ * projection: mamba2_conv1d over all Cc = H*P + 2*G*N xBC channels followed by
+ * mamba2_ssd_prefill on its x, B and C columns (the conv and the scan of the
+ * block: hyper.ai summary, section "方法"). For bf16 io at chunk 64 the conv is
+ * applied inside the scan's kernels as they stage each chunk, so the conv output
+ * never goes through device memory; the results are bitwise those of the two calls
+ * in sequence. Other supported settings run the two steps through the workspace.
+ *
+ *   xBC        [B][L][Cc] io raw (pre-conv) x | B | C, row stride xbc_stride
+ *   conv_w     [Cc][4] f32; conv_bias [Cc] f32 or NULL
+ *   conv_state [B][3][Cc] io, dense, or NULL: the raw history before token 0
+ *              (zeros if NULL), replaced by the last 3 raw inputs of (history,
+ *              xBC), as mamba2_conv1d does
+ *   dt_raw, dt_bias, A, D, z, h0, h_final, y: as in mamba2_ssd_prefill
+ *   workspace, workspace_bytes: at least mamba2_conv_ssd_prefill_workspace_bytes(dims)
+ *              bytes, 16-byte aligned, not overlapping any other argument
+ * y, conv_state, h_final and the workspace must not overlap each other or any
+ * input (h_final may equal h0). With seqlen 0 the history is unchanged and
+ * h_final receives h0 (or zeros).
+ */
+int mamba2_conv_ssd_prefill(const mamba2_dims* dims, const void* xBC, int64_t xbc_stride,
+                            const float* conv_w, const float* conv_bias, void* conv_state,
+                            const void* dt_raw, const float* dt_bias, const float* A,
+                            const float* D, const void* z, int64_t z_stride, const float* h0,
+                            float* h_final, void* y, int64_t y_stride, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * mamba2_state_update -- one decode token per sequence (dims->seqlen must be

@@ -18,7 +18,9 @@ from typing import Optional
 __all__ = [
     "LIB_PATH", "Mamba2Error", "Dims", "lib", "io_dtype_of",
     "mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update",
-    "mamba2_ssd_prefill_workspace_bytes", "mamba2_abi_version", "mamba2_last_error",
+    "mamba2_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill",
+    "mamba2_conv_ssd_prefill_workspace_bytes", "mamba2_group_rmsnorm",
+    "mamba2_abi_version", "mamba2_last_error",
     "MAMBA2_F32", "MAMBA2_BF16", "STATUS",
 ]
 
@@ -60,9 +62,14 @@ lib.mamba2_ssd_prefill_workspace_bytes.argtypes = [_dims]
 lib.mamba2_ssd_prefill_workspace_bytes.restype = _sz
 lib.mamba2_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                    _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
+lib.mamba2_conv_ssd_prefill_workspace_bytes.argtypes = [_dims]
+lib.mamba2_conv_ssd_prefill_workspace_bytes.restype = _sz
+lib.mamba2_conv_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
 lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.mamba2_group_rmsnorm.argtypes = [_dims, _vp, _i64, _vp, ctypes.c_float, _vp, _i64, _vp]
-for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm"):
+for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_conv_ssd_prefill", "mamba2_state_update",
+           "mamba2_group_rmsnorm"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -140,6 +147,28 @@ def mamba2_ssd_prefill(x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, h_final, y, *, n
         _ptr(workspace), ws_bytes, _stream()))
 
 
+def mamba2_conv_ssd_prefill_workspace_bytes(d: Dims) -> int:
+    return lib.mamba2_conv_ssd_prefill_workspace_bytes(ctypes.byref(d))
+
+
+def mamba2_conv_ssd_prefill(xBC, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z, h0,
+                            h_final, y, *, ngroups: int, chunk: int, workspace=None) -> None:
+    """conv1d over the raw xBC ([B, L, Cc], row-strided) then the scan, in one call;
+    conv_state ([B, 3, Cc] or None) is updated in place."""
+    B, L, H = dt_raw.shape
+    d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(xBC))
+    if workspace is None:
+        need = lib.mamba2_conv_ssd_prefill_workspace_bytes(ctypes.byref(d))
+        if need:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=dt_raw.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.mamba2_conv_ssd_prefill(
+        ctypes.byref(d), _ptr(xBC), _row_stride(xBC), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
+        _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z), 0 if z is None else _row_stride(z),
+        _ptr(h0), _ptr(h_final), _ptr(y), _row_stride(y), _ptr(workspace), ws_bytes, _stream()))
+
+
 def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,
                         *, ngroups: int) -> None:
     """One decode token; conv_state and ssm_state are updated in place."""
@@ -154,7 +183,7 @@ def mamba2_group_rmsnorm(g, weight, out, *, ngroups: int, eps: float = 1e-5) -> 
     """Group RMSNorm of the gated output g ([B, L, H*P] or [B, H*P]) into out (may be g)."""
     if g.dim() == 2:
         B, W = g.shape
-        L, gs, os_ = 1, W, out.shape[-1]
+        L = 1
         gs, os_ = (g.stride(0) if g.numel() else W), (out.stride(0) if out.numel() else W)
         if g.stride(-1) != 1 or out.stride(-1) != 1:
             raise Mamba2Error(2, "the last dimension must be contiguous")

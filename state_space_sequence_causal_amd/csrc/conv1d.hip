@@ -31,11 +31,11 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
   const T* ub = u + (int64_t)b * L * u_stride + c0;
   T* ob = out + (int64_t)b * L * out_stride + c0;
 
-  float wt[VE][CONV_W], bs[VE];
+  f32x4 wt[VE];
+  float bs[VE];
 #pragma unroll
   for (int i = 0; i < VE; ++i) {
-    f32x4 wv = *reinterpret_cast<const f32x4*>(w + (int64_t)(c0 + i) * CONV_W);
-    wt[i][0] = wv[0]; wt[i][1] = wv[1]; wt[i][2] = wv[2]; wt[i][3] = wv[3];
+    wt[i] = *reinterpret_cast<const f32x4*>(w + (int64_t)(c0 + i) * CONV_W);
     bs[i] = bias ? bias[c0 + i] : 0.f;
   }
 
@@ -61,11 +61,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
     for (int k = 0; k < U; ++k) {
       Vec<T> o;
 #pragma unroll
-      for (int i = 0; i < VE; ++i) {
-        float v = bs[i] + wt[i][0] * e0.get(i) + wt[i][1] * e1.get(i) + wt[i][2] * e2.get(i) +
-                  wt[i][3] * cur[k].get(i);
-        o.set(i, silu_fast(v));
-      }
+      for (int i = 0; i < VE; ++i)
+        o.set(i, conv4_silu(wt[i], bs[i], e0.get(i), e1.get(i), e2.get(i), cur[k].get(i)));
       st16(ob + (int64_t)(t + k) * out_stride, o);
       e0 = e1; e1 = e2; e2 = cur[k];
     }
@@ -74,11 +71,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv1d_kernel(
     Vec<T> cur = ld16(ub + (int64_t)t * u_stride);
     Vec<T> o;
 #pragma unroll
-    for (int i = 0; i < VE; ++i) {
-      float v = bs[i] + wt[i][0] * e0.get(i) + wt[i][1] * e1.get(i) + wt[i][2] * e2.get(i) +
-                wt[i][3] * cur.get(i);
-      o.set(i, silu_fast(v));
-    }
+    for (int i = 0; i < VE; ++i)
+      o.set(i, conv4_silu(wt[i], bs[i], e0.get(i), e1.get(i), e2.get(i), cur.get(i)));
     st16(ob + (int64_t)t * out_stride, o);
     e0 = e1; e1 = e2; e2 = cur;
   }

@@ -95,6 +95,13 @@ __device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
+// One conv output: bias + w[0] u[t-3] + w[1] u[t-2] + w[2] u[t-1] + w[3] u[t] in one fixed
+// fma order, then SiLU. Every conv of the library (the conv call, the conv fused into the
+// prefill, the decode step) goes through it, so equal inputs give equal values in all three.
+__device__ __forceinline__ float conv4_silu(const f32x4& w, float bias, float e0, float e1, float e2,
+                                            float e3) {
+  return silu_fast(fmaf(w[3], e3, fmaf(w[2], e2, fmaf(w[1], e1, fmaf(w[0], e0, bias)))));
+}
 
 // ---------------------------------------------------------------- MFMA 32x32, K in steps of 16
 // An operand fragment holds, per lane, 8 values along K for one row (A) or one

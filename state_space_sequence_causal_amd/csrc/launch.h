@@ -24,6 +24,15 @@ struct PrefillArgs {
   int B, L, H, G;
 };
 hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream);
+// The conv fused into the prefill (bf16, chunk 64): x, Bm and Cm of `a` are the raw xBC
+// columns; w [Cc][4], bias [Cc] (or NULL) and the [B][3][Cc] history (or NULL; updated to
+// the last 3 raw tokens) cover all Cc xBC channels.
+struct ConvArgs {
+  const float* w; const float* bias;
+  void* state;
+  int Cc;
+};
+hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream);
 // Workspace bytes the prep/scan pair needs: per (sequence, group, chunk) the causal Gram
 // tiles in fp32 and B^T and C in MFMA operand order; per (sequence, head, chunk) dt and
 // its block prefix sums.

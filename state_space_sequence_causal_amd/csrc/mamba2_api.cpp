@@ -73,6 +73,9 @@ int check_stride(const char* name, const void* p, int64_t stride, int64_t width,
   return MAMBA2_OK;
 }
 
+// The prefill kernels form offsets inside a chunk's rows in 32 bits.
+constexpr int64_t kMaxStride = (int64_t)1 << 25;
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MAMBA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -150,6 +153,9 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
   if ((st = check_stride("Cm", Cm, c_stride, G * N, io))) return st;
   if ((st = check_stride("y", y, y_stride, H * P, io))) return st;
   if (z && (st = check_stride("z", z, z_stride, H * P, io))) return st;
+  if (x_stride > kMaxStride || b_stride > kMaxStride || c_stride > kMaxStride || y_stride > kMaxStride ||
+      (z && z_stride > kMaxStride))
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
   if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
     return fail(MAMBA2_ERR_ALIGN, "h0 / h_final must be 16-byte aligned");
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
@@ -180,6 +186,108 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
                     d->nheads, d->ngroups};
   return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, static_cast<hipStream_t>(stream)),
                     "ssd_prefill launch");
+}
+
+namespace {
+// The conv is fused into the prefill's kernels for bf16 io at chunk 64; other supported
+// settings run the conv into the tail of the workspace first.
+bool conv_fused(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && d->chunk == 64; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+size_t conv_prefill_ws(const mamba2_dims* d, size_t* scan_part) {
+  const size_t ws = m2::ssd_prefill_workspace(d->io_dtype == MAMBA2_BF16, d->chunk, d->batch,
+                                              d->seqlen, d->nheads, d->ngroups);
+  if (scan_part) *scan_part = ws;
+  if (conv_fused(d) || d->seqlen == 0) return ws;
+  const int64_t Cc = (int64_t)d->nheads * d->headdim + 2LL * d->ngroups * d->dstate;
+  return align256(ws) + (size_t)d->batch * d->seqlen * Cc * esize_of(d->io_dtype);
+}
+}  // namespace
+
+M2_EXPORT size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
+  if (check_dims(d, true) != MAMBA2_OK || !chunk_supported(d)) return 0;
+  return conv_prefill_ws(d, nullptr);
+}
+
+M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stride,
+                                      const float* conv_w, const float* conv_bias, void* conv_state,
+                                      const void* dt_raw, const float* dt_bias, const float* A,
+                                      const float* D, const void* z, int64_t z_stride,
+                                      const float* h0, float* h_final, void* y, int64_t y_stride,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  const int io = d->io_dtype, es = esize_of(io);
+  if (!chunk_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
+                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+  if (!dt_bias || !A || !conv_w) return fail(MAMBA2_ERR_NULL, "dt_bias, A and conv_w must not be NULL");
+  if (d->seqlen > 0 && (!xBC || !dt_raw || !y))
+    return fail(MAMBA2_ERR_NULL, "xBC, dt_raw and y must not be NULL when seqlen > 0");
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
+  const int64_t HP = H * P, Cc = HP + 2 * G * N, BL = (int64_t)d->batch * d->seqlen;
+  if (Cc > (int64_t)1 << 24) return fail(MAMBA2_ERR_SHAPE, "too many xBC channels");
+  if ((st = check_stride("xBC", xBC, xbc_stride, Cc, io))) return st;
+  if ((st = check_stride("y", y, y_stride, HP, io))) return st;
+  if (z && (st = check_stride("z", z, z_stride, HP, io))) return st;
+  if (xbc_stride > kMaxStride || y_stride > kMaxStride || (z && z_stride > kMaxStride))
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
+  if (!aligned16(conv_w)) return fail(MAMBA2_ERR_ALIGN, "conv_w is not 16-byte aligned");
+  if (conv_state && !aligned16(conv_state)) return fail(MAMBA2_ERR_ALIGN, "conv_state is not 16-byte aligned");
+  if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
+    return fail(MAMBA2_ERR_ALIGN, "h0 / h_final must be 16-byte aligned");
+  size_t ws_scan = 0;
+  const size_t ws_need = conv_prefill_ws(d, &ws_scan);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", ws_need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (ws_need > 0 && !aligned16(workspace))
+    return fail(MAMBA2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const int64_t state_elems = (int64_t)d->batch * H * N * P;
+  Range ry = span(y, BL, y_stride, HP, es), rcs = span(conv_state, 1, 0, (int64_t)d->batch * 3 * Cc, es);
+  Range rh0 = span(h0, 1, 0, state_elems, 4), rhf = span(h_final, 1, 0, state_elems, 4);
+  Range rws = span(workspace, 1, 0, (int64_t)ws_need, 1);
+  // inputs read only; the first three are the per-token ones
+  Range ins[] = {span(xBC, BL, xbc_stride, Cc, es), span(dt_raw, BL, H, H, es),
+                 span(z, BL, z_stride, HP, es),     span(conv_w, 1, 0, Cc * 4, 4),
+                 span(conv_bias, 1, 0, Cc, 4),      span(dt_bias, 1, 0, H, 4),
+                 span(A, 1, 0, H, 4),               span(D, 1, 0, H, 4)};
+  for (const Range& r : ins) {
+    if (overlap(ry, r)) return fail(MAMBA2_ERR_ALIAS, "y overlaps an input");
+    if (overlap(rcs, r)) return fail(MAMBA2_ERR_ALIAS, "conv_state overlaps an input");
+    if (overlap(rws, r)) return fail(MAMBA2_ERR_ALIAS, "workspace overlaps an input");
+  }
+  for (int i = 0; i < 3; ++i)
+    if (overlap(rhf, ins[i])) return fail(MAMBA2_ERR_ALIAS, "h_final overlaps an input");
+  const Range outs[] = {ry, rcs, rhf, rws};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(MAMBA2_ERR_ALIAS, "y, conv_state, h_final and workspace must not overlap");
+  for (const Range& r : {ry, rcs, rws})
+    if (overlap(r, rh0)) return fail(MAMBA2_ERR_ALIAS, "y, conv_state or workspace overlaps h0");
+  if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
+    return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* cx = static_cast<const char*>(xBC);
+  if (conv_fused(d) || d->seqlen == 0) {
+    m2::PrefillArgs a{xBC, xbc_stride, cx ? cx + HP * es : nullptr, xbc_stride,
+                      cx ? cx + (HP + G * N) * es : nullptr, xbc_stride, dt_raw, dt_bias, A, D,
+                      z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
+                      d->nheads, d->ngroups};
+    if (d->seqlen == 0)   // nothing to convolve; the history is unchanged, h_final gets h0
+      return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
+    m2::ConvArgs cv{conv_w, conv_bias, conv_state, (int)Cc};
+    return hip_status(m2::launch_ssd_prefill_conv(a, cv, s), "conv_ssd_prefill launch");
+  }
+  // the conv into the workspace's tail, then the prefill from there
+  char* tail = static_cast<char*>(workspace) + align256(ws_scan);
+  hipError_t e = m2::launch_conv1d(io == MAMBA2_BF16, xBC, xbc_stride, conv_w, conv_bias, conv_state,
+                                   tail, Cc, d->batch, d->seqlen, (int)Cc, s);
+  if (e != hipSuccess) return hip_status(e, "conv_ssd_prefill conv launch");
+  m2::PrefillArgs a{tail, Cc, tail + HP * es, Cc, tail + (HP + G * N) * es, Cc, dt_raw, dt_bias, A, D,
+                    z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
+                    d->nheads, d->ngroups};
+  return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
 }
 
 M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const float* w,

@@ -120,11 +120,13 @@ __device__ __forceinline__ Frag<T> ld_frag(const void* p) {
 }
 
 // ---------------------------------------------------------------------------- prep kernel
-template <typename T, int Q>
-__global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
+// With CONV, Bm and Cm are the raw xBC columns and the conv (with its 3-token history at the
+// sequence start) is applied while the chunk's rows are staged.
+template <typename T, int Q, bool CONV>
+__global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void ssd_prep_kernel(
     const T* __restrict__ Bm, int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
     const T* __restrict__ dt_raw, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    unsigned char* __restrict__ ws, int L, int H, int G, int nC) {
+    unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv) {
   using C = Cfg<T, Q>;
   constexpr int VE = C::VE;
   extern __shared__ __align__(16) unsigned char prep_smem[];
@@ -145,35 +147,111 @@ __global__ __launch_bounds__(PREP_THREADS) void ssd_prep_kernel(
   const int col = lane & 31, g2 = lane >> 5;
   const int nvalid = min(Q, L - t0);
 
-  // B and C rows of the chunk into LDS (zero past the end of the sequence)
-  for (int v = tid; v < Q * SN / VE; v += PREP_THREADS) {
-    int s = v / (SN / VE), cv = v % (SN / VE);
-    bool ok = s < nvalid;
-    st16(&sB[s][cv * VE], ok ? ld16(Bb + (int64_t)s * b_stride + cv * VE) : zero16<T>());
-    st16(&sC[s][cv * VE], ok ? ld16(Cb + (int64_t)s * c_stride + cv * VE) : zero16<T>());
+  // The B and C rows are requested first; the dt records are formed while they arrive, and
+  // then the rows go to LDS (zero past the end of the sequence).
+  constexpr int NR = CONV ? 11 : Q * SN / VE / PREP_THREADS;   // 16-byte row vectors per thread
+  constexpr bool HOLD = CONV;   // rows held in registers across the dt phase
+  Vec<T> rB[HOLD ? NR : 1], rC[CONV || !HOLD ? 1 : NR];
+  // CONV: a thread convolves one 16-byte vector of B (vectors 0..15) or C (16..31) over 8
+  // consecutive tokens s1 .. s1 + 7, from the 11 raw rows s1 - 3 .. s1 + 7 (chunk-relative;
+  // before the sequence start: the history, zeros without one; past the end: the last row,
+  // whose outputs are dropped)
+  const int vec = tid & 31, s1 = 8 * (tid >> 5);
+  const int n0 = (vec & 15) * VE;
+  [[maybe_unused]] const bool isC = vec >= 16;
+  [[maybe_unused]] const int ch = H * SP + (isC ? G * SN : 0) + g * SN + n0;   // xBC channel
+  if constexpr (CONV) {
+    static_assert(Q == 64 && SN / VE == 16 && PREP_THREADS == 256, "conv staging layout");
+    const T* src = (isC ? Cb : Bb) + n0;
+    const int64_t stride = isC ? c_stride : b_stride;
+    const T* hist = cv.state ? static_cast<const T*>(cv.state) + (int64_t)b * 3 * cv.Cc + ch : nullptr;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int s = min(s1 - 3 + k, nvalid - 1);
+      if (t0 + s < 0) rB[k] = hist ? ld16(hist + (int64_t)(t0 + s + 3) * cv.Cc) : zero16<T>();
+      else rB[k] = ld16(src + (int64_t)s * stride);
+    }
+  } else if constexpr (HOLD) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int v = tid + i * PREP_THREADS;
+      const int s = min(v / (SN / VE), nvalid - 1), e0 = v % (SN / VE) * VE;
+      rB[i] = ld16(Bb + (int64_t)s * b_stride + e0);
+      rC[i] = ld16(Cb + (int64_t)s * c_stride + e0);
+    }
+  } else {
+    for (int v = tid; v < Q * SN / VE; v += PREP_THREADS) {
+      const int s = v / (SN / VE), e0 = v % (SN / VE) * VE;
+      const bool ok = s < nvalid;
+      st16(&sB[s][e0], ok ? ld16(Bb + (int64_t)s * b_stride + e0) : zero16<T>());
+      st16(&sC[s][e0], ok ? ld16(Cb + (int64_t)s * c_stride + e0) : zero16<T>());
+    }
   }
-  // per head of the group: dt and the 32-token block prefix of dt*A*log2(e)
+  // per head of the group: dt and the 32-token block prefix of dt*A*log2(e); a wave takes
+  // items wave, wave + 4, ... and requests up to 8 of them at once
   {
-    const int hpg = H / G;
+    const int hpg = H / G, nitems = hpg * C::TPL;
     const size_t hrec0 = (size_t)b * H * nC;
     unsigned char* hbase = ws + (size_t)gridDim.x * C::REC_BYTES;
-    for (int item = wave; item < hpg * C::TPL; item += PREP_THREADS / 64) {
-      const int j = item / C::TPL, k = item % C::TPL;
-      const int h = g * hpg + j;
-      const int s = 64 * k + lane;
-      float dt = 0.f;
-      if (s < nvalid) dt = softplus_f(to_f(dt_raw[(row0 + s) * H + h]) + dt_bias[h]);
-      float run = dt * A[h] * kLog2e;
+    constexpr int DB = 8;
+    for (int i0 = wave; i0 < nitems; i0 += DB * (PREP_THREADS / 64)) {
+      float raw[DB];
 #pragma unroll
-      for (int d = 1; d < 32; d <<= 1) {
-        float o = __shfl_up(run, d, 32);
-        if ((lane & 31) >= d) run += o;
+      for (int u = 0; u < DB; ++u) {
+        const int item = i0 + u * (PREP_THREADS / 64);
+        const int j = item / C::TPL, s = 64 * (item % C::TPL) + lane;
+        raw[u] = item < nitems && s < nvalid ? to_f(dt_raw[(row0 + s) * H + g * hpg + j]) : 0.f;
       }
-      const float tot = __shfl(run, (lane & 32) + 31);   // the block's total
-      float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
-      hr[s] = dt;
-      hr[Q + s] = run;
-      hr[2 * Q + s] = exp2_hw(tot - run) * dt;   // decay from s to the end of its block, times dt
+#pragma unroll
+      for (int u = 0; u < DB; ++u) {
+        const int item = i0 + u * (PREP_THREADS / 64);
+        if (item >= nitems) break;
+        const int j = item / C::TPL, k = item % C::TPL;
+        const int h = g * hpg + j;
+        const int s = 64 * k + lane;
+        const float dt = s < nvalid ? softplus_f(raw[u] + dt_bias[h]) : 0.f;
+        float run = dt * A[h] * kLog2e;
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) {
+          float o = __shfl_up(run, d, 32);
+          if ((lane & 31) >= d) run += o;
+        }
+        const float tot = __shfl(run, (lane & 32) + 31);   // the block's total
+        float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
+        hr[s] = dt;
+        hr[Q + s] = run;
+        hr[2 * Q + s] = exp2_hw(tot - run) * dt;   // decay from s to the end of its block, times dt
+      }
+    }
+  }
+  if constexpr (CONV) {
+    f32x4 wv[VE];
+    float bs[VE];
+#pragma unroll
+    for (int i = 0; i < VE; ++i) {
+      wv[i] = *reinterpret_cast<const f32x4*>(cv.w + (int64_t)(ch + i) * 4);
+      bs[i] = cv.bias ? cv.bias[ch + i] : 0.f;
+    }
+    T (*dst)[C::LDN] = isC ? sC : sB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Vec<T> o = zero16<T>();
+      if (s1 + j < nvalid) {
+#pragma unroll
+        for (int i = 0; i < VE; ++i)
+          o.set(i, conv4_silu(wv[i], bs[i], rB[j].get(i), rB[j + 1].get(i), rB[j + 2].get(i),
+                              rB[j + 3].get(i)));
+      }
+      st16(&dst[s1 + j][n0], o);
+    }
+  } else if constexpr (HOLD) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int v = tid + i * PREP_THREADS;
+      const int s = v / (SN / VE), e0 = v % (SN / VE) * VE;
+      const bool ok = s < nvalid;
+      st16(&sB[s][e0], ok ? rB[i] : zero16<T>());
+      st16(&sC[s][e0], ok ? rC[i] : zero16<T>());
     }
   }
   __syncthreads();
@@ -1210,11 +1288,15 @@ struct Pipe64Smem {
   float sRec[3][3 * P64];                   // dt | pi | v, chunk c in slot c % 3
 };
 
+// With CONV, x is the raw xBC tensor (x_stride its row stride): the helper waves apply the
+// conv to the head's x channels as they stage them, and at the end write the new conv
+// history of those channels (and, in the first head of each group, of the group's B and C).
+template <bool CONV>
 __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
                        const bf16* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
                        bf16* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                       int L, int H, int G) {
+                       int L, int H, int G, ConvArgs cv) {
   using T = bf16;
   using C = Cfg<T, P64>;
   constexpr int Q = P64;
@@ -1398,6 +1480,18 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     const float Dh = D ? D[h] : 0.f;
     // thread: token pair (s0, s0 + 1) = 2 (htid / 16), columns p0 .. p0 + 3 = 4 (htid % 16)
     const int s0 = 2 * (htid >> 4), p0 = 4 * (htid & 15);
+    // conv of channels h SP + p0 .. + 3: taps, bias and the history of the sequence start
+    f32x4 cw[4];
+    float cb[4];
+    const T* hist = nullptr;
+    if constexpr (CONV) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cw[e] = *reinterpret_cast<const f32x4*>(cv.w + (int64_t)(h * SP + p0 + e) * 4);
+        cb[e] = cv.bias ? cv.bias[h * SP + p0 + e] : 0.f;
+      }
+      if (cv.state) hist = static_cast<const T*>(cv.state) + (int64_t)b * 3 * cv.Cc + h * SP + p0;
+    }
     // per-thread element offsets inside a chunk's rows fit 32 bits; chunk bases are uniform
     const uint32_t xs = (uint32_t)x_stride, zs = (uint32_t)z_stride, ys = (uint32_t)y_stride;
     // M^T tiles: helper waves 0, 1 build tile 0 (diagonal 0) in halves (k steps hm of 16
@@ -1413,7 +1507,9 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     auto helpers = [&](auto part_tag, auto rec_tag) {
       constexpr int PART = decltype(part_tag)::value;   // 2: a diagonal half, 4: an off quarter
       constexpr bool REC = decltype(rec_tag)::value;
-      Raw4<T> rX[2], rZ[2];
+      // x rows of the thread's tokens; with the conv, raw rows s0 - 3 .. s0 + 1
+      constexpr int NX = CONV ? 5 : 2;
+      Raw4<T> rX[NX], rZ[2];
       float rRec = 0.f;
       f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7 (4 hq .. 4 hq + 3)
       auto load_set = [&](int c) {       // x and z of this thread's tokens
@@ -1426,8 +1522,20 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const uint32_t s = (uint32_t)min(s0 + k, lim);
-          rX[k] = ld4(xc + (s * xs + p0));
+          if constexpr (!CONV) rX[k] = ld4(xc + (s * xs + p0));
           rZ[k] = ld4(zc + (s * zs + p0));
+        }
+        if constexpr (CONV) {
+          // raw rows s0 - 3 .. s0 + 1 of the chunk, addressed from a base 3 rows back; past the
+          // end the last row is read, and in the first chunk the rows before the sequence are
+          // read as row 0 and replaced when that chunk is staged
+          const T* xh = xc - 3 * x_stride;
+          const int lo = c == 0 ? 3 : 0;
+#pragma unroll
+          for (int k = 0; k < NX; ++k) {
+            const uint32_t s = (uint32_t)min(max(s0 + k, lo), lim + 3);
+            rX[k] = ld4(xh + (s * xs + p0));
+          }
         }
       };
       auto load_rec = [&](int c) {
@@ -1445,8 +1553,21 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           if (full || c * Q + s < L) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
         }
       };
-      // x^T, (w x)^T and z of chunk c (its set in registers) into buffers c & 1
-      auto stage = [&](int c) {
+      // the history rows before the sequence that this thread's first tokens read (zeros
+      // without a history); used only when chunk 0 is staged
+      Raw4<T> rH[3];
+      auto load_hist = [&]() {
+        if constexpr (CONV) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            rH[k].v = (bf16x4){};
+            if (hist && s0 + k < 3) rH[k] = ld4(hist + (s0 + k) * cv.Cc);
+          }
+        }
+      };
+      // x^T, (w x)^T and z of chunk c (its set in registers) into buffers c & 1; FIRST: chunk 0
+      auto stage = [&](int c, auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
         const int buf = c & 1;
         if (z) {
 #pragma unroll
@@ -1458,9 +1579,32 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         const float2 vs = *reinterpret_cast<const float2*>(&rec[2 * Q + s0]);
         const float wb = s0 < 32 ? exp2_hw(rec[Q + 63]) : 1.f;
         const float w0 = vs.x * wb, w1 = vs.y * wb;
+        T xv[2][4];
+        if constexpr (CONV) {
+          Raw4<T> r[NX];
+#pragma unroll
+          for (int k = 0; k < NX; ++k) r[k] = rX[k];
+          if constexpr (FIRST) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+              if (s0 - 3 + k < 0) r[k] = rH[k];   // rH[k] holds history row s0 + k
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              xv[k][e] = (T)conv4_silu(cw[e], cb[e], r[k].get(e), r[k + 1].get(e), r[k + 2].get(e),
+                                       r[k + 3].get(e));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[0][e] = rX[0].v[e];
+            xv[1][e] = rX[1].v[e];
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const T x0 = rX[0].v[e], x1 = rX[1].v[e];
+          const T x0 = xv[0][e], x1 = xv[1][e];
           const Split2 v = split2(to_f(x0) * w0, to_f(x1) * w1);
           const int p = p0 + e, sw = xs64(p, s0);
           st_pair(&S.sXt[buf][p][sw], x0, x1);
@@ -1524,6 +1668,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       // prologue: records 0 and 1 into LDS; then chunk 0 staged and its tiles built, chunk 1's
       // set in flight
       if (nC > 0) {
+        load_hist();
         load_set(0);
         load_rec(0);
         put_rec(0);
@@ -1534,7 +1679,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       }
       __syncthreads();
       if (nC > 0) {
-        stage(0);
+        stage(0, std::true_type{});
         load_set(min(1, nC - 1));
         build(0);
         fetch_gram(min(1, nC - 1));
@@ -1546,13 +1691,37 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         build(c + 1);
         fetch_gram(min(c + 2, nC - 1));
         if (c >= 1) flush_y(c - 1, true);   // chunk c - 1 < nC - 1 is full
-        stage(c + 1);
+        stage(c + 1, std::false_type{});
         put_rec(c + 2);
         load_set(min(c + 2, nC - 1));
         load_rec(min(c + 3, nC - 1));
         __syncthreads();
       }
       if (nC > 0) flush_y(nC - 1, false);   // y of the last chunk
+      if constexpr (CONV) {
+        // the new history: the last 3 raw inputs of (history, sequence). One thread per 4
+        // channels reads all 3 before writing any, so an in-place shift (L < 3) is safe; every
+        // read of the old history (the staging of chunk 0 here, the prep kernel for B and C)
+        // is complete by now.
+        const int hpg = H / G;
+        int ch = -1;
+        if (htid < 16) ch = h * SP + p0;   // the head's x channels
+        else if (htid < 80 && h % hpg == 0) {
+          const int q = htid - 16;         // the group's B (q < 32) and C channels
+          ch = H * SP + (q < 32 ? 0 : G * SN) + g * SN + 4 * (q & 31);
+        }
+        if (cv.state && ch >= 0) {
+          T* hs = static_cast<T*>(cv.state) + (int64_t)b * 3 * cv.Cc + ch;
+          Raw4<T> f[3];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const int t = L - 3 + j;
+            f[j] = ld4(t >= 0 ? x + (row0 + t) * x_stride + ch : hs + (t + 3) * cv.Cc);
+          }
+#pragma unroll
+          for (int j = 0; j < 3; ++j) *reinterpret_cast<bf16x4*>(hs + j * cv.Cc) = f[j].v;
+        }
+      }
     };
     using Half = std::integral_constant<int, 2>;
     using Quarter = std::integral_constant<int, 4>;
@@ -1572,40 +1741,76 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
   using C = Cfg<T, Q>;
   const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
   constexpr bool WIDE = Q > 128;
+  constexpr bool PIPE64 = Q == 64 && sizeof(T) == 2;
   using ScanFn = void (*)(const T*, int64_t, const float*, const T*, int64_t, const float*, float*, T*,
                           int64_t, const unsigned char*, int, int, int);
   size_t scan_lds;
-  ScanFn scan;
-  if constexpr (WIDE) {
-    scan_lds = sizeof(WideSmem<T, Q>);
-    scan = &ssd_scan_wide_kernel<T, Q>;
-  } else if constexpr (Q == 64 && sizeof(T) == 2) {
+  const void* scan_fn;
+  ScanFn scan = nullptr;
+  if constexpr (PIPE64) {
     scan_lds = sizeof(Pipe64Smem);
-    scan = &ssd_scan64_kernel;
+    scan_fn = reinterpret_cast<const void*>(&ssd_scan64_kernel<false>);
   } else {
-    scan_lds = sizeof(ScanSmem<T, Q>);
-    scan = &ssd_scan_kernel<T, Q>;
+    if constexpr (WIDE) {
+      scan_lds = sizeof(WideSmem<T, Q>);
+      scan = &ssd_scan_wide_kernel<T, Q>;
+    } else {
+      scan_lds = sizeof(ScanSmem<T, Q>);
+      scan = &ssd_scan_kernel<T, Q>;
+    }
+    scan_fn = reinterpret_cast<const void*>(scan);
   }
-  const void* scan_fn = reinterpret_cast<const void*>(scan);
   static bool configured = false;
   if (!configured) {
-    hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q>), prep_lds);
+    hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, false>), prep_lds);
     if (e == hipSuccess) e = set_lds(scan_fn, scan_lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int nC = (a.L + Q - 1) / Q;
   if (nC > 0) {
-    hipLaunchKernelGGL((ssd_prep_kernel<T, Q>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
+    hipLaunchKernelGGL((ssd_prep_kernel<T, Q, false>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
-                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC);
+                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{});
   }
-  constexpr int threads = (Q == 64 && sizeof(T) == 2) ? P64_THREADS : SCAN_THREADS;
-  hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(threads), scan_lds, stream,
-                     static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+  if constexpr (PIPE64) {
+    hipLaunchKernelGGL((ssd_scan64_kernel<false>), dim3(a.B * a.H), dim3(P64_THREADS), scan_lds, stream,
+                       static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                       a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{});
+  } else {
+    hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
+                       static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                       a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream) {
+  using T = bf16;
+  constexpr int Q = P64;
+  using C = Cfg<T, Q>;
+  const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, true>), prep_lds);
+    if (e == hipSuccess) e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<true>), sizeof(Pipe64Smem));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int nC = (a.L + Q - 1) / Q;
+  if (nC > 0) {
+    hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
+                       stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
+                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
+                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv);
+  }
+  hipLaunchKernelGGL((ssd_scan64_kernel<true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
+                     stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);
+                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv);
   return hipGetLastError();
 }
 

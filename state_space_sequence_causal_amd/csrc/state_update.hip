@@ -148,11 +148,7 @@ void state_update_kernel(
   // conv step on the owned channels; the cache shifts by one token
   if (conv_thread) {
 #pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const float acc = bv[i] + wv[i][0] * s0.get(i) + wv[i][1] * s1.get(i) + wv[i][2] * s2.get(i) +
-                        wv[i][3] * cur.get(i);
-      smem[lc + i] = silu_fast(acc);
-    }
+    for (int i = 0; i < CV; ++i) smem[lc + i] = conv4_silu(wv[i], bv[i], s0.get(i), s1.get(i), s2.get(i), cur.get(i));
     *reinterpret_cast<decltype(s1.v)*>(csb + c) = s1.v;
     *reinterpret_cast<decltype(s2.v)*>(csb + Cc + c) = s2.v;
     *reinterpret_cast<decltype(cur.v)*>(csb + 2 * Cc + c) = cur.v;
@@ -165,9 +161,7 @@ void state_update_kernel(
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
       const f32x4 wq = *reinterpret_cast<const f32x4*>(w + (int64_t)(c2 + i) * DEC_W);
-      const float acc = (bias ? bias[c2 + i] : 0.f) + wq[0] * a0.get(i) + wq[1] * a1.get(i) +
-                        wq[2] * a2.get(i) + wq[3] * a3.get(i);
-      smem[l2 + i] = silu_fast(acc);
+      smem[l2 + i] = conv4_silu(wq, bias ? bias[c2 + i] : 0.f, a0.get(i), a1.get(i), a2.get(i), a3.get(i));
     }
     *reinterpret_cast<decltype(a1.v)*>(csb + c2) = a1.v;
     *reinterpret_cast<decltype(a2.v)*>(csb + Cc + c2) = a2.v;

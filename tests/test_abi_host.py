@@ -26,6 +26,7 @@ def declared():
 def test_header_declares_the_calls():
     names = declared()
     for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm",
+              "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_workspace_bytes",
               "mamba2_ssd_prefill_workspace_bytes", "mamba2_last_error", "mamba2_abi_version"):
         assert n in names
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 2
+    assert m2.mamba2_abi_version() == 3
 
 
 def dims(**kw):
@@ -94,6 +95,7 @@ def test_prefill_rejects_dims(kw, code):
     (dict(bs=100), ESHAPE), (dict(ys=250), ESHAPE), (dict(h0=BASE + 16 * MB + 8), EALIGN),
     (dict(y=BASE + 4 * MB), EALIAS), (dict(y=BASE), EALIAS), (dict(hf=BASE + 12 * MB), EALIAS),
     (dict(y=BASE + 20 * MB), EALIAS), (dict(hf=BASE + 16 * MB + 4096), EALIAS),
+    (dict(xs=(1 << 25) + 4), ESHAPE), (dict(zs=(1 << 25) + 4), ESHAPE),
 ])
 def test_prefill_rejects_pointers(kw, code):
     assert prefill(dims(), **kw) == code, m2.mamba2_last_error()
@@ -175,3 +177,52 @@ def test_rmsnorm_rejects(kw, code):
 def test_rmsnorm_rejects_model_shape():
     assert rmsnorm(dims(nheads=6, ngroups=4)) == ESHAPE
     assert rmsnorm(dims(seqlen=0), g=None, out=None) == OK
+
+
+# ------------------------------------------------------------------ conv + prefill in one call
+def conv_prefill(d, **kw):
+    H, G = d.nheads, d.ngroups
+    cc = H * 64 + 2 * G * 128
+    a = dict(u=BASE, us=cc, w=BASE + 4 * MB, b=BASE + 5 * MB, cs=BASE + 6 * MB, dt=BASE + 8 * MB,
+             dtb=BASE + 9 * MB, A=BASE + 10 * MB, D=BASE + 11 * MB, z=BASE + 12 * MB, zs=H * 64,
+             h0=BASE + 16 * MB, hf=BASE + 20 * MB, y=BASE + 24 * MB, ys=H * 64, ws=BASE + 64 * MB,
+             wsb=1 << 30)
+    a.update(kw)
+    return m2.lib.mamba2_conv_ssd_prefill(ctypes.byref(d), a["u"], a["us"], a["w"], a["b"], a["cs"],
+                                          a["dt"], a["dtb"], a["A"], a["D"], a["z"], a["zs"], a["h0"],
+                                          a["hf"], a["y"], a["ys"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), ENULL), (dict(w=None), ENULL), (dict(dt=None), ENULL), (dict(y=None), ENULL),
+    (dict(dtb=None), ENULL), (dict(A=None), ENULL),
+    (dict(us=500), ESHAPE), (dict(us=1028), EALIGN), (dict(u=BASE + 8), EALIGN),
+    (dict(w=BASE + 4 * MB + 4), EALIGN), (dict(cs=BASE + 6 * MB + 8), EALIGN),
+    (dict(us=(1 << 25) + 8), ESHAPE), (dict(ys=250), ESHAPE),
+    (dict(y=BASE), EALIAS), (dict(y=BASE + 6 * MB), EALIAS), (dict(cs=BASE), EALIAS),
+    (dict(cs=BASE + 24 * MB), EALIAS), (dict(hf=BASE), EALIAS), (dict(cs=BASE + 16 * MB), EALIAS),
+    (dict(ws=BASE + 6 * MB), EALIAS), (dict(ws=None), 7), (dict(wsb=1000), 7),
+])
+def test_conv_prefill_rejects(kw, code):
+    d = dims(io=m2.MAMBA2_BF16)
+    assert conv_prefill(d, **kw) == code, m2.mamba2_last_error()
+
+
+def test_conv_prefill_rejects_dims():
+    assert conv_prefill(dims(chunk=128)) == EUNSUP
+    assert conv_prefill(dims(io=m2.MAMBA2_BF16, chunk=48)) == EUNSUP
+    assert conv_prefill(dims(nheads=6, ngroups=4)) == ESHAPE
+
+
+def test_conv_prefill_workspace_size():
+    """Fused (bf16, chunk 64): the prefill's workspace; otherwise that (rounded up to 256 bytes)
+    plus the conv output of all xBC channels."""
+    for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_BF16, 2, 256),
+                          (m2.MAMBA2_F32, 4, 64)):
+        d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
+        base = m2.mamba2_ssd_prefill_workspace_bytes(d)
+        want = base if (io == m2.MAMBA2_BF16 and chunk == 64) else \
+            -(-base // 256) * 256 + 3 * 1000 * (16 * 64 + 2 * 8 * 128) * es
+        assert m2.mamba2_conv_ssd_prefill_workspace_bytes(d) == want
+    assert m2.mamba2_conv_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
+    assert m2.lib.mamba2_conv_ssd_prefill_workspace_bytes(None) == 0
