@@ -265,10 +265,10 @@ def cpu_baseline(cfg, inp):
 def counter_kernels(chunk: int) -> dict:
     """traffic entry -> (mangled) kernel-name fragments summed per call, for the bf16 prefill
     at chunk length ``chunk``"""
-    scan = {64: ("ssd_scan64_kernelILb0E", "ssd_scan64_kernel<false>"),
+    scan = {64: ("ssd_scan64_kernelILb0E", "ssd_scan64_kernel<false>", "ssd_scan64_kernel#1"),
             256: "ssd_scan_wide_kernelIDF16bLi256E"}.get(chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
     return {"conv_ssd_prefill": ["ssd_prep_kernelIDF16bLi64ELb1E",
-                                 ("ssd_scan64_kernelILb1E", "ssd_scan64_kernel<true>")],
+                                 ("ssd_scan64_kernelILb1E", "ssd_scan64_kernel<true>", "ssd_scan64_kernel#0")],
             "ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}ELb0E", scan],
             "conv1d": ["conv1d_kernel"],
             "state_update": ["state_update_kernel"],
@@ -286,12 +286,24 @@ def _counter_means(path: str, counter: str):
             if row["Counter_Name"] != counter:
                 continue
             v = float(row["Counter_Value"])
-            a = acc.setdefault(row["Kernel_Name"], [0.0, 0])
+            a = acc.setdefault((row["Kernel_Name"], row["Kernel_Id"]), [0.0, 0, int(row["Dispatch_Id"])])
             a[0] += v
             a[1] += 1
+            a[2] = min(a[2], int(row["Dispatch_Id"]))
             if "elementwise_kernel" in row["Kernel_Name"]:
                 calib = max(calib, v)
-    return {k: v[0] / v[1] for k, v in acc.items()}, calib
+    # Template instantiations can share one (demangled, argument-less) name: such names get
+    # "#0", "#1", ... in the order of their first dispatch. In a bench run the one-call step
+    # runs first, so "ssd_scan64_kernel#0" is its scan and "#1" the two-call path's.
+    names = {}
+    for (name, kid), a in acc.items():
+        names.setdefault(name, []).append((a[2], kid))
+    out = {}
+    for (name, kid), a in acc.items():
+        ids = sorted(names[name])
+        key = name if len(ids) == 1 else f"{name}#{ids.index((a[2], kid))}"
+        out[key] = a[0] / a[1]
+    return out, calib
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, chunk: int) -> dict:
