@@ -220,6 +220,45 @@ def run_rmsnorm(args, torch, m2, si, cfg):
     return us, nbytes
 
 
+def run_varlen(args, torch, m2, si, cfg):
+    """The one-call prefill over a packed continuous batch at the 12B shape: 16 sequences of
+    seeded log-uniform lengths summing to the workload's 8192 tokens, half of them continuing
+    from their entries in a pool of 40 cached states (seeded inputs stand in for requests)."""
+    nseq, npool = 16, 40
+    lens = si.draw_lengths(cfg, nseq, 16, 2048, cfg.batch * cfg.seqlen)
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(int(v) for v in lens)),
+                      dtype=torch.int32, device="cuda")
+    slots = torch.from_numpy(si.draw_slots(cfg, nseq, npool)).cuda()
+    init = torch.from_numpy(si.draw_has_init(cfg, nseq)).cuda()
+    inp = si.draw_prefill(cfg)
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    u, z, dt = dev(inp["xbc"][0]), dev(inp["z"][0]), dev(inp["dt_raw"][0])
+    w, bias, dtb, A, D = (f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
+    cpool_np, spool_np = si.draw_pools(cfg, npool)
+    cpool, spool = dev(cpool_np), f32(spool_np)
+    y = torch.empty((u.shape[0], cfg.d_inner), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(
+        m2.make_dims(nseq, u.shape[0], cfg.nheads, cfg.ngroups, 64, m2.MAMBA2_BF16)), dtype=torch.uint8,
+        device="cuda")
+
+    def step():
+        m2.mamba2_conv_ssd_prefill_varlen(u, w, bias, cu, slots, init, cpool, spool, dt, dtb, A, D, z, y,
+                                          ngroups=cfg.ngroups, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    return us, [int(v) for v in lens]
+
+
 CALIB_BYTES = 1 << 30
 
 
@@ -387,6 +426,7 @@ def main():
         ["conv1d_kernel"] + counter_kernels(args.chunk)["ssd_prefill"]
     dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
     rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
+    vl_us, vl_lens = run_varlen(args, torch, m2, si, cfg)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -443,6 +483,10 @@ def main():
         "frac": rms_bytes / (rms_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": rms_bytes,
         "traffic": measured_traffic("group_rmsnorm"),
         "note": "block RMSNorm of the gated output over 8 groups of 1280 channels (not in the step)"}
+    out["kernels"]["conv_ssd_prefill_varlen"] = {
+        "us": vl_us, "tokens_per_s": tokens / (vl_us * 1e-6), "lengths": vl_lens,
+        "note": "continuous batch: 16 packed sequences of the 12B shape summing to 8192 tokens, "
+                "states in a pool of 40 entries, half continuing from their entry (not the step)"}
     if alt is not None:
         out["kernels"][f"conv_ssd_prefill_chunk{cfg.chunk}"] = {
             "us": alt[2][0], "tokens_per_s": tokens / (alt[2][0] * 1e-6),

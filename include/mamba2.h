@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 3
+#define MAMBA2_ABI_VERSION 4
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -177,6 +177,57 @@ int mamba2_conv_ssd_prefill(const mamba2_dims* dims, const void* xBC, int64_t xb
                             const float* D, const void* z, int64_t z_stride, const float* h0,
                             float* h_final, void* y, int64_t y_stride, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * mamba2_conv_ssd_prefill_varlen_workspace_bytes -- device workspace of
+ * mamba2_conv_ssd_prefill_varlen for `dims` (batch = number of sequences, seqlen =
+ * total packed rows; bf16 io, chunk 64), 0 if `dims` is invalid or another setting:
+ *   M * (ngroups * R + nheads * 768) + 8 * (batch + 1),   M = seqlen / 64 + batch
+ * with R the per-(group, chunk) record of mamba2_ssd_prefill_workspace_bytes at chunk 64
+ * (4096 * 3 + 2 * 128 * 64 * 2 bytes).
+ */
+size_t mamba2_conv_ssd_prefill_varlen_workspace_bytes(const mamba2_dims* dims);
+
+/*
+ * mamba2_conv_ssd_prefill_varlen -- mamba2_conv_ssd_prefill over a packed batch of
+ * sequences of different lengths whose states live in slot pools, as an inference engine
+ * with continuous batching keeps them (the deployment of the hyper.ai / neurohive pages
+ * serves the model through such an engine with an fp32 Mamba cache: neurohive, section
+ * "Развертывание"). dims->batch is the number of sequences S, dims->seqlen the number of
+ * packed rows; only bf16 io at chunk 64 is supported (MAMBA2_ERR_UNSUPPORTED otherwise).
+ *
+ *   xBC        [seqlen][Cc] io raw rows, row stride xbc_stride; sequence i is rows
+ *              cu_seqlens[i] .. cu_seqlens[i+1]
+ *   conv_w, conv_bias  as in mamba2_conv1d
+ *   cu_seqlens [S+1] int32 (device): 0 = cu[0] <= cu[1] <= ... <= cu[S] <= seqlen.
+ *              Offsets that break this are clamped into it (negative to 0, above seqlen
+ *              to seqlen, decreasing to the previous one) so that no access leaves
+ *              the packed rows; results are then those of the clamped offsets.
+ *   slots      [S] int32 (device) or NULL (= 0, 1, ..., S-1): the pool entry of each
+ *              sequence. An entry outside [0, npool) means "no entry": the sequence
+ *              starts from zeros and its final state and history are not stored.
+ *              Two sequences must not share an entry (their writes would race).
+ *   has_init   [S] int32 (device) or NULL (= all 0): nonzero when the sequence
+ *              continues from the state and conv history in its entry; zero when it
+ *              starts from a zero state and a zero history
+ *   conv_pool  [npool][3][Cc] io, ssm_pool [npool][H][N][P] f32: the caches. Each
+ *              sequence with an entry leaves there its last 3 raw xBC rows (history
+ *              included, as mamba2_conv1d) and its final state. May be NULL if npool == 0.
+ *   dt_raw     [seqlen][H] io dense; dt_bias, A, D as in mamba2_ssd_prefill
+ *   z, y       [seqlen][H*P] io with row strides (z may be NULL)
+ *   workspace, workspace_bytes: at least mamba2_conv_ssd_prefill_varlen_workspace_bytes
+ * Each sequence's y, final state and history are bitwise those of mamba2_conv_ssd_prefill
+ * on that sequence alone (batch 1) started from the same state and history. y, the pools
+ * and the workspace must not overlap each other or any input.
+ */
+int mamba2_conv_ssd_prefill_varlen(const mamba2_dims* dims, const void* xBC, int64_t xbc_stride,
+                                   const float* conv_w, const float* conv_bias,
+                                   const int32_t* cu_seqlens, const int32_t* slots,
+                                   const int32_t* has_init, void* conv_pool, float* ssm_pool,
+                                   int32_t npool, const void* dt_raw, const float* dt_bias,
+                                   const float* A, const float* D, const void* z, int64_t z_stride,
+                                   void* y, int64_t y_stride, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * mamba2_state_update -- one decode token per sequence (dims->seqlen must be

@@ -167,3 +167,59 @@ def split_xbc(xbc, nheads: int, ngroups: int, headdim: int = 64, dstate: int = 1
     """Views of the x, B and C channel ranges of an xBC tensor [..][Cc]."""
     di, gn = nheads * headdim, ngroups * dstate
     return xbc[..., :di], xbc[..., di:di + gn], xbc[..., di + gn:di + 2 * gn]
+
+
+def round_bf16(a):
+    """Each value stored as bfloat16: rounded to float32, then to 8 significand bits by
+    round-to-nearest-even on its bit pattern (finite inputs)."""
+    u = np.ascontiguousarray(np.asarray(a, dtype=np.float32)).view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def conv_ssd_prefill_varlen(xbc, cu_seqlens, slots, has_init, conv_pool, ssm_pool, conv_w, conv_b,
+                            dt_raw, dt_bias, A, D=None, z=None, *, nheads: int, ngroups: int,
+                            io: str = "f32"):
+    """The serving form of the prefill: packed sequences of different lengths whose states
+    live in slot pools. Sequence i is rows cu_seqlens[i] .. cu_seqlens[i+1] of xbc, dt_raw
+    and z; it starts from the history conv_pool[slots[i]] and the state ssm_pool[slots[i]]
+    when has_init[i] is nonzero (else from zeros), runs conv1d and then ssd_scan on its own
+    rows, and, when 0 <= slots[i] < npool, leaves its last three raw rows (history first)
+    and its final state in that entry. slots None means entry i; has_init None means all
+    zero. With io "bf16" the conv output is stored as bf16 before the scan reads it, as the
+    library stores it in that io type. This is conv1d and ssd_scan applied one sequence at a
+    time.
+
+    Returns (y [T][H*P], conv_pool', ssm_pool') with new pool arrays."""
+    xbc = _d(xbc)
+    dt_raw = _d(dt_raw)
+    z = None if z is None else _d(z)
+    cu = [int(v) for v in np.asarray(cu_seqlens)]
+    S = len(cu) - 1
+    conv_pool = np.array(_d(conv_pool), copy=True) if conv_pool is not None else None
+    ssm_pool = np.array(_d(ssm_pool), copy=True) if ssm_pool is not None else None
+    npool = 0 if ssm_pool is None else ssm_pool.shape[0]
+    Cc = xbc.shape[-1]
+    N, P = 128, 64
+    y = np.zeros((xbc.shape[0], nheads * P))
+    for i in range(S):
+        a, b = cu[i], cu[i + 1]
+        s = i if slots is None else int(slots[i])
+        has_slot = 0 <= s < npool
+        init = has_slot and has_init is not None and int(has_init[i]) != 0
+        hist = conv_pool[s][None] if init else np.zeros((1, 3, Cc))
+        h0 = ssm_pool[s][None] if init else np.zeros((1, nheads, N, P))
+        if b > a:
+            xr, hist_new = conv1d(xbc[None, a:b], conv_w, conv_b, hist)
+            if io == "bf16":
+                xr = round_bf16(xr)
+            x, Bm, Cm = split_xbc(xr, nheads, ngroups)
+            yi, hf = ssd_scan(x, Bm, Cm, dt_raw[None, a:b], dt_bias, A, D,
+                              None if z is None else z[None, a:b], h0, ngroups=ngroups)
+            y[a:b] = yi[0]
+        else:   # an empty sequence keeps its history and state
+            hist_new, hf = hist, h0
+        if has_slot:
+            conv_pool[s] = hist_new[0]
+            ssm_pool[s] = hf[0]
+    return y, conv_pool, ssm_pool

@@ -37,6 +37,7 @@ TOKEN_BLOCK = 256  # tokens per independently seeded block
 # tensor ids (part of the stream key; never renumber)
 _T_ALOG, _T_DTB, _T_D, _T_CW, _T_CB, _T_XBC, _T_Z, _T_DT, _T_H0, _T_CS = range(10)
 _T_GATED, _T_NW = 10, 11
+_T_LEN, _T_SLOT, _T_INIT = 12, 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -301,3 +302,38 @@ def draw_gated(cfg: Config, t0: int = 0, t1: Optional[int] = None) -> np.ndarray
 def draw_norm_weight(cfg: Config) -> np.ndarray:
     """Per-channel RMSNorm weight [d_inner] ~ U(0.5, 1.5), fp32."""
     return _rng(cfg.seed, _T_NW).uniform(0.5, 1.5, cfg.d_inner).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- packed batches
+def draw_lengths(cfg: Config, nseq: int, lo: int, hi: int, total: Optional[int] = None) -> np.ndarray:
+    """Sequence lengths for a packed (continuous-batching) prefill: log-uniform in [lo, hi],
+    int. With ``total`` the lengths are rescaled (largest remainders) to sum exactly to it."""
+    r = _rng(cfg.seed, _T_LEN, nseq)
+    lens = np.floor(np.exp(r.uniform(np.log(lo), np.log(hi + 1), nseq))).astype(np.int64)
+    lens = np.clip(lens, lo, hi)
+    if total is not None:
+        w = lens / lens.sum() * total
+        base = np.floor(w).astype(np.int64)
+        rest = total - int(base.sum())
+        order = np.argsort(-(w - base), kind="stable")
+        base[order[:rest]] += 1
+        lens = base
+    return lens.astype(np.int32)
+
+
+def draw_slots(cfg: Config, nseq: int, npool: int) -> np.ndarray:
+    """Distinct pool entries for nseq sequences: a seeded random choice out of npool."""
+    return _rng(cfg.seed, _T_SLOT, nseq, npool).permutation(npool)[:nseq].astype(np.int32)
+
+
+def draw_has_init(cfg: Config, nseq: int, p: float = 0.5) -> np.ndarray:
+    """Per-sequence flags (int32 0/1): 1 with probability p (the sequence continues from its
+    cached state), else 0 (a new request)."""
+    return (_rng(cfg.seed, _T_INIT, nseq).uniform(0, 1, nseq) < p).astype(np.int32)
+
+
+def draw_pools(cfg: Config, npool: int) -> tuple:
+    """Cache pools for npool entries: conv history [npool][3][Cc] drawn like xBC rows (io
+    precision) and fp32 states [npool][H][N][P] ~ N(0, 0.1^2)."""
+    c = dataclasses.replace(cfg, batch=npool, h0_std=cfg.h0_std or 0.1)
+    return draw_conv_state(c), draw_h0(c)

@@ -19,7 +19,8 @@ __all__ = [
     "LIB_PATH", "Mamba2Error", "Dims", "lib", "io_dtype_of",
     "mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update",
     "mamba2_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill",
-    "mamba2_conv_ssd_prefill_workspace_bytes", "mamba2_group_rmsnorm",
+    "mamba2_conv_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill_varlen",
+    "mamba2_conv_ssd_prefill_varlen_workspace_bytes", "mamba2_group_rmsnorm",
     "mamba2_abi_version", "mamba2_last_error",
     "MAMBA2_F32", "MAMBA2_BF16", "STATUS",
 ]
@@ -66,10 +67,14 @@ lib.mamba2_conv_ssd_prefill_workspace_bytes.argtypes = [_dims]
 lib.mamba2_conv_ssd_prefill_workspace_bytes.restype = _sz
 lib.mamba2_conv_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
+lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes.argtypes = [_dims]
+lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes.restype = _sz
+lib.mamba2_conv_ssd_prefill_varlen.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                               _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.mamba2_group_rmsnorm.argtypes = [_dims, _vp, _i64, _vp, ctypes.c_float, _vp, _i64, _vp]
-for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_conv_ssd_prefill", "mamba2_state_update",
-           "mamba2_group_rmsnorm"):
+for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_varlen",
+           "mamba2_state_update", "mamba2_group_rmsnorm"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -167,6 +172,38 @@ def mamba2_conv_ssd_prefill(xBC, conv_w, conv_bias, conv_state, dt_raw, dt_bias,
         ctypes.byref(d), _ptr(xBC), _row_stride(xBC), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
         _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z), 0 if z is None else _row_stride(z),
         _ptr(h0), _ptr(h_final), _ptr(y), _row_stride(y), _ptr(workspace), ws_bytes, _stream()))
+
+
+def mamba2_conv_ssd_prefill_varlen_workspace_bytes(d: Dims) -> int:
+    return lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes(ctypes.byref(d))
+
+
+def mamba2_conv_ssd_prefill_varlen(xBC, conv_w, conv_bias, cu_seqlens, slots, has_init, conv_pool,
+                                   ssm_pool, dt_raw, dt_bias, A, D, z, y, *, ngroups: int,
+                                   workspace=None) -> None:
+    """The one-call prefill over packed sequences (xBC [T, Cc] rows, cu_seqlens int32 [S+1]),
+    states in slot pools (conv_pool [npool, 3, Cc], ssm_pool [npool, H, N, P]); slots and
+    has_init are int32 [S] or None. bf16 io, chunk 64."""
+    T, H = dt_raw.shape
+    S = cu_seqlens.numel() - 1
+    npool = 0 if ssm_pool is None else ssm_pool.shape[0]
+    d = make_dims(S, T, H, ngroups, 64, io_dtype_of(xBC))
+    if workspace is None:
+        import torch
+        workspace = torch.empty(lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes(ctypes.byref(d)),
+                                dtype=torch.uint8, device=dt_raw.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    def rs(t):
+        if t.numel() == 0:
+            return t.shape[-1]
+        if t.stride(-1) != 1:
+            raise Mamba2Error(2, "the last dimension must be contiguous")
+        return t.stride(0)
+    _check(lib.mamba2_conv_ssd_prefill_varlen(
+        ctypes.byref(d), _ptr(xBC), rs(xBC), _ptr(conv_w), _ptr(conv_bias), _ptr(cu_seqlens), _ptr(slots),
+        _ptr(has_init), _ptr(conv_pool), _ptr(ssm_pool), npool, _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D),
+        _ptr(z), 0 if z is None else rs(z), _ptr(y), rs(y), _ptr(workspace), ws_bytes, _stream()))
 
 
 def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,

@@ -33,6 +33,22 @@ struct ConvArgs {
   int Cc;
 };
 hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream);
+// Packed variable-length sequences with states in slot pools (bf16, chunk 64, conv fused):
+// sequence i covers packed rows cu[i] .. cu[i+1] of x / Bm / Cm / dt_raw / z / y (a.L is
+// the total row count, a.B the sequence count); it starts from ssm_pool / conv_pool entry
+// slots[i] when has_init[i] != 0 (else from zeros) and leaves its final state and conv
+// history there when 0 <= slots[i] < npool. slots NULL: sequence i uses entry i; has_init
+// NULL: every sequence starts from zeros.
+struct VarlenArgs {
+  const int32_t* cu; const int32_t* slots; const int32_t* has_init;
+  float* ssm_pool; void* conv_pool;
+  int nseq, npool;
+};
+hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, const VarlenArgs& va,
+                                     hipStream_t stream);
+// Workspace of the variable-length prefill: the records of ssd_prefill_workspace for up to
+// seqlen / 64 + nseq chunks, then the sanitized offsets and the per-sequence chunk offsets.
+size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G);
 // Workspace bytes the prep/scan pair needs: per (sequence, group, chunk) the causal Gram
 // tiles in fp32 and B^T and C in MFMA operand order; per (sequence, head, chunk) dt and
 // its block prefix sums.

@@ -290,6 +290,80 @@ M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int
   return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
 }
 
+namespace {
+bool varlen_supported(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && d->chunk == 64; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+}  // namespace
+
+M2_EXPORT size_t mamba2_conv_ssd_prefill_varlen_workspace_bytes(const mamba2_dims* d) {
+  if (check_dims(d, true) != MAMBA2_OK || !varlen_supported(d)) return 0;
+  return m2::ssd_prefill_varlen_workspace(d->seqlen, d->batch, d->nheads, d->ngroups);
+}
+
+M2_EXPORT int mamba2_conv_ssd_prefill_varlen(
+    const mamba2_dims* d, const void* xBC, int64_t xbc_stride, const float* conv_w, const float* conv_bias,
+    const int32_t* cu_seqlens, const int32_t* slots, const int32_t* has_init, void* conv_pool,
+    float* ssm_pool, int32_t npool, const void* dt_raw, const float* dt_bias, const float* A,
+    const float* D, const void* z, int64_t z_stride, void* y, int64_t y_stride, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  const int io = d->io_dtype, es = esize_of(io);
+  if (!varlen_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED, "the packed prefill runs with bf16 io at chunk 64 (got chunk %d, %s)",
+                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+  if (!cu_seqlens || !dt_bias || !A || !conv_w)
+    return fail(MAMBA2_ERR_NULL, "cu_seqlens, dt_bias, A and conv_w must not be NULL");
+  if (d->seqlen > 0 && (!xBC || !dt_raw || !y))
+    return fail(MAMBA2_ERR_NULL, "xBC, dt_raw and y must not be NULL when seqlen > 0");
+  if (npool < 0) return fail(MAMBA2_ERR_SHAPE, "npool %d < 0", npool);
+  if (npool > 0 && (!conv_pool || !ssm_pool))
+    return fail(MAMBA2_ERR_NULL, "conv_pool and ssm_pool must not be NULL when npool > 0");
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
+  const int64_t HP = H * P, Cc = HP + 2 * G * N, T = d->seqlen, S = d->batch;
+  if (Cc > (int64_t)1 << 24) return fail(MAMBA2_ERR_SHAPE, "too many xBC channels");
+  if ((int64_t)G * (T / 64 + S) > ((int64_t)1 << 31) - 1 || S * H > ((int64_t)1 << 31) - 1)
+    return fail(MAMBA2_ERR_SHAPE, "packed batch too large");
+  if ((st = check_stride("xBC", xBC, xbc_stride, Cc, io))) return st;
+  if ((st = check_stride("y", y, y_stride, HP, io))) return st;
+  if (z && (st = check_stride("z", z, z_stride, HP, io))) return st;
+  if (xbc_stride > kMaxStride || y_stride > kMaxStride || (z && z_stride > kMaxStride))
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
+  if (!aligned16(conv_w) || !aligned16(conv_pool) || !aligned16(ssm_pool))
+    return fail(MAMBA2_ERR_ALIGN, "conv_w, conv_pool and ssm_pool must be 16-byte aligned");
+  if (!aligned4(cu_seqlens) || !aligned4(slots) || !aligned4(has_init))
+    return fail(MAMBA2_ERR_ALIGN, "cu_seqlens, slots and has_init must be 4-byte aligned");
+  const size_t ws_need = m2::ssd_prefill_varlen_workspace((int)T, (int)S, (int)H, (int)G);
+  if (!workspace || workspace_bytes < ws_need)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", ws_need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned16(workspace)) return fail(MAMBA2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Range ry = span(y, T, y_stride, HP, es), rws = span(workspace, 1, 0, (int64_t)ws_need, 1);
+  Range rcp = span(conv_pool, 1, 0, (int64_t)npool * 3 * Cc, es);
+  Range rsp = span(ssm_pool, 1, 0, (int64_t)npool * H * N * P, 4);
+  Range ins[] = {span(xBC, T, xbc_stride, Cc, es), span(dt_raw, T, H, H, es), span(z, T, z_stride, HP, es),
+                 span(conv_w, 1, 0, Cc * 4, 4),        span(conv_bias, 1, 0, Cc, 4),
+                 span(dt_bias, 1, 0, H, 4),            span(A, 1, 0, H, 4),
+                 span(D, 1, 0, H, 4),                  span(cu_seqlens, 1, 0, S + 1, 4),
+                 span(slots, 1, 0, S, 4),              span(has_init, 1, 0, S, 4)};
+  const Range outs[] = {ry, rcp, rsp, rws};
+  for (const Range& o : outs)
+    for (const Range& r : ins)
+      if (overlap(o, r)) return fail(MAMBA2_ERR_ALIAS, "y, the pools and the workspace must not overlap an input");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(MAMBA2_ERR_ALIAS, "y, the pools and the workspace must not overlap");
+  const char* cx = static_cast<const char*>(xBC);
+  m2::PrefillArgs a{xBC, xbc_stride, cx ? cx + HP * es : nullptr, xbc_stride,
+                    cx ? cx + (HP + G * N) * es : nullptr, xbc_stride, dt_raw, dt_bias, A, D,
+                    z, z_stride, nullptr, nullptr, y, y_stride, workspace, d->batch, d->seqlen,
+                    d->nheads, d->ngroups};
+  const m2::ConvArgs cv{conv_w, conv_bias, nullptr, (int)Cc};
+  const m2::VarlenArgs va{cu_seqlens, slots, has_init, ssm_pool, conv_pool, d->batch, npool};
+  return hip_status(m2::launch_ssd_prefill_varlen(a, cv, va, static_cast<hipStream_t>(stream)),
+                    "conv_ssd_prefill_varlen launch");
+}
+
 M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const float* w,
                                   const float* bias, void* conv_state, const void* dt_raw_t,
                                   const float* dt_bias, const float* A, const float* D,

@@ -119,14 +119,79 @@ __device__ __forceinline__ Frag<T> ld_frag(const void* p) {
   return f;
 }
 
+// Device view of a packed variable-length batch: sanitized row offsets cu[nseq + 1] and the
+// first global chunk of each sequence cc[nseq + 1] (both in the workspace), the slot map
+// and the initial-state flags, the pools, and the chunk capacity of the workspace records.
+struct VarlenDev {
+  const int32_t* cu; const int32_t* cc;
+  const int32_t* slots; const int32_t* has_init;
+  float* ssm_pool; bf16* conv_pool;
+  int nseq, npool, maxC;
+  // pool entry of sequence i, or -1 when it has none (slot out of range)
+  __device__ __forceinline__ int slot(int i) const {
+    const int s = slots ? slots[i] : i;
+    return s >= 0 && s < npool ? s : -1;
+  }
+  __device__ __forceinline__ bool init(int i) const { return has_init && has_init[i] != 0; }
+};
+
+// Offsets of a packed batch, made safe to index with: cu'[i] = min(max(0, cu[0..i]), total),
+// so every sequence lies inside the packed rows whatever the caller passed, and the first
+// global chunk of each sequence, cc[i] = sum over j < i of ceil((cu'[j+1] - cu'[j]) / 64).
+// One workgroup; thread t takes a contiguous run of the nseq + 1 entries.
+constexpr int VIDX_THREADS = 1024;
+__global__ __launch_bounds__(VIDX_THREADS) void varlen_index_kernel(const int32_t* __restrict__ cu_in, int nseq,
+                                                                    int total, int32_t* __restrict__ cu_out,
+                                                                    int32_t* __restrict__ cc_out) {
+  __shared__ int part[VIDX_THREADS];
+  const int t = threadIdx.x, n = nseq + 1;
+  const int per = (n + VIDX_THREADS - 1) / VIDX_THREADS;
+  const int j0 = min(n, t * per), j1 = min(n, j0 + per);
+  // running maximum of the clamped offsets
+  int m = 0;
+  for (int j = j0; j < j1; ++j) m = max(m, min(max(cu_in[j], 0), total));
+  part[t] = m;
+  __syncthreads();
+  for (int d = 1; d < VIDX_THREADS; d <<= 1) {   // inclusive max scan
+    const int o = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] = max(part[t], o);
+    __syncthreads();
+  }
+  m = t > 0 ? part[t - 1] : 0;
+  for (int j = j0; j < j1; ++j) {
+    m = max(m, min(max(cu_in[j], 0), total));
+    cu_out[j] = m;
+  }
+  __syncthreads();
+  // chunk counts and their exclusive sum
+  int sum = 0;
+  for (int j = j0; j < min(j1, nseq); ++j) sum += (cu_out[j + 1] - cu_out[j] + 63) / 64;
+  part[t] = sum;
+  __syncthreads();
+  for (int d = 1; d < VIDX_THREADS; d <<= 1) {   // inclusive sum scan
+    const int o = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += o;
+    __syncthreads();
+  }
+  int run = t > 0 ? part[t - 1] : 0;
+  for (int j = j0; j < j1; ++j) {
+    cc_out[j] = run;
+    if (j < nseq) run += (cu_out[j + 1] - cu_out[j] + 63) / 64;
+  }
+}
+
 // ---------------------------------------------------------------------------- prep kernel
 // With CONV, Bm and Cm are the raw xBC columns and the conv (with its 3-token history at the
-// sequence start) is applied while the chunk's rows are staged.
-template <typename T, int Q, bool CONV>
+// sequence start) is applied while the chunk's rows are staged. With VARLEN (CONV only) the
+// grid is (group, global chunk) over a packed batch; records are laid out [group][chunk].
+template <typename T, int Q, bool CONV, bool VARLEN = false>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void ssd_prep_kernel(
     const T* __restrict__ Bm, int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
     const T* __restrict__ dt_raw, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv) {
+    unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv, VarlenDev vd) {
+  static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
   using C = Cfg<T, Q>;
   constexpr int VE = C::VE;
   extern __shared__ __align__(16) unsigned char prep_smem[];
@@ -134,9 +199,37 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
   T (*sC)[C::LDN] = reinterpret_cast<T (*)[C::LDN]>(prep_smem + sizeof(T) * Q * C::LDN);
 
   const int rec = blockIdx.x;
-  const int c = rec % nC, bg = rec / nC, g = bg % G, b = bg / G;
-  const int t0 = c * Q;
-  const int64_t row0 = (int64_t)b * L + t0;
+  // c: the chunk's record index; t0: its first token inside its sequence
+  int c, g, b, t0, len;
+  int64_t row0;
+  const T* hist0 = nullptr;   // conv history of the chunk's sequence, or none
+  if constexpr (VARLEN) {
+    g = rec / vd.maxC;
+    c = rec % vd.maxC;
+    b = 0;
+    if (c >= vd.cc[vd.nseq]) return;   // past the batch's chunks: the whole workgroup leaves
+    int lo = 0, hi = vd.nseq - 1;        // the sequence: the last i with cc[i] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (vd.cc[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    t0 = (c - vd.cc[lo]) * Q;
+    len = vd.cu[lo + 1] - vd.cu[lo];
+    row0 = vd.cu[lo] + t0;
+    const int sl = vd.slot(lo);
+    if (sl >= 0 && vd.init(lo)) hist0 = reinterpret_cast<const T*>(vd.conv_pool) + (int64_t)sl * 3 * cv.Cc;
+    nC = vd.maxC;
+  } else {
+    c = rec % nC;
+    const int bg = rec / nC;
+    g = bg % G;
+    b = bg / G;
+    t0 = c * Q;
+    len = L;
+    row0 = (int64_t)b * L + t0;
+    if (CONV && cv.state) hist0 = static_cast<const T*>(cv.state) + (int64_t)b * 3 * cv.Cc;
+  }
   const T* Bb = Bm + row0 * b_stride + g * SN;
   const T* Cb = Cm + row0 * c_stride + g * SN;
   unsigned char* recp = ws + (size_t)rec * C::REC_BYTES;
@@ -145,7 +238,7 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
   unsigned char* cff = btf + C::BT_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g2 = lane >> 5;
-  const int nvalid = min(Q, L - t0);
+  const int nvalid = min(Q, len - t0);
 
   // The B and C rows are requested first; the dt records are formed while they arrive, and
   // then the rows go to LDS (zero past the end of the sequence).
@@ -164,7 +257,7 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
     static_assert(Q == 64 && SN / VE == 16 && PREP_THREADS == 256, "conv staging layout");
     const T* src = (isC ? Cb : Bb) + n0;
     const int64_t stride = isC ? c_stride : b_stride;
-    const T* hist = cv.state ? static_cast<const T*>(cv.state) + (int64_t)b * 3 * cv.Cc + ch : nullptr;
+    const T* hist = hist0 ? hist0 + ch : nullptr;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int s = min(s1 - 3 + k, nvalid - 1);
@@ -1291,12 +1384,15 @@ struct Pipe64Smem {
 // With CONV, x is the raw xBC tensor (x_stride its row stride): the helper waves apply the
 // conv to the head's x channels as they stage them, and at the end write the new conv
 // history of those channels (and, in the first head of each group, of the group's B and C).
-template <bool CONV>
+// With VARLEN (CONV only) workgroup (i, h) runs sequence i of a packed batch: its rows, its
+// workspace records, and its state and conv history in the slot pools.
+template <bool CONV, bool VARLEN = false>
 __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
                        const bf16* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
                        bf16* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                       int L, int H, int G, ConvArgs cv) {
+                       int Lrows, int H, int G, ConvArgs cv, VarlenDev vd) {
+  static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
   using T = bf16;
   using C = Cfg<T, P64>;
   constexpr int Q = P64;
@@ -1306,16 +1402,50 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   const int id = xcd_local_order(blockIdx.x, gridDim.x);
   const int b = id / H, h = id % H;
   const int g = h / (H / G);
-  const int nC = (L + Q - 1) / Q;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g2 = lane >> 5;
 
-  const int64_t row0 = (int64_t)b * L;
-  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
-  const float* hrec = reinterpret_cast<const float*>(
-      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
-      ((size_t)b * H + h) * nC * C::HREC_BYTES);
+  // the workgroup's sequence: its L rows from row0, its records, its initial and final state
+  // (h0b / hfb: the head's N x P block, or none) and its conv history (read / written)
+  int L;
+  int64_t row0;
+  const unsigned char* wsg;
+  const float* hrec;
+  const float* h0b;
+  float* hfb;
+  const T* hist_rd = nullptr;
+  T* hist_wr = nullptr;
+  if constexpr (VARLEN) {
+    row0 = vd.cu[b];
+    L = vd.cu[b + 1] - vd.cu[b];
+    const int cc0 = vd.cc[b];
+    wsg = ws + ((size_t)g * vd.maxC + cc0) * C::REC_BYTES;
+    hrec = reinterpret_cast<const float*>(ws + (size_t)G * vd.maxC * C::REC_BYTES +
+                                          ((size_t)h * vd.maxC + cc0) * C::HREC_BYTES);
+    const int sl = vd.slot(b);
+    const bool init = sl >= 0 && vd.init(b);
+    const size_t sb = ((size_t)max(sl, 0) * H + h) * SN * SP;
+    h0b = init ? vd.ssm_pool + sb : nullptr;
+    hfb = sl >= 0 ? vd.ssm_pool + sb : nullptr;
+    if (sl >= 0) hist_wr = vd.conv_pool + (int64_t)sl * 3 * cv.Cc;
+    if (init) hist_rd = hist_wr;
+  } else {
+    L = Lrows;
+    row0 = (int64_t)b * L;
+    const int nCw = (L + Q - 1) / Q;
+    wsg = ws + (size_t)(b * G + g) * nCw * C::REC_BYTES;
+    hrec = reinterpret_cast<const float*>(ws + (size_t)G * nCw * C::REC_BYTES * (size_t)(gridDim.x / H) +
+                                          ((size_t)b * H + h) * nCw * C::HREC_BYTES);
+    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
+    h0b = h0 ? h0 + sbase : nullptr;
+    hfb = h_final ? h_final + sbase : nullptr;
+    if (CONV && cv.state) {
+      hist_wr = static_cast<T*>(cv.state) + (int64_t)b * 3 * cv.Cc;
+      hist_rd = hist_wr;
+    }
+  }
+  const int nC = (L + Q - 1) / Q;
   // block totals of chunk c (pi at the ends of its two 32-token blocks), from LDS
   auto tot_of = [&](int c, int k) { return S.sRec[c % 3][Q + 32 * k + 31]; };
 
@@ -1408,13 +1538,12 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     const int hw = wave - 4;
     f32x16 hacc[2];                     // [p-block]
     Frag<T> af[C::KS_Q];
-    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n = hw * 32 + acc_row(r, lane);
-        hacc[i][r] = h0 ? h0[sbase + n * SP + i * 32 + col] : 0.f;
+        hacc[i][r] = h0b ? h0b[n * SP + i * 32 + col] : 0.f;
       }
     auto fetch_bt = [&](int c) {
       const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
@@ -1462,13 +1591,13 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       fetch_bt(min(c + 1, nC - 1));
       __syncthreads();
     }
-    if (h_final) {
+    if (hfb) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int n = hw * 32 + acc_row(r, lane);
-          h_final[sbase + n * SP + i * 32 + col] = hacc[i][r];
+          hfb[n * SP + i * 32 + col] = hacc[i][r];
         }
     }
   } else {
@@ -1490,7 +1619,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         cw[e] = *reinterpret_cast<const f32x4*>(cv.w + (int64_t)(h * SP + p0 + e) * 4);
         cb[e] = cv.bias ? cv.bias[h * SP + p0 + e] : 0.f;
       }
-      if (cv.state) hist = static_cast<const T*>(cv.state) + (int64_t)b * 3 * cv.Cc + h * SP + p0;
+      if (hist_rd) hist = hist_rd + h * SP + p0;
     }
     // per-thread element offsets inside a chunk's rows fit 32 bits; chunk bases are uniform
     const uint32_t xs = (uint32_t)x_stride, zs = (uint32_t)z_stride, ys = (uint32_t)y_stride;
@@ -1710,13 +1839,16 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           const int q = htid - 16;         // the group's B (q < 32) and C channels
           ch = H * SP + (q < 32 ? 0 : G * SN) + g * SN + 4 * (q & 31);
         }
-        if (cv.state && ch >= 0) {
-          T* hs = static_cast<T*>(cv.state) + (int64_t)b * 3 * cv.Cc + ch;
+        if (hist_wr && ch >= 0) {
+          T* hs = hist_wr + ch;
+          const T* hr = hist_rd ? hist_rd + ch : nullptr;   // the old history, or zeros
           Raw4<T> f[3];
 #pragma unroll
           for (int j = 0; j < 3; ++j) {
             const int t = L - 3 + j;
-            f[j] = ld4(t >= 0 ? x + (row0 + t) * x_stride + ch : hs + (t + 3) * cv.Cc);
+            if (t >= 0) f[j] = ld4(x + (row0 + t) * x_stride + ch);
+            else if (hr) f[j] = ld4(hr + (t + 3) * cv.Cc);
+            else f[j].v = (bf16x4){};
           }
 #pragma unroll
           for (int j = 0; j < 3; ++j) *reinterpret_cast<bf16x4*>(hs + j * cv.Cc) = f[j].v;
@@ -1772,13 +1904,13 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, false>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
-                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{});
+                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{}, VarlenDev{});
   }
   if constexpr (PIPE64) {
     hipLaunchKernelGGL((ssd_scan64_kernel<false>), dim3(a.B * a.H), dim3(P64_THREADS), scan_lds, stream,
                        static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                        a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{});
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{}, VarlenDev{});
   } else {
     hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
                        static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
@@ -1805,12 +1937,53 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
-                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv);
+                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv, VarlenDev{});
   }
   hipLaunchKernelGGL((ssd_scan64_kernel<true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
                      stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv);
+                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{});
+  return hipGetLastError();
+}
+
+// records for up to total / 64 + nseq chunks (the most a packed batch of nseq sequences over
+// total rows can have), then the sanitized offsets and the per-sequence first chunks
+static int varlen_max_chunks(int total, int nseq) { return total / P64 + nseq; }
+
+size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G) {
+  using C = Cfg<bf16, P64>;
+  const size_t maxC = (size_t)varlen_max_chunks(total, nseq);
+  return maxC * ((size_t)G * C::REC_BYTES + (size_t)H * C::HREC_BYTES) + 2 * ((size_t)nseq + 1) * sizeof(int32_t);
+}
+
+hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, const VarlenArgs& va,
+                                     hipStream_t stream) {
+  using T = bf16;
+  constexpr int Q = P64;
+  using C = Cfg<T, Q>;
+  const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, true, true>), prep_lds);
+    if (e == hipSuccess)
+      e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<true, true>), sizeof(Pipe64Smem));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int maxC = varlen_max_chunks(a.L, va.nseq);
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  int32_t* cu = reinterpret_cast<int32_t*>(ws + (size_t)maxC * ((size_t)a.G * C::REC_BYTES + (size_t)a.H * C::HREC_BYTES));
+  int32_t* cc = cu + va.nseq + 1;
+  hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(VIDX_THREADS), 0, stream, va.cu, va.nseq, a.L, cu, cc);
+  const VarlenDev vd{cu, cc, va.slots, va.has_init, va.ssm_pool, static_cast<bf16*>(va.conv_pool),
+                     va.nseq, va.npool, maxC};
+  hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true, true>), dim3(a.G * maxC), dim3(PREP_THREADS), prep_lds,
+                     stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
+                     a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, ws, a.L, a.H, a.G, maxC,
+                     cv, vd);
+  hipLaunchKernelGGL((ssd_scan64_kernel<true, true>), dim3(va.nseq * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
+                     stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                     a.z_stride, nullptr, nullptr, static_cast<T*>(a.y), a.y_stride, ws, a.L, a.H, a.G, cv, vd);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 3
+    assert m2.mamba2_abi_version() == 4
 
 
 def dims(**kw):
