@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 4
+#define MAMBA2_ABI_VERSION 5
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -247,6 +247,26 @@ int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w
                         const float* bias, void* conv_state, const void* dt_raw_t,
                         const float* dt_bias, const float* A, const float* D, const void* z_t,
                         float* ssm_state, void* y_t, void* stream);
+
+/*
+ * mamba2_state_update_slots -- mamba2_state_update for a continuous batch whose caches
+ * live in pools (as an inference engine keeps them: neurohive, section
+ * "Развертывание"): token b (row b of u_t, dt_raw_t, z_t, y_t) updates entry slots[b]
+ * of conv_pool [npool][W-1][Cc] and ssm_pool [npool][H][N][P] in place. A token whose
+ * entry is outside [0, npool) is skipped: its y row is written as zeros and no cache is
+ * touched. Two tokens must not share an entry (their updates would race).
+ *
+ *   slots  [B] int32 (device), 4-byte aligned; dims->seqlen must be 1
+ *   other arguments as in mamba2_state_update (the pools in place of the caches; they may
+ *   be NULL when npool == 0)
+ * For an entry in range the results are bitwise those of mamba2_state_update on that
+ * entry's caches.
+ */
+int mamba2_state_update_slots(const mamba2_dims* dims, const void* u_t, const float* w,
+                              const float* bias, void* conv_pool, const void* dt_raw_t,
+                              const float* dt_bias, const float* A, const float* D,
+                              const void* z_t, float* ssm_pool, const int32_t* slots,
+                              int32_t npool, void* y_t, void* stream);
 
 /*
  * mamba2_group_rmsnorm -- the block's RMSNorm of the gated output (hyper.ai summary,

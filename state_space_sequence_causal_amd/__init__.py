@@ -21,6 +21,7 @@ __all__ = [
     "mamba2_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill",
     "mamba2_conv_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill_varlen",
     "mamba2_conv_ssd_prefill_varlen_workspace_bytes", "mamba2_group_rmsnorm",
+    "mamba2_state_update_slots",
     "mamba2_abi_version", "mamba2_last_error",
     "MAMBA2_F32", "MAMBA2_BF16", "STATUS",
 ]
@@ -72,9 +73,11 @@ lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes.restype = _sz
 lib.mamba2_conv_ssd_prefill_varlen.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                                _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.mamba2_state_update_slots.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _i32, _vp, _vp]
 lib.mamba2_group_rmsnorm.argtypes = [_dims, _vp, _i64, _vp, ctypes.c_float, _vp, _i64, _vp]
 for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_varlen",
-           "mamba2_state_update", "mamba2_group_rmsnorm"):
+           "mamba2_state_update", "mamba2_state_update_slots", "mamba2_group_rmsnorm"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -214,6 +217,18 @@ def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, 
     _check(lib.mamba2_state_update(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_state),
                                    _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
                                    _ptr(ssm_state), _ptr(y_t), _stream()))
+
+
+def mamba2_state_update_slots(u_t, w, bias, conv_pool, dt_raw_t, dt_bias, A, D, z_t, ssm_pool, slots, y_t,
+                              *, ngroups: int) -> None:
+    """One decode token per row of u_t; row b updates pool entry slots[b] (int32 [B]) of
+    conv_pool [npool, 3, Cc] and ssm_pool [npool, H, N, P] in place."""
+    B, H = dt_raw_t.shape
+    npool = 0 if ssm_pool is None else ssm_pool.shape[0]
+    d = make_dims(B, 1, H, ngroups, 64, io_dtype_of(u_t))
+    _check(lib.mamba2_state_update_slots(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_pool),
+                                         _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
+                                         _ptr(ssm_pool), _ptr(slots), npool, _ptr(y_t), _stream()))
 
 
 def mamba2_group_rmsnorm(g, weight, out, *, ngroups: int, eps: float = 1e-5) -> None:

@@ -64,6 +64,8 @@ struct DecodeArgs {
   float* ssm_state;
   void* y_t;
   int B, H, G;
+  const int32_t* slots = nullptr;   // token -> pool entry, or NULL for entry = token
+  int npool = 0;
 };
 hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream);
 

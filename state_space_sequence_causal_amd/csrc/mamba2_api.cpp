@@ -396,6 +396,43 @@ M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const f
                     "state_update launch");
 }
 
+M2_EXPORT int mamba2_state_update_slots(const mamba2_dims* d, const void* u_t, const float* w,
+                                        const float* bias, void* conv_pool, const void* dt_raw_t,
+                                        const float* dt_bias, const float* A, const float* D,
+                                        const void* z_t, float* ssm_pool, const int32_t* slots,
+                                        int32_t npool, void* y_t, void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if (d->seqlen != 1) return fail(MAMBA2_ERR_SHAPE, "state_update_slots needs seqlen 1 (got %d)", d->seqlen);
+  if (!u_t || !w || !dt_raw_t || !dt_bias || !A || !y_t || !slots)
+    return fail(MAMBA2_ERR_NULL, "u_t, w, dt_raw_t, dt_bias, A, slots and y_t must not be NULL");
+  if (npool < 0) return fail(MAMBA2_ERR_SHAPE, "npool %d < 0", npool);
+  if (npool > 0 && (!conv_pool || !ssm_pool))
+    return fail(MAMBA2_ERR_NULL, "conv_pool and ssm_pool must not be NULL when npool > 0");
+  const int io = d->io_dtype, es = esize_of(io);
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, B = d->batch;
+  if (H / G > 256) return fail(MAMBA2_ERR_UNSUPPORTED, "more than 256 heads per group");
+  const int64_t Cc = H * P + 2 * G * N;
+  const void* al[] = {u_t, w, conv_pool, ssm_pool, y_t, z_t};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "u_t, w, conv_pool, ssm_pool, y_t, z_t must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(slots) & 3u) return fail(MAMBA2_ERR_ALIGN, "slots must be 4-byte aligned");
+  Range ry = span(y_t, B, H * P, H * P, es);
+  Range rcs = span(conv_pool, 1, 0, npool * 3 * Cc, es), rss = span(ssm_pool, 1, 0, npool * H * N * P, 4);
+  Range ins[] = {span(u_t, B, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
+                 span(dt_raw_t, B, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
+                 span(D, 1, 0, H, 4),         span(z_t, B, H * P, H * P, es), span(slots, 1, 0, B, 4)};
+  for (const Range& r : ins)
+    if (overlap(ry, r) || overlap(rcs, r) || overlap(rss, r))
+      return fail(MAMBA2_ERR_ALIAS, "y_t or a pool overlaps an input");
+  if (overlap(ry, rcs) || overlap(ry, rss) || overlap(rcs, rss))
+    return fail(MAMBA2_ERR_ALIAS, "y_t and the pools must not overlap");
+  m2::DecodeArgs a{u_t, w, bias, conv_pool, dt_raw_t, dt_bias, A, D, z_t, ssm_pool, y_t,
+                   d->batch, d->nheads, d->ngroups, slots, npool};
+  return hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, static_cast<hipStream_t>(stream)),
+                    "state_update_slots launch");
+}
+
 M2_EXPORT int mamba2_group_rmsnorm(const mamba2_dims* d, const void* g, int64_t g_stride,
                                    const float* weight, float eps, void* out, int64_t out_stride,
                                    void* stream) {

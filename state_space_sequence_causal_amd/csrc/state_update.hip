@@ -6,6 +6,9 @@
 // ~0.5 KiB of token inputs. The kernel is therefore a pure HBM stream of the
 // state with the conv, dt, gate and output folded into it.
 //
+// With a slot map the caches of token b are an entry of cache pools (continuous
+// batching); the rest is unchanged.
+//
 // One workgroup per (sequence b, group g): it owns the x channels of the
 // group's heads and the group's B and C channels, so every conv-cache column
 // has exactly one reader-writer (no cross-workgroup ordering is needed). Each of
@@ -60,7 +63,8 @@ void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
     const float* __restrict__ A, const float* __restrict__ D, const T* __restrict__ z_t,
-    float* __restrict__ ssm_state, T* __restrict__ y_t, int H, int G) {
+    float* __restrict__ ssm_state, T* __restrict__ y_t, int H, int G, const int32_t* __restrict__ slots,
+    int npool) {
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
   const int hpg = H / G;
@@ -79,6 +83,17 @@ void state_update_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // the caches of token b are entry sb of the pools (entry b without a slot map); a token
+  // whose entry is out of range is skipped: its y is zero and no cache is touched
+  int sb = b;
+  if (slots) {
+    sb = slots[b];
+    if (sb < 0 || sb >= npool) {
+      for (int i = tid; i < hpg * DEC_P / 4; i += DEC_THREADS)
+        store4(y_t + (int64_t)b * di + g * hpg * DEC_P + 4 * i, 0.f, 0.f, 0.f, 0.f);
+      return;   // the whole workgroup leaves
+    }
+  }
   const int q = lane & 15, rg = lane >> 4;
 
   // Work items of this wave: (head j, part) for j = wave, wave + DEC_WAVES, ...; part m holds
@@ -89,7 +104,7 @@ void state_update_kernel(
   // the wave's state base is uniform; an item is a 32-bit byte offset from it (heads of a
   // wave are DEC_WAVES apart, parts of a head 4 DEC_K rows apart)
   const char* wbase = reinterpret_cast<const char*>(
-      ssm_state + ((int64_t)b * H + g * hpg + wave) * DEC_N * DEC_P);
+      ssm_state + ((int64_t)sb * H + g * hpg + wave) * DEC_N * DEC_P);
   const uint32_t lane_off = (uint32_t)(rg * DEC_P + 4 * q) * 4u;
   auto item_off = [&](int it) -> uint32_t {
     return (uint32_t)((it / DEC_IPH) * DEC_WAVES * DEC_N * DEC_P + (it % DEC_IPH) * 4 * DEC_K * DEC_P) * 4u;
@@ -113,7 +128,7 @@ void state_update_kernel(
   // stream, must not queue behind the state. Each conv thread owns 4 channels.
   constexpr int CV = 4;
   const T* ub = u_t + (int64_t)b * Cc;
-  T* csb = conv_state + (int64_t)b * (DEC_W - 1) * Cc;
+  T* csb = conv_state + (int64_t)sb * (DEC_W - 1) * Cc;
   const int lc = tid * CV;
   const bool conv_thread = lc < nch;
   const int c = lc < nx ? g * nx + lc
@@ -243,7 +258,8 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((state_update_kernel<T>), dim3(a.B * a.G), dim3(DEC_THREADS), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
-                     static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G);
+                     static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
+                     a.npool);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ def test_header_declares_the_calls():
     names = declared()
     for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm",
               "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_workspace_bytes",
+              "mamba2_conv_ssd_prefill_varlen", "mamba2_state_update_slots",
               "mamba2_ssd_prefill_workspace_bytes", "mamba2_last_error", "mamba2_abi_version"):
         assert n in names
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 4
+    assert m2.mamba2_abi_version() == 5
 
 
 def dims(**kw):
@@ -226,3 +227,60 @@ def test_conv_prefill_workspace_size():
         assert m2.mamba2_conv_ssd_prefill_workspace_bytes(d) == want
     assert m2.mamba2_conv_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
     assert m2.lib.mamba2_conv_ssd_prefill_workspace_bytes(None) == 0
+
+
+# ------------------------------------------------------------------ decode with slot pools
+def decode_slots(d, **kw):
+    a = dict(u=BASE, w=BASE + 1 * MB, b=BASE + 2 * MB, cs=BASE + 3 * MB, dt=BASE + 4 * MB,
+             dtb=BASE + 5 * MB, A=BASE + 6 * MB, D=BASE + 7 * MB, z=BASE + 8 * MB,
+             ss=BASE + 64 * MB, sl=BASE + 9 * MB, npool=4, y=BASE + 10 * MB)
+    a.update(kw)
+    return m2.lib.mamba2_state_update_slots(ctypes.byref(d), a["u"], a["w"], a["b"], a["cs"], a["dt"],
+                                            a["dtb"], a["A"], a["D"], a["z"], a["ss"], a["sl"], a["npool"],
+                                            a["y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=None), ENULL), (dict(u=None), ENULL), (dict(y=None), ENULL), (dict(cs=None), ENULL),
+    (dict(npool=-1), ESHAPE), (dict(sl=BASE + 9 * MB + 2), EALIGN), (dict(ss=BASE + 64 * MB + 4), EALIGN),
+    (dict(y=BASE), EALIAS), (dict(cs=BASE + 64 * MB), EALIAS), (dict(sl=BASE + 10 * MB), EALIAS),
+])
+def test_decode_slots_rejects(kw, code):
+    assert decode_slots(dims(seqlen=1, batch=3), **kw) == code, m2.mamba2_last_error()
+
+
+def test_decode_slots_needs_one_token():
+    assert decode_slots(dims(seqlen=2)) == ESHAPE
+
+
+# ------------------------------------------------------------------ packed prefill
+def varlen(d, **kw):
+    cc = d.nheads * 64 + 2 * d.ngroups * 128
+    a = dict(u=BASE, us=cc, w=BASE + 4 * MB, b=BASE + 5 * MB, cu=BASE + 6 * MB, sl=BASE + 7 * MB,
+             hi=BASE + 8 * MB, cp=BASE + 9 * MB, sp=BASE + 64 * MB, npool=4, dt=BASE + 10 * MB,
+             dtb=BASE + 11 * MB, A=BASE + 12 * MB, D=BASE + 13 * MB, z=BASE + 14 * MB, zs=d.nheads * 64,
+             y=BASE + 18 * MB, ys=d.nheads * 64, ws=BASE + 128 * MB, wsb=1 << 30)
+    a.update(kw)
+    return m2.lib.mamba2_conv_ssd_prefill_varlen(
+        ctypes.byref(d), a["u"], a["us"], a["w"], a["b"], a["cu"], a["sl"], a["hi"], a["cp"], a["sp"],
+        a["npool"], a["dt"], a["dtb"], a["A"], a["D"], a["z"], a["zs"], a["y"], a["ys"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), ENULL), (dict(u=None), ENULL), (dict(y=None), ENULL), (dict(cp=None), ENULL),
+    (dict(npool=-2), ESHAPE), (dict(us=500), ESHAPE), (dict(cu=BASE + 6 * MB + 2), EALIGN),
+    (dict(cp=BASE + 9 * MB + 8), EALIGN), (dict(y=BASE), EALIAS), (dict(sp=BASE + 6 * MB), EALIAS),
+    (dict(ws=BASE + 18 * MB), EALIAS), (dict(ws=None), 7), (dict(wsb=100), 7),
+])
+def test_varlen_rejects(kw, code):
+    assert varlen(dims(io=m2.MAMBA2_BF16, batch=3, seqlen=300), **kw) == code, m2.mamba2_last_error()
+
+
+def test_varlen_settings_and_workspace():
+    assert varlen(dims(io=m2.MAMBA2_F32, batch=3)) == EUNSUP
+    assert varlen(dims(io=m2.MAMBA2_BF16, chunk=128, batch=3)) == EUNSUP
+    d = dims(io=m2.MAMBA2_BF16, batch=5, seqlen=1000, nheads=16, ngroups=8)
+    m = 1000 // 64 + 5
+    rec = 4096 * 3 + 2 * 128 * 64 * 2
+    assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == m * (8 * rec + 16 * 768) + 8 * 6
+    assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(dims(io=m2.MAMBA2_F32)) == 0
