@@ -182,7 +182,8 @@ int mamba2_conv_ssd_prefill(const mamba2_dims* dims, const void* xBC, int64_t xb
  * mamba2_conv_ssd_prefill_varlen_workspace_bytes -- device workspace of
  * mamba2_conv_ssd_prefill_varlen for `dims` (batch = number of sequences, seqlen =
  * total packed rows; bf16 io, chunk 64), 0 if `dims` is invalid or another setting:
- *   M * (ngroups * R + nheads * 768) + 8 * (batch + 1),   M = seqlen / 64 + batch
+ *   M * (ngroups * R + nheads * 768 + 16 + 384 * nheads) + 8 * (batch + 1),
+ *   M = seqlen / 64 + batch
  * with R the per-(group, chunk) record of mamba2_ssd_prefill_workspace_bytes at chunk 64
  * (4096 * 3 + 2 * 128 * 64 * 2 bytes).
  */

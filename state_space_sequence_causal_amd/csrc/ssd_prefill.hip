@@ -119,14 +119,20 @@ __device__ __forceinline__ Frag<T> ld_frag(const void* p) {
   return f;
 }
 
-// Device view of a packed variable-length batch: sanitized row offsets cu[nseq + 1] and the
-// first global chunk of each sequence cc[nseq + 1] (both in the workspace), the slot map
-// and the initial-state flags, the pools, and the chunk capacity of the workspace records.
+// Device view of a packed variable-length batch: sanitized row offsets cu[nseq + 1], the
+// first global chunk of each sequence cc[nseq + 1] and, per global chunk, info = {first packed
+// row, valid rows | 256 if the sequence starts there | 512 if it starts from its entry's state,
+// sequence, the sequence's pool entry or -1} (all three in the workspace), and, also in the
+// workspace, the x-channel conv history of each sequence at its first chunk (written by the
+// prep kernel, read by the scan at a fixed place per chunk),
+// the slot map and the initial-state flags, the pools, the chunk capacity of the workspace
+// records, and the number of scan workgroups per head (each walks a range of sequences).
 struct VarlenDev {
-  const int32_t* cu; const int32_t* cc;
+  const int32_t* cu; const int32_t* cc; const int4* info;
   const int32_t* slots; const int32_t* has_init;
   float* ssm_pool; bf16* conv_pool;
-  int nseq, npool, maxC;
+  bf16* hist;   // [chunk][3][H * P]: at a sequence's first chunk, the x-channel conv history
+  int nseq, npool, maxC, K;
   // pool entry of sequence i, or -1 when it has none (slot out of range)
   __device__ __forceinline__ int slot(int i) const {
     const int s = slots ? slots[i] : i;
@@ -140,9 +146,14 @@ struct VarlenDev {
 // global chunk of each sequence, cc[i] = sum over j < i of ceil((cu'[j+1] - cu'[j]) / 64).
 // One workgroup; thread t takes a contiguous run of the nseq + 1 entries.
 constexpr int VIDX_THREADS = 1024;
+constexpr int INFO_FIRST = 256, INFO_INIT = 512;
 __global__ __launch_bounds__(VIDX_THREADS) void varlen_index_kernel(const int32_t* __restrict__ cu_in, int nseq,
                                                                     int total, int32_t* __restrict__ cu_out,
-                                                                    int32_t* __restrict__ cc_out) {
+                                                                    int32_t* __restrict__ cc_out,
+                                                                    int4* __restrict__ info,
+                                                                    const int32_t* __restrict__ slots,
+                                                                    const int32_t* __restrict__ has_init,
+                                                                    int npool) {
   __shared__ int part[VIDX_THREADS];
   const int t = threadIdx.x, n = nseq + 1;
   const int per = (n + VIDX_THREADS - 1) / VIDX_THREADS;
@@ -178,7 +189,15 @@ __global__ __launch_bounds__(VIDX_THREADS) void varlen_index_kernel(const int32_
   int run = t > 0 ? part[t - 1] : 0;
   for (int j = j0; j < j1; ++j) {
     cc_out[j] = run;
-    if (j < nseq) run += (cu_out[j + 1] - cu_out[j] + 63) / 64;
+    if (j < nseq) {
+      const int len = cu_out[j + 1] - cu_out[j];
+      int sl = slots ? slots[j] : j;
+      if (sl < 0 || sl >= npool) sl = -1;
+      const int init = sl >= 0 && has_init && has_init[j] != 0 ? INFO_INIT : 0;
+      for (int k = 0; k < (len + 63) / 64; ++k)
+        info[run + k] = make_int4(cu_out[j] + 64 * k, min(64, len - 64 * k) | (k == 0 ? INFO_FIRST : 0) | init, j, sl);
+      run += (len + 63) / 64;
+    }
   }
 }
 
@@ -208,17 +227,11 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
     c = rec % vd.maxC;
     b = 0;
     if (c >= vd.cc[vd.nseq]) return;   // past the batch's chunks: the whole workgroup leaves
-    int lo = 0, hi = vd.nseq - 1;        // the sequence: the last i with cc[i] <= c
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (vd.cc[mid] <= c) lo = mid;
-      else hi = mid - 1;
-    }
-    t0 = (c - vd.cc[lo]) * Q;
-    len = vd.cu[lo + 1] - vd.cu[lo];
-    row0 = vd.cu[lo] + t0;
-    const int sl = vd.slot(lo);
-    if (sl >= 0 && vd.init(lo)) hist0 = reinterpret_cast<const T*>(vd.conv_pool) + (int64_t)sl * 3 * cv.Cc;
+    const int4 ci = vd.info[c];
+    t0 = ci.x - vd.cu[ci.z];
+    len = t0 + (ci.y & 255);           // rows of the sequence up to the chunk's end
+    row0 = ci.x;
+    if (ci.y & INFO_INIT) hist0 = reinterpret_cast<const T*>(vd.conv_pool) + (int64_t)ci.w * 3 * cv.Cc;
     nC = vd.maxC;
   } else {
     c = rec % nC;
@@ -345,6 +358,20 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
       const bool ok = s < nvalid;
       st16(&sB[s][e0], ok ? rB[i] : zero16<T>());
       st16(&sC[s][e0], ok ? rC[i] : zero16<T>());
+    }
+  }
+  if constexpr (VARLEN) {
+    // a sequence's first chunk: the conv history of the group's x channels (zeros without an
+    // initial state) goes to the chunk's place in the history area, where the scan reads it
+    const int4 ci = vd.info[c];
+    if (ci.y & INFO_FIRST) {
+      const int nxv = (H / G) * SP / VE;   // 16-byte vectors of the group's x channels per row
+      const int HP = H * SP;
+      for (int v = tid; v < 3 * nxv; v += PREP_THREADS) {
+        const int j = v / nxv, e0 = g * (H / G) * SP + (v % nxv) * VE;
+        const Vec<T> hv = hist0 ? ld16(hist0 + (int64_t)j * cv.Cc + e0) : zero16<T>();
+        st16(reinterpret_cast<T*>(vd.hist) + ((size_t)c * 3 + j) * HP + e0, hv);
+      }
     }
   }
   __syncthreads();
@@ -1379,13 +1406,19 @@ struct Pipe64Smem {
   bf16 sHt[2][SP][SN];                      // H^T hi by chunk parity (hsw)
   bf16 sHtlo[2][SP][SN];                    //     lo
   float sRec[3][3 * P64];                   // dt | pi | v, chunk c in slot c % 3
+  int4 sInfo[5];                            // packed batch: chunk info, chunk c in slot c % 5
 };
 
 // With CONV, x is the raw xBC tensor (x_stride its row stride): the helper waves apply the
 // conv to the head's x channels as they stage them, and at the end write the new conv
 // history of those channels (and, in the first head of each group, of the group's B and C).
-// With VARLEN (CONV only) workgroup (i, h) runs sequence i of a packed batch: its rows, its
-// workspace records, and its state and conv history in the slot pools.
+// With VARLEN (CONV only) workgroup (k, h) runs head h over the k-th of K ranges of
+// consecutive sequences of a packed batch (ranges balanced by chunk count): it walks their
+// chunks as one stream, whose records are contiguous in the workspace. Where a sequence
+// ends the H waves store its state to its pool entry and take up the next sequence's
+// initial state, which they publish in place of the carried one; the helper waves take
+// each chunk's rows from the per-chunk info and, at a sequence start, the conv history
+// from the pool. The new conv histories are written at the end.
 template <bool CONV, bool VARLEN = false>
 __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
@@ -1407,9 +1440,12 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   const int col = lane & 31, g2 = lane >> 5;
 
   // the workgroup's sequence: its L rows from row0, its records, its initial and final state
-  // (h0b / hfb: the head's N x P block, or none) and its conv history (read / written)
+  // (h0b / hfb: the head's N x P block, or none) and its conv history (read / written).
+  // VARLEN: sequences s_begin .. s_end, chunks gc0 + (0 .. nC) with info cinfo[0 .. nC].
   int L;
   int64_t row0;
+  [[maybe_unused]] int s_begin = 0, s_end = 0, gc0 = 0;
+  [[maybe_unused]] const int4* cinfo = nullptr;
   const unsigned char* wsg;
   const float* hrec;
   const float* h0b;
@@ -1417,19 +1453,35 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   const T* hist_rd = nullptr;
   T* hist_wr = nullptr;
   if constexpr (VARLEN) {
-    row0 = vd.cu[b];
-    L = vd.cu[b + 1] - vd.cu[b];
-    const int cc0 = vd.cc[b];
-    wsg = ws + ((size_t)g * vd.maxC + cc0) * C::REC_BYTES;
+    const int TC = vd.cc[vd.nseq];
+    // first sequence of range kk: the first i with cc[i] >= ceil(kk TC / K)
+    auto split = [&](int kk) -> int {
+      if (kk <= 0) return 0;
+      if (kk >= vd.K) return vd.nseq;
+      const int target = (int)(((int64_t)kk * TC + vd.K - 1) / vd.K);
+      int lo = 0, hi = vd.nseq;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (vd.cc[mid] < target) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    s_begin = split(b);
+    s_end = split(b + 1);
+    gc0 = vd.cc[s_begin];
+    L = (vd.cc[s_end] - gc0) * Q;   // the stream's chunks, as rows
+    row0 = 0;
+    cinfo = vd.info + gc0;
+    wsg = ws + ((size_t)g * vd.maxC + gc0) * C::REC_BYTES;
     hrec = reinterpret_cast<const float*>(ws + (size_t)G * vd.maxC * C::REC_BYTES +
-                                          ((size_t)h * vd.maxC + cc0) * C::HREC_BYTES);
-    const int sl = vd.slot(b);
-    const bool init = sl >= 0 && vd.init(b);
-    const size_t sb = ((size_t)max(sl, 0) * H + h) * SN * SP;
-    h0b = init ? vd.ssm_pool + sb : nullptr;
-    hfb = sl >= 0 ? vd.ssm_pool + sb : nullptr;
-    if (sl >= 0) hist_wr = vd.conv_pool + (int64_t)sl * 3 * cv.Cc;
-    if (init) hist_rd = hist_wr;
+                                          ((size_t)h * vd.maxC + gc0) * C::HREC_BYTES);
+    h0b = nullptr;                  // the initial state of the stream's first sequence
+    hfb = nullptr;                  // states are stored per sequence
+    if (L > 0) {
+      const int4 c0 = cinfo[0];
+      if (c0.y & INFO_INIT) h0b = vd.ssm_pool + ((size_t)c0.w * H + h) * SN * SP;
+    }
   } else {
     L = Lrows;
     row0 = (int64_t)b * L;
@@ -1448,6 +1500,10 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   const int nC = (L + Q - 1) / Q;
   // block totals of chunk c (pi at the ends of its two 32-token blocks), from LDS
   auto tot_of = [&](int c, int k) { return S.sRec[c % 3][Q + 32 * k + 31]; };
+  // packed batch: the info of chunk c, from the workspace (prologue, epilogue) or from the LDS
+  // ring, which holds chunks c - 1 .. c + 2 during iteration c (a global read in the loop would
+  // be a scalar load, and a pending scalar load makes every LDS wait a full drain)
+  [[maybe_unused]] auto info_at = [&](int c, bool ring) -> int4 { return ring ? S.sInfo[c % 5] : cinfo[c]; };
 
   if (wave < 4) {
     // ========================================================== Y waves
@@ -1538,13 +1594,26 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     const int hw = wave - 4;
     f32x16 hacc[2];                     // [p-block]
     Frag<T> af[C::KS_Q];
+    // the head's N x P state block <-> this wave's rows of the accumulators
+    auto load_state = [&](const float* src) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = hw * 32 + acc_row(r, lane);
-        hacc[i][r] = h0b ? h0b[n * SP + i * 32 + col] : 0.f;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int n = hw * 32 + acc_row(r, lane);
+          hacc[i][r] = src ? src[n * SP + i * 32 + col] : 0.f;
+        }
+    };
+    [[maybe_unused]] auto store_state = [&](float* dst) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = hw * 32 + acc_row(r, lane);
+          dst[n * SP + i * 32 + col] = hacc[i][r];
+        }
+    };
+    load_state(h0b);
     auto fetch_bt = [&](int c) {
       const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
 #pragma unroll
@@ -1587,9 +1656,38 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           mma(hacc[i], af[j], frag_contig(&S.sXWlo[cur][prow][k0], 0));
         }
       }
+      if constexpr (VARLEN) {
+        // the next chunk starts a sequence: store this sequence's state in its entry, then take
+        // up the next one's initial state (zeros without one), which is published below
+        if (c + 1 < nC) {
+          const int4 cn = info_at(c + 1, true);
+          if (cn.y & INFO_FIRST) {
+            const int so = info_at(c, true).w;
+            if (so >= 0) store_state(vd.ssm_pool + ((size_t)so * H + h) * SN * SP);
+            load_state(cn.y & INFO_INIT ? vd.ssm_pool + ((size_t)cn.w * H + h) * SN * SP : nullptr);
+          }
+        }
+      }
       publish(cur);
       fetch_bt(min(c + 1, nC - 1));
       __syncthreads();
+    }
+    if constexpr (VARLEN) {
+      if (nC > 0) {
+        const int so = cinfo[nC - 1].w;
+        if (so >= 0) store_state(vd.ssm_pool + ((size_t)so * H + h) * SN * SP);
+      }
+      // an empty sequence without an initial state leaves a zero state in its entry
+      for (int i = s_begin; i < s_end; ++i) {
+        const int sl = vd.slot(i);
+        if (vd.cu[i + 1] == vd.cu[i] && sl >= 0 && !vd.init(i)) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              vd.ssm_pool[((size_t)sl * H + h) * SN * SP + (hw * 32 + acc_row(r, lane)) * SP + ii * 32 + col] = 0.f;
+        }
+      }
     }
     if (hfb) {
 #pragma unroll
@@ -1633,21 +1731,45 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
     // copy issues a fixed sequence of memory operations and the compiler's count of
     // outstanding loads stays exact: a merged count would wait for loads just issued.
-    auto helpers = [&](auto part_tag, auto rec_tag) {
+    auto helpers = [&](auto part_tag, auto rec_tag, auto duty_tag) {
       constexpr int PART = decltype(part_tag)::value;   // 2: a diagonal half, 4: an off quarter
       constexpr bool REC = decltype(rec_tag)::value;
+      // VARLEN duties: HIST, helper wave 0 (whose threads hold the first tokens of a chunk),
+      // loads each chunk's conv history rows; RING, helper wave 4, keeps the info ring
+      constexpr bool HIST = VARLEN && decltype(duty_tag)::value == 1;
+      constexpr bool RING = VARLEN && decltype(duty_tag)::value == 2;
       // x rows of the thread's tokens; with the conv, raw rows s0 - 3 .. s0 + 1
       constexpr int NX = CONV ? 5 : 2;
       Raw4<T> rX[NX], rZ[2];
       float rRec = 0.f;
       f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7 (4 hq .. 4 hq + 3)
-      auto load_set = [&](int c) {       // x and z of this thread's tokens
-        const int64_t r0 = row0 + (int64_t)c * Q;
+      // the history rows before the sequence that this thread's first tokens read (zeros
+      // without a history): for one sequence loaded once in the prologue, for a packed batch
+      // by the HIST role with each chunk's rows, from the chunk's place in the history area
+      Raw4<T> rH[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) rH[k].v = (bf16x4){};
+      // VARLEN: ci is the info of chunk c (from the workspace in the prologue, from the ring in
+      // the loop, read at the top of the iteration)
+      auto load_set = [&](int c, int4 ci) {   // x and z of this thread's tokens
+        // chunk c: its first row, its valid rows and whether a sequence starts there
+        int64_t r0;
+        int nval;
+        bool first;
+        if constexpr (VARLEN) {
+          r0 = ci.x;
+          nval = ci.y & 255;
+          first = (ci.y & INFO_FIRST) != 0;
+        } else {
+          r0 = row0 + (int64_t)c * Q;
+          nval = L - c * Q;
+          first = c == 0;
+        }
         const T* xc = xb + r0 * x_stride;
         const T* zc = zb + r0 * z_stride;
         // Rows past the end of the sequence load the last row instead (finite values; their
         // dt and v are zero, so they add nothing), which keeps the loads unconditional.
-        const int lim = L - 1 - c * Q;
+        const int lim = nval - 1;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const uint32_t s = (uint32_t)min(s0 + k, lim);
@@ -1659,11 +1781,17 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           // end the last row is read, and in the first chunk the rows before the sequence are
           // read as row 0 and replaced when that chunk is staged
           const T* xh = xc - 3 * x_stride;
-          const int lo = c == 0 ? 3 : 0;
+          const int lo = first ? 3 : 0;
 #pragma unroll
           for (int k = 0; k < NX; ++k) {
             const uint32_t s = (uint32_t)min(max(s0 + k, lo), lim + 3);
             rX[k] = ld4(xh + (s * xs + p0));
+          }
+          if constexpr (HIST) {
+            // every chunk issues the same 3 loads (used only where a sequence starts)
+            const T* hp = vd.hist + (size_t)(gc0 + c) * 3 * (H * SP) + h * SP + p0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) rH[k] = ld4(hp + min(s0 + k, 2) * (H * SP));
           }
         }
       };
@@ -1673,30 +1801,37 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       auto put_rec = [&](int c) {
         if constexpr (REC) S.sRec[c % 3][htid] = rRec;
       };
-      auto flush_y = [&](int c, bool full) {   // y of chunk c out of sZ[c & 1]
-        T* yc = yb + (row0 + (int64_t)c * Q) * y_stride;
+      auto flush_y = [&](int c, bool full, int4 cf) {   // y of chunk c out of sZ[c & 1]
+        int64_t r0;
+        int nval;
+        if constexpr (VARLEN) {
+          r0 = cf.x;
+          nval = cf.y & 255;
+        } else {
+          r0 = row0 + (int64_t)c * Q;
+          nval = L - c * Q;
+        }
+        T* yc = yb + r0 * y_stride;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int s = s0 + k;
           const Raw4<T> v = ld4(&S.sZ[c & 1][s][zpos<T>(s, p0)]);
-          if (full || c * Q + s < L) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
+          if (full || s < nval) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
         }
       };
-      // the history rows before the sequence that this thread's first tokens read (zeros
-      // without a history); used only when chunk 0 is staged
-      Raw4<T> rH[3];
-      auto load_hist = [&]() {
-        if constexpr (CONV) {
+      auto load_hist = [&]() {   // one sequence: the history rows, once
+        if constexpr (CONV && !VARLEN) {
 #pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            rH[k].v = (bf16x4){};
+          for (int k = 0; k < 3; ++k)
             if (hist && s0 + k < 3) rH[k] = ld4(hist + (s0 + k) * cv.Cc);
-          }
         }
       };
       // x^T, (w x)^T and z of chunk c (its set in registers) into buffers c & 1; FIRST: chunk 0
-      auto stage = [&](int c, auto first_tag) {
-        constexpr bool FIRST = decltype(first_tag)::value;
+      auto stage = [&](int c, auto first_tag, int4 cs) {
+        // one sequence: FIRST marks chunk 0 (the prologue's call); a packed batch: the chunk's
+        // info cs says whether a sequence starts there
+        bool first = decltype(first_tag)::value;
+        if constexpr (VARLEN) first = (cs.y & INFO_FIRST) != 0;
         const int buf = c & 1;
         if (z) {
 #pragma unroll
@@ -1713,7 +1848,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           Raw4<T> r[NX];
 #pragma unroll
           for (int k = 0; k < NX; ++k) r[k] = rX[k];
-          if constexpr (FIRST) {
+          if (first) {
 #pragma unroll
             for (int k = 0; k < 3; ++k)
               if (s0 - 3 + k < 0) r[k] = rH[k];   // rH[k] holds history row s0 + k
@@ -1796,9 +1931,28 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       };
       // prologue: records 0 and 1 into LDS; then chunk 0 staged and its tiles built, chunk 1's
       // set in flight
+      // packed batch: the HIST role keeps the info ring: chunks 0 .. 2 now, chunk c + 3 in
+      // iteration c (requested one iteration earlier). Lane l moves word l % 4 of the info:
+      // the per-lane address makes it a vector load (a scalar load in the loop would turn the
+      // LDS waits into full drains), and every lane of the wave takes part, so the role's
+      // memory operations stay unconditional
+      [[maybe_unused]] int rInfo = 0;
+      [[maybe_unused]] auto info_word = [&](int c) {
+        return reinterpret_cast<const int*>(cinfo + min(c, nC - 1))[lane & 3];
+      };
+      if constexpr (RING) {
+        if (nC > 0) {
+#pragma unroll
+          for (int k = 0; k < 3; ++k) reinterpret_cast<int*>(&S.sInfo[k])[lane & 3] = info_word(k);
+          rInfo = info_word(3);
+        }
+      }
+      // prologue info from the workspace (the ring is filled at the first barrier)
+      [[maybe_unused]] const int4 ci0 = VARLEN && nC > 0 ? cinfo[0] : int4{};
+      [[maybe_unused]] const int4 ci1 = VARLEN && nC > 0 ? cinfo[min(1, nC - 1)] : int4{};
       if (nC > 0) {
         load_hist();
-        load_set(0);
+        load_set(0, ci0);
         load_rec(0);
         put_rec(0);
         load_rec(min(1, nC - 1));
@@ -1808,25 +1962,37 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       }
       __syncthreads();
       if (nC > 0) {
-        stage(0, std::true_type{});
-        load_set(min(1, nC - 1));
+        stage(0, std::true_type{}, ci0);
+        load_set(min(1, nC - 1), ci1);
         build(0);
         fetch_gram(min(1, nC - 1));
       }
       __syncthreads();
       for (int c = 0; c < nC; ++c) {
+        // packed batch: the infos this iteration uses (chunks c - 1, c + 1, c + 2), read from
+        // the ring now so that their latency hides behind the tile build
+        int4 im1 = {}, ip1 = {}, ip2 = {};
+        if constexpr (VARLEN) {
+          im1 = S.sInfo[(c + 4) % 5];
+          ip1 = S.sInfo[min(c + 1, nC - 1) % 5];
+          ip2 = S.sInfo[min(c + 2, nC - 1) % 5];
+        }
         // ---- chunk c + 1: tiles and staging. Chunk indices are clamped, so every iteration
         // issues the same memory operations (the last stages a copy nobody reads).
         build(c + 1);
         fetch_gram(min(c + 2, nC - 1));
-        if (c >= 1) flush_y(c - 1, true);   // chunk c - 1 < nC - 1 is full
-        stage(c + 1, std::false_type{});
+        if (c >= 1) flush_y(c - 1, !VARLEN, im1);   // one sequence: chunk c - 1 < nC - 1 is full
+        stage(c + 1, std::false_type{}, ip1);
         put_rec(c + 2);
-        load_set(min(c + 2, nC - 1));
+        load_set(min(c + 2, nC - 1), ip2);
         load_rec(min(c + 3, nC - 1));
+        if constexpr (RING) {
+          reinterpret_cast<int*>(&S.sInfo[(c + 3) % 5])[lane & 3] = rInfo;
+          rInfo = info_word(c + 4);
+        }
         __syncthreads();
       }
-      if (nC > 0) flush_y(nC - 1, false);   // y of the last chunk
+      if (nC > 0) flush_y(nC - 1, false, VARLEN ? S.sInfo[(nC - 1) % 5] : int4{});   // y of the last chunk
       if constexpr (CONV) {
         // the new history: the last 3 raw inputs of (history, sequence). One thread per 4
         // channels reads all 3 before writing any, so an in-place shift (L < 3) is safe; every
@@ -1839,7 +2005,27 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           const int q = htid - 16;         // the group's B (q < 32) and C channels
           ch = H * SP + (q < 32 ? 0 : G * SN) + g * SN + 4 * (q & 31);
         }
-        if (hist_wr && ch >= 0) {
+        if constexpr (VARLEN) {
+          // every sequence of the workgroup's range that has an entry
+          for (int i = s_begin; ch >= 0 && i < s_end; ++i) {
+            const int sl = vd.slot(i);
+            if (sl < 0) continue;
+            T* hs = vd.conv_pool + (int64_t)sl * 3 * cv.Cc + ch;
+            const bool init = vd.init(i);
+            const int64_t ri = vd.cu[i];
+            const int Li = vd.cu[i + 1] - vd.cu[i];
+            Raw4<T> f[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+              const int t = Li - 3 + j;
+              if (t >= 0) f[j] = ld4(x + (ri + t) * x_stride + ch);
+              else if (init) f[j] = ld4(hs + (t + 3) * cv.Cc);
+              else f[j].v = (bf16x4){};
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) *reinterpret_cast<bf16x4*>(hs + j * cv.Cc) = f[j].v;
+          }
+        } else if (hist_wr && ch >= 0) {
           T* hs = hist_wr + ch;
           const T* hr = hist_rd ? hist_rd + ch : nullptr;   // the old history, or zeros
           Raw4<T> f[3];
@@ -1857,9 +2043,14 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     };
     using Half = std::integral_constant<int, 2>;
     using Quarter = std::integral_constant<int, 4>;
-    if (hv < 3) helpers(Half{}, std::true_type{});
-    else if (hv < 4) helpers(Half{}, std::false_type{});
-    else helpers(Quarter{}, std::false_type{});
+    using NoDuty = std::integral_constant<int, 0>;
+    using Hist = std::integral_constant<int, 1>;
+    using Ring = std::integral_constant<int, 2>;
+    if (VARLEN && hv == 0) helpers(Half{}, std::true_type{}, Hist{});
+    else if (hv < 3) helpers(Half{}, std::true_type{}, NoDuty{});
+    else if (hv < 4) helpers(Half{}, std::false_type{}, NoDuty{});
+    else if (VARLEN && hv == 4) helpers(Quarter{}, std::false_type{}, Ring{});
+    else helpers(Quarter{}, std::false_type{}, NoDuty{});
   }
 }
 
@@ -1947,13 +2138,32 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
 }
 
 // records for up to total / 64 + nseq chunks (the most a packed batch of nseq sequences over
-// total rows can have), then the sanitized offsets and the per-sequence first chunks
+// total rows can have), the per-chunk info, the per-chunk history area, then the sanitized
+// offsets and the per-sequence first chunks
 static int varlen_max_chunks(int total, int nseq) { return total / P64 + nseq; }
 
 size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G) {
   using C = Cfg<bf16, P64>;
   const size_t maxC = (size_t)varlen_max_chunks(total, nseq);
-  return maxC * ((size_t)G * C::REC_BYTES + (size_t)H * C::HREC_BYTES) + 2 * ((size_t)nseq + 1) * sizeof(int32_t);
+  return maxC * ((size_t)G * C::REC_BYTES + (size_t)H * C::HREC_BYTES + sizeof(int4) +
+                 (size_t)3 * H * SP * sizeof(bf16)) +
+         2 * ((size_t)nseq + 1) * sizeof(int32_t);
+}
+
+// scan workgroups per head: ranges of sequences enough for about two rounds of workgroups on
+// the CUs (one workgroup fits a CU), which uses the whole chip while a workgroup's fixed
+// start-up and drain stay a small part of its time
+static int varlen_ranges(int nseq, int H) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    return n;
+  }();
+  return max(1, min(nseq, (2 * cus + H / 2) / H));
 }
 
 hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, const VarlenArgs& va,
@@ -1972,16 +2182,20 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
   }
   const int maxC = varlen_max_chunks(a.L, va.nseq);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  int32_t* cu = reinterpret_cast<int32_t*>(ws + (size_t)maxC * ((size_t)a.G * C::REC_BYTES + (size_t)a.H * C::HREC_BYTES));
+  int4* info = reinterpret_cast<int4*>(ws + (size_t)maxC * ((size_t)a.G * C::REC_BYTES + (size_t)a.H * C::HREC_BYTES));
+  bf16* hist = reinterpret_cast<bf16*>(info + maxC);
+  int32_t* cu = reinterpret_cast<int32_t*>(hist + (size_t)maxC * 3 * a.H * SP);
   int32_t* cc = cu + va.nseq + 1;
-  hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(VIDX_THREADS), 0, stream, va.cu, va.nseq, a.L, cu, cc);
-  const VarlenDev vd{cu, cc, va.slots, va.has_init, va.ssm_pool, static_cast<bf16*>(va.conv_pool),
-                     va.nseq, va.npool, maxC};
+  hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(VIDX_THREADS), 0, stream, va.cu, va.nseq, a.L, cu, cc,
+                     info, va.slots, va.has_init, va.npool);
+  const int K = varlen_ranges(va.nseq, a.H);
+  const VarlenDev vd{cu, cc, info, va.slots, va.has_init, va.ssm_pool, static_cast<bf16*>(va.conv_pool),
+                     hist, va.nseq, va.npool, maxC, K};
   hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true, true>), dim3(a.G * maxC), dim3(PREP_THREADS), prep_lds,
                      stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
                      a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, ws, a.L, a.H, a.G, maxC,
                      cv, vd);
-  hipLaunchKernelGGL((ssd_scan64_kernel<true, true>), dim3(va.nseq * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
+  hipLaunchKernelGGL((ssd_scan64_kernel<true, true>), dim3(K * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
                      stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, nullptr, nullptr, static_cast<T*>(a.y), a.y_stride, ws, a.L, a.H, a.G, cv, vd);
   return hipGetLastError();

@@ -282,5 +282,5 @@ def test_varlen_settings_and_workspace():
     d = dims(io=m2.MAMBA2_BF16, batch=5, seqlen=1000, nheads=16, ngroups=8)
     m = 1000 // 64 + 5
     rec = 4096 * 3 + 2 * 128 * 64 * 2
-    assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == m * (8 * rec + 16 * 768) + 8 * 6
+    assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == m * (8 * rec + 16 * 768 + 16 + 384 * 16) + 8 * 6
     assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(dims(io=m2.MAMBA2_F32)) == 0
