@@ -191,6 +191,47 @@ def run_decode(args, torch, m2, si):
     return cfg, sum(times) / n, times[n // 2]
 
 
+def run_decode_tokens(args, torch, m2, si, T=4):
+    """The 9B-shape batch-64 decode with T new tokens per sequence in one call (the state is
+    streamed once for the T tokens), on two alternating state/cache sets like the one-token
+    decode."""
+    import numpy as np
+    cfg = si.CONFIGS[2]
+    p = si.draw_params(cfg)
+    steps = si.draw_decode_steps(cfg, 0, T)
+    tok = {k: np.ascontiguousarray(v.transpose(1, 0, 2)) for k, v in steps.items()}   # [B][T][...]
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    u, z, dt = (dev(tok[k]) for k in ("xbc", "z", "dt_raw"))
+    w, bias, dtb, A, D = (f32(p[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
+    h0 = f32(si.draw_h0(cfg))
+    cs0 = dev(si.draw_conv_state(cfg))
+    states, caches = [h0, h0.clone()], [cs0, cs0.clone()]
+    y = torch.empty((cfg.batch, T, cfg.d_inner), dtype=torch.bfloat16, device="cuda")
+
+    def step(k):
+        m2.mamba2_state_update(u, w, bias, caches[k & 1], dt, dtb, A, D, z, states[k & 1], y,
+                               ngroups=cfg.ngroups)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    n = args.decode_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(n):
+        step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    e = 2
+    B, H, P, G, N, Cc = cfg.batch, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.conv_channels
+    nbytes = B * (2 * H * N * P * 4 + 2 * 3 * Cc * e + T * (Cc * e + 2 * H * P * e + H * e)) + Cc * 5 * 4 + 3 * H * 4
+    return {"tokens_per_call": T, "us": us, "tokens_per_s": B * T / (us * 1e-6),
+            "GB_s": nbytes / (us * 1e-6) / 1e9, "algorithmic_bytes": nbytes,
+            "note": f"9B-shape batch 64, {T} new tokens per sequence in one call"}
+
+
 def run_rmsnorm(args, torch, m2, si, cfg):
     """The group RMSNorm over the prefill's gated output shape (seeded stand-in input). Two
     input/output sets are used in turn (672 MB together), so no step finds its input in the
@@ -427,6 +468,7 @@ def main():
     dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
     rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
     vl_us, vl_lens = run_varlen(args, torch, m2, si, cfg)
+    dec4 = run_decode_tokens(args, torch, m2, si, 4)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -475,7 +517,8 @@ def main():
                    "us_per_step": dec_us, "us_p50": dec_p50, "GB_s": dec_gbs,
                    "hbm_frac": dec_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dby,
                    "tokens_per_s": dcfg.batch / (dec_us * 1e-6),
-                   "traffic": measured_traffic("state_update")},
+                   "traffic": measured_traffic("state_update"),
+                   "tokens4": dec4},
         "wall_s_timed": wall,
     }
     out["kernels"]["group_rmsnorm"] = {

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 5
+#define MAMBA2_ABI_VERSION 6
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -231,18 +231,20 @@ int mamba2_conv_ssd_prefill_varlen(const mamba2_dims* dims, const void* xBC, int
                                    size_t workspace_bytes, void* stream);
 
 /*
- * mamba2_state_update -- one decode token per sequence (dims->seqlen must be
- * 1), updating both caches in place: the conv step above on the token's raw
- * xBC, then one step of the recurrence on the fp32 state.
+ * mamba2_state_update -- decode of T = dims->seqlen new tokens per sequence (1 to 6;
+ * several tokens serve e.g. the check of drafted tokens), updating both caches in
+ * place: for each token in order, the conv step above on its raw xBC, then one step of
+ * the recurrence on the fp32 state. The state is read and written once per call; the
+ * results are bitwise those of T one-token calls.
  *
- *   u_t        [B][Cc] io raw xBC of the new token, Cc = H*P + 2*G*N, dense
+ *   u_t        [B][T][Cc] io raw xBC of the new tokens, Cc = H*P + 2*G*N, dense
  *   w, bias    conv parameters as in mamba2_conv1d ([Cc][W], [Cc] or NULL)
  *   conv_state [B][W-1][Cc] io, updated in place (shifted by one token)
- *   dt_raw_t   [B][H] io, dense
+ *   dt_raw_t   [B][T][H] io, dense
  *   dt_bias, A, D as in mamba2_ssd_prefill (D may be NULL)
- *   z_t        [B][H*P] io or NULL
+ *   z_t        [B][T][H*P] io or NULL
  *   ssm_state  [B][H][N][P] f32, updated in place
- *   y_t        [B][H*P] io; must not overlap any other argument
+ *   y_t        [B][T][H*P] io; must not overlap any other argument
  */
 int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w,
                         const float* bias, void* conv_state, const void* dt_raw_t,
@@ -252,12 +254,13 @@ int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w
 /*
  * mamba2_state_update_slots -- mamba2_state_update for a continuous batch whose caches
  * live in pools (as an inference engine keeps them: neurohive, section
- * "Развертывание"): token b (row b of u_t, dt_raw_t, z_t, y_t) updates entry slots[b]
- * of conv_pool [npool][W-1][Cc] and ssm_pool [npool][H][N][P] in place. A token whose
- * entry is outside [0, npool) is skipped: its y row is written as zeros and no cache is
- * touched. Two tokens must not share an entry (their updates would race).
+ * "Развертывание"): sequence b (rows b T .. b T + T - 1 of u_t, dt_raw_t, z_t, y_t)
+ * updates entry slots[b] of conv_pool [npool][W-1][Cc] and ssm_pool [npool][H][N][P] in
+ * place. A sequence whose entry is outside [0, npool) is skipped: its y rows are written
+ * as zeros and no cache is touched. Two sequences must not share an entry (their updates
+ * would race).
  *
- *   slots  [B] int32 (device), 4-byte aligned; dims->seqlen must be 1
+ *   slots  [B] int32 (device), 4-byte aligned; dims->seqlen = T, 1 to 6 tokens
  *   other arguments as in mamba2_state_update (the pools in place of the caches; they may
  *   be NULL when npool == 0)
  * For an entry in range the results are bitwise those of mamba2_state_update on that

@@ -150,6 +150,24 @@ def state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_sta
     return y, cs, ss
 
 
+def state_update_tokens(u, w, bias, conv_state, dt_raw, dt_bias, A, D, z, ssm_state, *,
+                        nheads: int, ngroups: int):
+    """T decode tokens per sequence, in order: u [B][T][Cc], dt_raw [B][T][H], z [B][T][H*P]
+    or None; state_update applied to one token after the other. Returns
+    (y [B][T][H*P], conv_state', ssm_state')."""
+    u, dt_raw = _d(u), _d(dt_raw)
+    z = None if z is None else _d(z)
+    B, T = u.shape[0], u.shape[1]
+    cs = np.array(conv_state, dtype=np.float64, copy=True)
+    ss = np.array(ssm_state, dtype=np.float64, copy=True)
+    y = np.zeros((B, T, nheads * 64))
+    for t in range(T):
+        y[:, t], cs, ss = state_update(u[:, t], w, bias, cs, dt_raw[:, t], dt_bias, A, D,
+                                       None if z is None else z[:, t], ss, nheads=nheads,
+                                       ngroups=ngroups)
+    return y, cs, ss
+
+
 def group_rmsnorm(g, weight=None, *, ngroups: int, eps: float = 1e-5):
     """Group RMSNorm of the gated output g [..][width]: each row is cut into ngroups
     contiguous groups, each scaled by 1 / sqrt(mean of squares + eps), then by weight."""

@@ -209,11 +209,20 @@ def mamba2_conv_ssd_prefill_varlen(xBC, conv_w, conv_bias, cu_seqlens, slots, ha
         _ptr(z), 0 if z is None else rs(z), _ptr(y), rs(y), _ptr(workspace), ws_bytes, _stream()))
 
 
+def _decode_shape(dt_raw_t):
+    """(B, T, H) of a decode call: dt_raw_t is [B, H] (one token) or [B, T, H]."""
+    if dt_raw_t.dim() == 2:
+        B, H = dt_raw_t.shape
+        return B, 1, H
+    return tuple(dt_raw_t.shape)
+
+
 def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,
                         *, ngroups: int) -> None:
-    """One decode token; conv_state and ssm_state are updated in place."""
-    B, H = dt_raw_t.shape
-    d = make_dims(B, 1, H, ngroups, 64, io_dtype_of(u_t))
+    """Decode of one token ([B, ...] rows) or of T tokens per sequence ([B, T, ...] rows, T up
+    to 6); conv_state and ssm_state are updated in place."""
+    B, T, H = _decode_shape(dt_raw_t)
+    d = make_dims(B, T, H, ngroups, 64, io_dtype_of(u_t))
     _check(lib.mamba2_state_update(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_state),
                                    _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
                                    _ptr(ssm_state), _ptr(y_t), _stream()))
@@ -221,11 +230,12 @@ def mamba2_state_update(u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, 
 
 def mamba2_state_update_slots(u_t, w, bias, conv_pool, dt_raw_t, dt_bias, A, D, z_t, ssm_pool, slots, y_t,
                               *, ngroups: int) -> None:
-    """One decode token per row of u_t; row b updates pool entry slots[b] (int32 [B]) of
-    conv_pool [npool, 3, Cc] and ssm_pool [npool, H, N, P] in place."""
-    B, H = dt_raw_t.shape
+    """Decode over cache pools: sequence b (one token, or T tokens with [B, T, ...] rows)
+    updates pool entry slots[b] (int32 [B]) of conv_pool [npool, 3, Cc] and
+    ssm_pool [npool, H, N, P] in place."""
+    B, T, H = _decode_shape(dt_raw_t)
     npool = 0 if ssm_pool is None else ssm_pool.shape[0]
-    d = make_dims(B, 1, H, ngroups, 64, io_dtype_of(u_t))
+    d = make_dims(B, T, H, ngroups, 64, io_dtype_of(u_t))
     _check(lib.mamba2_state_update_slots(ctypes.byref(d), _ptr(u_t), _ptr(w), _ptr(bias), _ptr(conv_pool),
                                          _ptr(dt_raw_t), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z_t),
                                          _ptr(ssm_pool), _ptr(slots), npool, _ptr(y_t), _stream()))

@@ -64,8 +64,9 @@ struct DecodeArgs {
   float* ssm_state;
   void* y_t;
   int B, H, G;
-  const int32_t* slots = nullptr;   // token -> pool entry, or NULL for entry = token
+  const int32_t* slots = nullptr;   // sequence -> pool entry, or NULL for entry = sequence
   int npool = 0;
+  int T = 1;                        // new tokens per sequence (1 .. 6), rows b T + t
 };
 hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream);
 

@@ -370,7 +370,8 @@ M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const f
                                   const void* z_t, float* ssm_state, void* y_t, void* stream) {
   int st = check_dims(d, true);
   if (st) return st;
-  if (d->seqlen != 1) return fail(MAMBA2_ERR_SHAPE, "state_update needs seqlen 1 (got %d)", d->seqlen);
+  if (d->seqlen < 1 || d->seqlen > 6)
+    return fail(MAMBA2_ERR_SHAPE, "state_update takes 1 to 6 tokens per sequence (seqlen %d)", d->seqlen);
   if (!u_t || !w || !conv_state || !dt_raw_t || !dt_bias || !A || !ssm_state || !y_t)
     return fail(MAMBA2_ERR_NULL, "u_t, w, conv_state, dt_raw_t, dt_bias, A, ssm_state and y_t must not be NULL");
   const int io = d->io_dtype, es = esize_of(io);
@@ -380,18 +381,19 @@ M2_EXPORT int mamba2_state_update(const mamba2_dims* d, const void* u_t, const f
   const void* al[] = {u_t, w, conv_state, ssm_state, y_t, z_t};
   for (const void* p : al)
     if (p && !aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "u_t, w, conv_state, ssm_state, y_t, z_t must be 16-byte aligned");
-  Range ry = span(y_t, B, H * P, H * P, es);
+  const int64_t BT = B * d->seqlen;   // token rows
+  Range ry = span(y_t, BT, H * P, H * P, es);
   Range rcs = span(conv_state, 1, 0, B * 3 * Cc, es), rss = span(ssm_state, 1, 0, B * H * N * P, 4);
-  Range ins[] = {span(u_t, B, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
-                 span(dt_raw_t, B, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
-                 span(D, 1, 0, H, 4),         span(z_t, B, H * P, H * P, es)};
+  Range ins[] = {span(u_t, BT, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
+                 span(dt_raw_t, BT, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
+                 span(D, 1, 0, H, 4),          span(z_t, BT, H * P, H * P, es)};
   for (const Range& r : ins)
     if (overlap(ry, r) || overlap(rcs, r) || overlap(rss, r))
       return fail(MAMBA2_ERR_ALIAS, "y_t, conv_state or ssm_state overlaps an input");
   if (overlap(ry, rcs) || overlap(ry, rss) || overlap(rcs, rss))
     return fail(MAMBA2_ERR_ALIAS, "y_t, conv_state and ssm_state must not overlap");
   m2::DecodeArgs a{u_t, w, bias, conv_state, dt_raw_t, dt_bias, A, D, z_t, ssm_state, y_t,
-                   d->batch, d->nheads, d->ngroups};
+                   d->batch, d->nheads, d->ngroups, nullptr, 0, d->seqlen};
   return hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, static_cast<hipStream_t>(stream)),
                     "state_update launch");
 }
@@ -403,7 +405,8 @@ M2_EXPORT int mamba2_state_update_slots(const mamba2_dims* d, const void* u_t, c
                                         int32_t npool, void* y_t, void* stream) {
   int st = check_dims(d, true);
   if (st) return st;
-  if (d->seqlen != 1) return fail(MAMBA2_ERR_SHAPE, "state_update_slots needs seqlen 1 (got %d)", d->seqlen);
+  if (d->seqlen < 1 || d->seqlen > 6)
+    return fail(MAMBA2_ERR_SHAPE, "state_update_slots takes 1 to 6 tokens per sequence (seqlen %d)", d->seqlen);
   if (!u_t || !w || !dt_raw_t || !dt_bias || !A || !y_t || !slots)
     return fail(MAMBA2_ERR_NULL, "u_t, w, dt_raw_t, dt_bias, A, slots and y_t must not be NULL");
   if (npool < 0) return fail(MAMBA2_ERR_SHAPE, "npool %d < 0", npool);
@@ -417,18 +420,19 @@ M2_EXPORT int mamba2_state_update_slots(const mamba2_dims* d, const void* u_t, c
   for (const void* p : al)
     if (p && !aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "u_t, w, conv_pool, ssm_pool, y_t, z_t must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(slots) & 3u) return fail(MAMBA2_ERR_ALIGN, "slots must be 4-byte aligned");
-  Range ry = span(y_t, B, H * P, H * P, es);
+  const int64_t BT = B * d->seqlen;   // token rows
+  Range ry = span(y_t, BT, H * P, H * P, es);
   Range rcs = span(conv_pool, 1, 0, npool * 3 * Cc, es), rss = span(ssm_pool, 1, 0, npool * H * N * P, 4);
-  Range ins[] = {span(u_t, B, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
-                 span(dt_raw_t, B, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
-                 span(D, 1, 0, H, 4),         span(z_t, B, H * P, H * P, es), span(slots, 1, 0, B, 4)};
+  Range ins[] = {span(u_t, BT, Cc, Cc, es),   span(w, 1, 0, Cc * 4, 4),   span(bias, 1, 0, Cc, 4),
+                 span(dt_raw_t, BT, H, H, es), span(dt_bias, 1, 0, H, 4), span(A, 1, 0, H, 4),
+                 span(D, 1, 0, H, 4),          span(z_t, BT, H * P, H * P, es), span(slots, 1, 0, B, 4)};
   for (const Range& r : ins)
     if (overlap(ry, r) || overlap(rcs, r) || overlap(rss, r))
       return fail(MAMBA2_ERR_ALIAS, "y_t or a pool overlaps an input");
   if (overlap(ry, rcs) || overlap(ry, rss) || overlap(rcs, rss))
     return fail(MAMBA2_ERR_ALIAS, "y_t and the pools must not overlap");
   m2::DecodeArgs a{u_t, w, bias, conv_pool, dt_raw_t, dt_bias, A, D, z_t, ssm_pool, y_t,
-                   d->batch, d->nheads, d->ngroups, slots, npool};
+                   d->batch, d->nheads, d->ngroups, slots, npool, d->seqlen};
   return hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, static_cast<hipStream_t>(stream)),
                     "state_update_slots launch");
 }

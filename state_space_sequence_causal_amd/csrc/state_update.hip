@@ -37,6 +37,8 @@ constexpr int DEC_W = 4;
 constexpr int DEC_K = 1;            // state rows per lane in one work item
 constexpr int DEC_NB = 4;           // item buffers
 constexpr int DEC_IPH = 32 / DEC_K;  // work items per head
+constexpr int DEC_MAX_HPG = 256;     // heads per group the kernel covers (one dt thread each)
+static_assert(DEC_MAX_HPG <= DEC_THREADS, "one thread per head for dt");
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
@@ -57,8 +59,12 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-template <typename T>
-__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+// NT tokens per sequence (1 .. 6; rows b NT + t of u_t, dt_raw_t, z_t, y_t), applied in order: the
+// conv over the extended sequence (cache, tokens), then for each state part NT updates in
+// registers, so the state is read and written once per call. Each token's arithmetic is the
+// one-token step's, so NT tokens give the bits of NT one-token calls.
+template <typename T, int NT>
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 8 : 4, 8)))
 void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
@@ -75,11 +81,13 @@ void state_update_kernel(
   const int Cc = di + 2 * G * DEC_N;
   const int nx = hpg * DEC_P;          // x channels owned
   const int nch = nx + 2 * DEC_N;      // plus B and C of the group
-  float* xs = smem;                    // [nx] conv output of the x channels
-  float* bsm = smem + nx;              // [N]
-  float* csm = bsm + DEC_N;            // [N]
-  float* dts = csm + DEC_N;            // [hpg]
-  float* das = dts + hpg;              // [hpg] decay a = exp(dt A)
+  // per token t: the conv output of x [nx], B [N], C [N] at smem + t nch; then dt and the decay
+  // a = exp(dt A) per (token, head)
+  auto xs = [&](int t) { return smem + t * nch; };
+  auto bsm = [&](int t) { return smem + t * nch + nx; };
+  auto csm = [&](int t) { return smem + t * nch + nx + DEC_N; };
+  float* dts = smem + NT * nch;        // [NT][hpg]
+  float* das = dts + NT * hpg;         // [NT][hpg]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -89,8 +97,10 @@ void state_update_kernel(
   if (slots) {
     sb = slots[b];
     if (sb < 0 || sb >= npool) {
-      for (int i = tid; i < hpg * DEC_P / 4; i += DEC_THREADS)
-        store4(y_t + (int64_t)b * di + g * hpg * DEC_P + 4 * i, 0.f, 0.f, 0.f, 0.f);
+      for (int i = tid; i < NT * hpg * DEC_P / 4; i += DEC_THREADS) {
+        const int t = i / (hpg * DEC_P / 4), k = i % (hpg * DEC_P / 4);
+        store4(y_t + ((int64_t)b * NT + t) * di + g * hpg * DEC_P + 4 * k, 0.f, 0.f, 0.f, 0.f);
+      }
       return;   // the whole workgroup leaves
     }
   }
@@ -127,19 +137,19 @@ void state_update_kernel(
   // for a load also waits for every load issued before it, so the conv, which gates the
   // stream, must not queue behind the state. Each conv thread owns 4 channels.
   constexpr int CV = 4;
-  const T* ub = u_t + (int64_t)b * Cc;
+  const T* ub = u_t + (int64_t)b * NT * Cc;
   T* csb = conv_state + (int64_t)sb * (DEC_W - 1) * Cc;
   const int lc = tid * CV;
   const bool conv_thread = lc < nch;
   const int c = lc < nx ? g * nx + lc
                         : (lc < nx + DEC_N ? di + g * DEC_N + (lc - nx) : di + G * DEC_N + g * DEC_N + (lc - nx - DEC_N));
-  Raw4<T> s0, s1, s2, cur;
+  Raw4<T> e[NT + 3];                   // the extended sequence: 3 cached rows, then the tokens
   f32x4 wv[CV], bv = {0.f, 0.f, 0.f, 0.f};
   if (conv_thread) {
-    s0 = ld4(csb + c);
-    s1 = ld4(csb + Cc + c);
-    s2 = ld4(csb + 2 * Cc + c);
-    cur = ld4(ub + c);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) e[k] = ld4(csb + k * Cc + c);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) e[3 + t] = ld4(ub + t * Cc + c);
 #pragma unroll
     for (int i = 0; i < CV; ++i) wv[i] = *reinterpret_cast<const f32x4*>(w + (int64_t)(c + i) * DEC_W);
     if (bias) {
@@ -147,11 +157,12 @@ void state_update_kernel(
       for (int i = 0; i < CV; ++i) bv[i] = bias[c + i];
     }
   }
-  float dtr = 0.f, dtb = 0.f, av = 0.f;
+  float dtr[NT], dtb = 0.f, av = 0.f;
   const bool dt_thread = tid < hpg;
   if (dt_thread) {
     const int h = g * hpg + tid;
-    dtr = to_f(dt_raw_t[(int64_t)b * H + h]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dtr[t] = to_f(dt_raw_t[((int64_t)b * NT + t) * H + h]);
     dtb = dt_bias[h];
     av = A[h];
   }
@@ -160,52 +171,67 @@ void state_update_kernel(
 #pragma unroll
     for (int k = 0; k < DEC_NB - 1; ++k) load_item(k, buf[k]);
   }
-  // conv step on the owned channels; the cache shifts by one token
+  // conv steps on the owned channels; the cache shifts by NT tokens
   if (conv_thread) {
 #pragma unroll
-    for (int i = 0; i < CV; ++i) smem[lc + i] = conv4_silu(wv[i], bv[i], s0.get(i), s1.get(i), s2.get(i), cur.get(i));
-    *reinterpret_cast<decltype(s1.v)*>(csb + c) = s1.v;
-    *reinterpret_cast<decltype(s2.v)*>(csb + Cc + c) = s2.v;
-    *reinterpret_cast<decltype(cur.v)*>(csb + 2 * Cc + c) = cur.v;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < CV; ++i)
+        smem[t * nch + lc + i] = conv4_silu(wv[i], bv[i], e[t].get(i), e[t + 1].get(i), e[t + 2].get(i),
+                                            e[t + 3].get(i));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
   }
   // groups wider than DEC_THREADS * CV channels: the rest, plainly
   for (int l2 = lc + DEC_THREADS * CV; l2 < nch; l2 += DEC_THREADS * CV) {
     const int c2 = l2 < nx ? g * nx + l2
                            : (l2 < nx + DEC_N ? di + g * DEC_N + (l2 - nx) : di + G * DEC_N + g * DEC_N + (l2 - nx - DEC_N));
-    const Raw4<T> a0 = ld4(csb + c2), a1 = ld4(csb + Cc + c2), a2 = ld4(csb + 2 * Cc + c2), a3 = ld4(ub + c2);
+    Raw4<T> a[NT + 3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a[k] = ld4(csb + k * Cc + c2);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) a[3 + t] = ld4(ub + t * Cc + c2);
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
       const f32x4 wq = *reinterpret_cast<const f32x4*>(w + (int64_t)(c2 + i) * DEC_W);
-      smem[l2 + i] = conv4_silu(wq, bias ? bias[c2 + i] : 0.f, a0.get(i), a1.get(i), a2.get(i), a3.get(i));
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        smem[t * nch + l2 + i] = conv4_silu(wq, bias ? bias[c2 + i] : 0.f, a[t].get(i), a[t + 1].get(i),
+                                            a[t + 2].get(i), a[t + 3].get(i));
     }
-    *reinterpret_cast<decltype(a1.v)*>(csb + c2) = a1.v;
-    *reinterpret_cast<decltype(a2.v)*>(csb + Cc + c2) = a2.v;
-    *reinterpret_cast<decltype(a3.v)*>(csb + 2 * Cc + c2) = a3.v;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(a[0].v)*>(csb + k * Cc + c2) = a[NT + k].v;
   }
-  for (int j = DEC_THREADS + tid; j < hpg; j += DEC_THREADS) {   // more heads than threads
-    const int h = g * hpg + j;
-    const float dt = softplus_f(to_f(dt_raw_t[(int64_t)b * H + h]) + dt_bias[h]);
-    dts[j] = dt;
-    das[j] = expf(dt * A[h]);
-  }
+  // dt and the decay per (token, head), one thread per head: the C ABI allows at most 256 heads
+  // per group, fewer than the workgroup's threads
   if (dt_thread) {
-    const float dt = softplus_f(dtr + dtb);
-    dts[tid] = dt;
-    das[tid] = expf(dt * av);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float dt = softplus_f(dtr[t] + dtb);
+      dts[t * hpg + tid] = dt;
+      das[t * hpg + tid] = expf(dt * av);
+    }
   }
   __syncthreads();
 
   // stream the heads: per part, request part it + DEC_NB - 1, then update part it in place
+  // (NT times, one token after the other)
   const T* zsrc = z_t ? z_t : u_t;     // without z a valid row is read and not used
   for (int hj = 0; hj < nheads_w; ++hj) {
     const int j = wave + DEC_WAVES * hj;
     const int h = g * hpg + j;
-    const float a = das[j], dt = dts[j];
-    const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs + j * DEC_P + 4 * q);
-    const f32x4 dx = dt * x4;
-    f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
-    // the gate's z is requested now and used after the head's stream, so its latency is hidden
-    const f32x4 zz = load4(zsrc + (int64_t)b * (z_t ? di : Cc) + h * DEC_P + 4 * q);
+    float a[NT];
+    f32x4 dx[NT], yacc[NT];
+    Raw4<T> zz[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      a[t] = das[t * hpg + j];
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs(t) + j * DEC_P + 4 * q);
+      dx[t] = dts[t * hpg + j] * x4;
+      yacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      // the gate's z is requested now and used after the head's stream, so its latency is hidden
+      zz[t] = ld4(zsrc + ((int64_t)b * NT + t) * (z_t ? di : Cc) + h * DEC_P + 4 * q);
+    }
     const float dh = D ? D[h] : 0.f;
 #pragma unroll 1
     for (int m0 = 0; m0 < DEC_IPH; m0 += DEC_NB) {
@@ -216,51 +242,84 @@ void state_update_kernel(
       load_item(it + DEC_NB - 1, buf[(mm + DEC_NB - 1) % DEC_NB]);
       // keep the request here: the scheduler would otherwise sink it below the update
       __builtin_amdgcn_sched_barrier(0);
-      const f32x4 (&hv)[DEC_K] = buf[mm];
       float* st = item_ptr(it);
       const int n0 = 4 * DEC_K * m + rg;
 #pragma unroll
       for (int k = 0; k < DEC_K; ++k) {
-        const float bn = bsm[n0 + 4 * k], cn = csm[n0 + 4 * k];
-        f32x4 nv;
-        nv[0] = a * hv[k][0] + bn * dx[0];
-        nv[1] = a * hv[k][1] + bn * dx[1];
-        nv[2] = a * hv[k][2] + bn * dx[2];
-        nv[3] = a * hv[k][3] + bn * dx[3];
-        yacc[0] += cn * nv[0];
-        yacc[1] += cn * nv[1];
-        yacc[2] += cn * nv[2];
-        yacc[3] += cn * nv[3];
-        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(st + 4 * k * DEC_P));
+        if constexpr (NT == 1) {
+          // one token: the update on the loaded part itself. In the loop form below, with one
+          // token, the compiler drops the store's non-temporal hint and the stream is ~10%
+          // slower; the arithmetic is the same
+          const f32x4 (&hv1)[DEC_K] = buf[mm];
+          const float bn = bsm(0)[n0 + 4 * k], cn = csm(0)[n0 + 4 * k];
+          const f32x4 nv = __builtin_elementwise_fma((f32x4)a[0], hv1[k], bn * dx[0]);
+          yacc[0] = __builtin_elementwise_fma((f32x4)cn, nv, yacc[0]);
+          __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(st + 4 * k * DEC_P));
+          continue;
+        }
+        f32x4 hv = buf[mm][k];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float bn = bsm(t)[n0 + 4 * k], cn = csm(t)[n0 + 4 * k];
+          // the same fma order as the one-token path, so T tokens give the bits of T calls
+          const f32x4 nv = __builtin_elementwise_fma((f32x4)a[t], hv, bn * dx[t]);
+          yacc[t] = __builtin_elementwise_fma((f32x4)cn, nv, yacc[t]);
+          // stored from inside the loop: a store of the loop-carried value after it loses its
+          // non-temporal hint in the compiler
+          if (t == NT - 1) __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(st + 4 * k * DEC_P));
+          hv = nv;
+        }
       }
     }
     }
-    // head done: reduce y over the four row groups (every lane ends with the sum), add the
-    // skip term, gate, store (the four row groups write the same values)
+    // head done: per token, reduce y over the four row groups (every lane ends with the sum),
+    // add the skip term, gate, store (the four row groups write the same values)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      yacc[i] += __shfl_xor(yacc[i], 16);
-      yacc[i] += __shfl_xor(yacc[i], 32);
-    }
-    f32x4 o = yacc + dh * x4;
-    if (z_t) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz[i]);
+      for (int i = 0; i < 4; ++i) {
+        yacc[t][i] += __shfl_xor(yacc[t][i], 16);
+        yacc[t][i] += __shfl_xor(yacc[t][i], 32);
+      }
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs(t) + j * DEC_P + 4 * q);
+      f32x4 o = yacc[t] + dh * x4;
+      if (z_t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz[t].get(i));
+      }
+      store4(y_t + ((int64_t)b * NT + t) * di + h * DEC_P + 4 * q, o[0], o[1], o[2], o[3]);
     }
-    store4(y_t + (int64_t)b * di + h * DEC_P + 4 * q, o[0], o[1], o[2], o[3]);
   }
 }
 
-template <typename T>
-static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int NT>
+static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int hpg = a.H / a.G;
-  size_t lds = sizeof(float) * (size_t)(hpg * DEC_P + 2 * DEC_N + 2 * hpg);
-  hipLaunchKernelGGL((state_update_kernel<T>), dim3(a.B * a.G), dim3(DEC_THREADS), lds, stream,
+  const size_t lds = sizeof(float) * ((size_t)NT * (hpg * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpg);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_update_kernel<T, NT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((state_update_kernel<T, NT>), dim3(a.B * a.G), dim3(DEC_THREADS), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
                      a.npool);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.T) {
+    case 1: return launch_nt<T, 1>(a, stream);
+    case 2: return launch_nt<T, 2>(a, stream);
+    case 3: return launch_nt<T, 3>(a, stream);
+    case 4: return launch_nt<T, 4>(a, stream);
+    case 5: return launch_nt<T, 5>(a, stream);
+    case 6: return launch_nt<T, 6>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream) {

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 5
+    assert m2.mamba2_abi_version() == 6
 
 
 def dims(**kw):
@@ -130,9 +130,15 @@ def test_decode_rejects(kw, code):
     assert decode(dims(seqlen=1), **kw) == code, m2.mamba2_last_error()
 
 
-def test_decode_needs_one_token():
-    assert decode(dims(seqlen=2)) == ESHAPE
+def test_decode_token_count():
+    """1 to 6 new tokens per sequence."""
+    assert decode(dims(seqlen=0)) == ESHAPE
+    assert decode(dims(seqlen=7)) == ESHAPE
     assert decode(dims(seqlen=1, nheads=512, ngroups=1)) == EUNSUP
+    # the token rows count in the overlap checks: y right after 2 rows of u_t overlaps at T = 3
+    d = dims(seqlen=3, batch=1)
+    cc = d.nheads * 64 + 2 * d.ngroups * 128
+    assert decode(d, y=BASE + 2 * cc * 4) == EALIAS
 
 
 def test_workspace_size_formula():
@@ -249,8 +255,9 @@ def test_decode_slots_rejects(kw, code):
     assert decode_slots(dims(seqlen=1, batch=3), **kw) == code, m2.mamba2_last_error()
 
 
-def test_decode_slots_needs_one_token():
-    assert decode_slots(dims(seqlen=2)) == ESHAPE
+def test_decode_slots_token_count():
+    assert decode_slots(dims(seqlen=0)) == ESHAPE
+    assert decode_slots(dims(seqlen=7)) == ESHAPE
 
 
 # ------------------------------------------------------------------ packed prefill
