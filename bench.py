@@ -345,13 +345,15 @@ def cpu_baseline(cfg, inp):
 def counter_kernels(chunk: int) -> dict:
     """traffic entry -> (mangled) kernel-name fragments summed per call, for the bf16 prefill
     at chunk length ``chunk``"""
-    scan = {64: ("ssd_scan64_kernelILb0E", "ssd_scan64_kernel<false>", "ssd_scan64_kernel#1"),
+    scan = {64: ("ssd_scan64_kernelILb0ELb0E", "ssd_scan64_kernel<false, false>", "ssd_scan64_kernel#1"),
             256: "ssd_scan_wide_kernelIDF16bLi256E"}.get(chunk, f"ssd_scan_kernelIDF16bLi{chunk}E")
-    return {"conv_ssd_prefill": ["ssd_prep_kernelIDF16bLi64ELb1E",
-                                 ("ssd_scan64_kernelILb1E", "ssd_scan64_kernel<true>", "ssd_scan64_kernel#0")],
-            "ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}ELb0E", scan],
+    return {"conv_ssd_prefill": ["ssd_prep_kernelIDF16bLi64ELb1ELb0E",
+                                 ("ssd_scan64_kernelILb1ELb0E", "ssd_scan64_kernel<true, false>",
+                                  "ssd_scan64_kernel#0")],
+            "ssd_prefill": [f"ssd_prep_kernelIDF16bLi{chunk}ELb0ELb0E", scan],
             "conv1d": ["conv1d_kernel"],
-            "state_update": ["state_update_kernel"],
+            "state_update": [("state_update_kernelIDF16bLi1E", "state_update_kernel<__hip_bfloat16, 1>",
+                              "state_update_kernel")],
             "group_rmsnorm": ["group_rmsnorm_kernel"]}
 
 
@@ -397,7 +399,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, chunk: int) -> dict:
 
     def pick(table, frag):
         alts = frag if isinstance(frag, tuple) else (frag,)   # mangled or demangled name
-        hits = [v for k, v in table.items() if any(a in k for a in alts)]
+        hits = [v for k, v in table.items() if k in alts] or \
+            [v for k, v in table.items() if any(a in k for a in alts)]
         if len(hits) != 1:
             raise SystemExit(f"expected one kernel matching {frag!r}, found {len(hits)}: "
                              f"{sorted(table)}")
