@@ -261,6 +261,92 @@ def run_rmsnorm(args, torch, m2, si, cfg):
     return us, nbytes
 
 
+def _mixer_inputs(torch, si, cfg, d_model, hidden):
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    p, w = si.draw_params(cfg), si.draw_mixer_weights(cfg, d_model)
+    return dict(hid=dev(hidden), w_in=dev(w["w_in"]), w_out=dev(w["w_out"]), norm_w=f32(w["norm_w"]),
+                **{k: f32(p[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D")})
+
+
+def mixer_flops(cfg, d_model: int, rows: int) -> float:
+    """The two projections' multiply-adds (2 flops each) per call."""
+    E = cfg.d_inner + cfg.conv_channels + cfg.nheads
+    return 2.0 * rows * d_model * (E + cfg.d_inner)
+
+
+def run_mixer_prefill(args, torch, m2, si, cfg, d_model: int = 5120):
+    """mamba2_mixer_prefill over the 12B-shape workload: hidden [1][8192][5120] (the 12B
+    model's hidden width), in-projection to z | xBC | dt_raw (22,688 features), the layer
+    core, the group RMSNorm and the out-projection back to 5120."""
+    t = _mixer_inputs(torch, si, cfg, d_model, si.draw_hidden(cfg, d_model))
+    cs = torch.zeros((cfg.batch, 3, cfg.conv_channels), dtype=torch.bfloat16, device="cuda")
+    hf = torch.empty((cfg.batch, cfg.nheads, cfg.dstate, cfg.headdim), dtype=torch.float32, device="cuda")
+    out = torch.empty((cfg.batch, cfg.seqlen, d_model), dtype=torch.bfloat16, device="cuda")
+    d = m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, 64, m2.MAMBA2_BF16)
+    ws = torch.empty(m2.mamba2_mixer_prefill_workspace_bytes(d, d_model), dtype=torch.uint8, device="cuda")
+
+    def step():
+        m2.mamba2_mixer_prefill(t["hid"], t["w_in"], t["conv_w"], t["conv_b"], cs, t["dt_bias"], t["A"], t["D"],
+                                None, hf, t["norm_w"], t["w_out"], out, ngroups=cfg.ngroups, chunk=64,
+                                workspace=ws)
+
+    n = max(1, args.steps // 4)
+    for _ in range(max(1, args.warmup // 10)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    rows = cfg.batch * cfg.seqlen
+    gf = mixer_flops(cfg, d_model, rows)
+    return {"us": us, "tokens_per_s": rows / (us * 1e-6), "d_model": d_model, "calls_timed": n,
+            "projection_GFLOP": gf / 1e9, "projection_TFLOP_s_over_whole_call": gf / (us * 1e-6) / 1e12,
+            "note": "the mixer around the step: in-projection (hipBLASLt), the step's layer core, "
+                    "group RMSNorm, out-projection (hipBLASLt); random-init weights"}
+
+
+def run_mixer_step(args, torch, m2, si, d_model: int = 4480):
+    """mamba2_mixer_step at the 9B decode shape: batch 64, one token, hidden width 4480 (the
+    pruned 9B model's), on two alternating cache sets like the decode step."""
+    cfg = si.CONFIGS[2]
+    t = _mixer_inputs(torch, si, cfg, d_model, si.draw_hidden(cfg, d_model, step=0))
+    h0 = torch.from_numpy(si.draw_h0(cfg)).cuda()
+    cs0 = torch.from_numpy(si.bf16_bits(si.draw_conv_state(cfg)).view("int16")).view(torch.bfloat16).cuda()
+    states, caches = [h0, h0.clone()], [cs0, cs0.clone()]
+    out = torch.empty((cfg.batch, 1, d_model), dtype=torch.bfloat16, device="cuda")
+    d = m2.make_dims(cfg.batch, 1, cfg.nheads, cfg.ngroups, 64, m2.MAMBA2_BF16)
+    ws = torch.empty(m2.mamba2_mixer_step_workspace_bytes(d, d_model), dtype=torch.uint8, device="cuda")
+
+    def step(k):
+        m2.mamba2_mixer_step(t["hid"], t["w_in"], t["conv_w"], t["conv_b"], caches[k & 1], t["dt_bias"], t["A"],
+                             t["D"], states[k & 1], t["norm_w"], t["w_out"], out, ngroups=cfg.ngroups,
+                             workspace=ws)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    n = args.decode_steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(n):
+        step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    E = cfg.d_inner + cfg.conv_channels + cfg.nheads
+    wbytes = 2 * d_model * (E + cfg.d_inner)
+    return {"us": us, "tokens_per_s": cfg.batch / (us * 1e-6), "d_model": d_model,
+            "weight_bytes": wbytes, "state_bytes": decode_bytes(cfg),
+            "GB_s_weights_and_state": (wbytes + decode_bytes(cfg)) / (us * 1e-6) / 1e9,
+            "note": "9B-shape batch 64, one token: in-projection, state update, group RMSNorm, "
+                    "out-projection; random-init weights"}
+
+
 def run_varlen(args, torch, m2, si, cfg):
     """The one-call prefill over a packed continuous batch at the 12B shape: 16 sequences of
     seeded log-uniform lengths summing to the workload's 8192 tokens, half of them continuing
@@ -472,6 +558,8 @@ def main():
     rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
     vl_us, vl_lens = run_varlen(args, torch, m2, si, cfg)
     dec4 = run_decode_tokens(args, torch, m2, si, 4)
+    mix_pre = run_mixer_prefill(args, torch, m2, si, cfg)
+    mix_step = run_mixer_step(args, torch, m2, si)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -522,6 +610,7 @@ def main():
                    "tokens_per_s": dcfg.batch / (dec_us * 1e-6),
                    "traffic": measured_traffic("state_update"),
                    "tokens4": dec4},
+        "mixer": {"prefill_12b_8k": mix_pre, "step_9b_b64": mix_step},
         "wall_s_timed": wall,
     }
     out["kernels"]["group_rmsnorm"] = {

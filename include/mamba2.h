@@ -23,7 +23,8 @@
  *    A, D) and SSM states are float32 in every mode.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *    null stream). Nothing synchronizes, nothing is allocated, no state is kept
- *    between calls. The caller owns every buffer and the stream.
+ *    between calls (the mixer calls' hipBLASLt handle aside: see there). The
+ *    caller owns every buffer and the stream.
  *  - Validation runs on the host before anything is enqueued. On failure the
  *    call returns a nonzero status, enqueues nothing and leaves every buffer
  *    untouched; mamba2_last_error() describes the failure. Launch failures
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 6
+#define MAMBA2_ABI_VERSION 7
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -292,6 +293,70 @@ int mamba2_state_update_slots(const mamba2_dims* dims, const void* u_t, const fl
 int mamba2_group_rmsnorm(const mamba2_dims* dims, const void* g, int64_t g_stride,
                          const float* weight, float eps, void* out, int64_t out_stride,
                          void* stream);
+
+/*
+ * The Mamba-2 mixer around the layer core: the pages' layer with its bias-free input and
+ * output projections and its RMSNorm (hyper.ai summary, section "方法"; neurohive,
+ * section "Архитектура": hidden width 5120 for the 12B model, 4480 after pruning to 9B,
+ * expansion 2, no bias in the linear layers, RMSNorm normalisation). Per token row:
+ *
+ *   [z | xBC | dt_raw] = hidden * w_in^T          E = 2 H P + 2 G N + H features
+ *   out_core           = the layer core on (xBC, dt_raw, z), as mamba2_conv_ssd_prefill
+ *                        (prefill) or mamba2_state_update (step) computes it
+ *   y_n                = mamba2_group_rmsnorm(out_core, norm_w, eps) over ngroups groups
+ *   out                = y_n * w_out^T
+ *
+ *   hidden  [rows][d_model] io, row stride hidden_stride (rows = batch * seqlen; for the
+ *           step, row b * seqlen + t is token t of sequence b)
+ *   w_in    [E][d_model] io dense: rows 0 .. HP-1 give z, the next Cc give xBC (x, B, C),
+ *           the last H give dt_raw (HP = nheads * 64, Cc = HP + 2 * ngroups * 128)
+ *   conv_w, conv_bias, dt_bias, A, D: the layer core's parameters
+ *   norm_w  [HP] f32 or NULL (= ones); eps >= 0
+ *   w_out   [d_model][HP] io dense
+ *   out     [rows][d_model] io, row stride out_stride
+ * d_model: a positive multiple of 8 (bf16) or 4 (f32) elements, at most 2^20.
+ *
+ * The projections are hipBLASLt GEMMs with fp32 accumulation. The projected rows
+ * [rows][Es] (Es = E rounded up to a multiple of 8), the core's output [rows][HP] and the
+ * normalised output [rows][HP] are stored in io precision at the start of the workspace,
+ * in that order, each at a 256-byte boundary, and stay there after the call. The first mixer call on a
+ * device creates that device's hipBLASLt handle, and each new GEMM shape runs hipBLASLt's
+ * algorithm heuristic once; the handle and the chosen algorithms are kept until the
+ * process ends. No tensor memory is allocated. MAMBA2_ERR_UNSUPPORTED when hipBLASLt has
+ * no algorithm for a shape; other hipBLASLt failures return MAMBA2_ERR_HIP.
+ * out, the workspace and the updated caches must not overlap each other or an input.
+ */
+
+/* mamba2_mixer_prefill_workspace_bytes -- device workspace of mamba2_mixer_prefill for
+ * `dims` and d_model, 0 if they are invalid:
+ *   a256(rows * Es * e) + 2 * a256(rows * HP * e) + a256(W) + 32 MiB
+ * with e the io size, Es = E rounded up to a multiple of 8, W the workspace of
+ * mamba2_conv_ssd_prefill for `dims`, a256 rounding up to 256 bytes. */
+size_t mamba2_mixer_prefill_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
+
+/* mamba2_mixer_prefill -- the mixer over batch sequences of seqlen tokens: the layer core
+ * is mamba2_conv_ssd_prefill (same dims, chunk and io settings; conv_state, h0 and h_final
+ * as there). seqlen 0 only carries h0 into h_final. */
+int mamba2_mixer_prefill(const mamba2_dims* dims, int32_t d_model, const void* hidden,
+                         int64_t hidden_stride, const void* w_in, const float* conv_w,
+                         const float* conv_bias, void* conv_state, const float* dt_bias,
+                         const float* A, const float* D, const float* h0, float* h_final,
+                         const float* norm_w, float eps, const void* w_out, void* out,
+                         int64_t out_stride, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* mamba2_mixer_step_workspace_bytes -- device workspace of mamba2_mixer_step, 0 if `dims`
+ * or d_model is invalid: a256(rows * Es * e) + 2 * a256(rows * HP * e) + 32 MiB. */
+size_t mamba2_mixer_step_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
+
+/* mamba2_mixer_step -- the mixer for dims->seqlen = 1 .. 6 new tokens per sequence: the
+ * layer core is mamba2_state_update (conv_state and ssm_state updated in place). */
+int mamba2_mixer_step(const mamba2_dims* dims, int32_t d_model, const void* hidden,
+                      int64_t hidden_stride, const void* w_in, const float* conv_w,
+                      const float* conv_bias, void* conv_state, const float* dt_bias,
+                      const float* A, const float* D, float* ssm_state, const float* norm_w,
+                      float eps, const void* w_out, void* out, int64_t out_stride,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Description of the last failure on the calling thread ("" after success). */
 const char* mamba2_last_error(void);

@@ -241,3 +241,55 @@ def conv_ssd_prefill_varlen(xbc, cu_seqlens, slots, has_init, conv_pool, ssm_poo
             conv_pool[s] = hist_new[0]
             ssm_pool[s] = hf[0]
     return y, conv_pool, ssm_pool
+
+
+def _project(rows, w):
+    """rows [..][K] times w[N][K] transposed, in fp64 (numpy matmul)."""
+    rows, w = _d(rows), _d(w)
+    return (rows.reshape(-1, rows.shape[-1]) @ w.T).reshape(rows.shape[:-1] + (w.shape[0],))
+
+
+def _split_projected(zx, nheads: int, ngroups: int):
+    """The in-projection's columns in the order z | xBC | dt_raw."""
+    di = nheads * 64
+    Cc = di + 2 * ngroups * 128
+    return zx[..., :di], zx[..., di:di + Cc], zx[..., di + Cc:di + Cc + nheads]
+
+
+def mixer_prefill(hidden, w_in, conv_w, conv_b, conv_state, dt_bias, A, D, h0, norm_w, w_out, *,
+                  nheads: int, ngroups: int, eps: float = 1e-5, io: str = "f32"):
+    """The Mamba-2 mixer around the layer core: the Nemotron-Nano-2 layer with its bias-free
+    linear layers and RMSNorm (hyper.ai summary, section "方法"; neurohive, section
+    "Архитектура"). For hidden [B][L][d_model]:
+
+    1. zx = hidden w_in^T (fp64 matmul), whose columns are z | xBC | dt_raw;
+    2. conv1d on xBC from conv_state, then ssd_scan gated by SiLU(z) from h0;
+    3. group_rmsnorm of the gated output over ngroups groups with norm_w;
+    4. out = (normalised output) w_out^T.
+
+    With io "bf16" every value the library keeps in bf16 between the steps (zx, the conv
+    output, the gated output, the normalised output) is rounded with round_bf16 first.
+    Returns (out [B][L][d_model], conv_state' [B][3][Cc], h_final [B][H][N][P])."""
+    r = round_bf16 if io == "bf16" else (lambda a: a)
+    zx = r(_project(hidden, w_in))
+    z, xbc, dt_raw = _split_projected(zx, nheads, ngroups)
+    xr, hist = conv1d(xbc, conv_w, conv_b, conv_state)
+    x, Bm, Cm = split_xbc(r(xr), nheads, ngroups)
+    y, hf = ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D, z, h0, ngroups=ngroups)
+    yn = r(group_rmsnorm(r(y), norm_w, ngroups=ngroups, eps=eps))
+    return _project(yn, w_out), hist, hf
+
+
+def mixer_step(hidden, w_in, conv_w, conv_b, conv_state, dt_bias, A, D, ssm_state, norm_w, w_out, *,
+               nheads: int, ngroups: int, eps: float = 1e-5, io: str = "f32"):
+    """The mixer for T new tokens per sequence, hidden [B][T][d_model]: as mixer_prefill with
+    state_update_tokens as the layer core (its conv output is not stored in between, so with
+    io "bf16" only zx, the gated output and the normalised output are rounded).
+    Returns (out [B][T][d_model], conv_state', ssm_state')."""
+    r = round_bf16 if io == "bf16" else (lambda a: a)
+    zx = r(_project(hidden, w_in))
+    z, xbc, dt_raw = _split_projected(zx, nheads, ngroups)
+    y, cs, ss = state_update_tokens(xbc, conv_w, conv_b, conv_state, dt_raw, dt_bias, A, D, z, ssm_state,
+                                    nheads=nheads, ngroups=ngroups)
+    yn = r(group_rmsnorm(r(y), norm_w, ngroups=ngroups, eps=eps))
+    return _project(yn, w_out), cs, ss

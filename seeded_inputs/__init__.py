@@ -29,7 +29,7 @@ __all__ = [
     "Config", "CONFIGS", "config", "bf16_round", "bf16_bits", "bits_to_f32",
     "draw_params", "draw_xbc", "draw_z", "draw_dt_raw", "draw_h0",
     "draw_conv_state", "draw_prefill", "draw_decode_step", "draw_decode_steps", "TOKEN_BLOCK",
-    "draw_gated", "draw_norm_weight",
+    "draw_gated", "draw_norm_weight", "draw_hidden", "draw_mixer_weights", "mixer_features",
 ]
 
 TOKEN_BLOCK = 256  # tokens per independently seeded block
@@ -38,6 +38,7 @@ TOKEN_BLOCK = 256  # tokens per independently seeded block
 _T_ALOG, _T_DTB, _T_D, _T_CW, _T_CB, _T_XBC, _T_Z, _T_DT, _T_H0, _T_CS = range(10)
 _T_GATED, _T_NW = 10, 11
 _T_LEN, _T_SLOT, _T_INIT = 12, 13, 14
+_T_HID, _T_WIN, _T_WOUT = 15, 16, 17
 
 
 @dataclasses.dataclass(frozen=True)
@@ -337,3 +338,49 @@ def draw_pools(cfg: Config, npool: int) -> tuple:
     precision) and fp32 states [npool][H][N][P] ~ N(0, 0.1^2)."""
     c = dataclasses.replace(cfg, batch=npool, h0_std=cfg.h0_std or 0.1)
     return draw_conv_state(c), draw_h0(c)
+
+
+# ----------------------------------------------------------------------------- the mixer
+def mixer_features(cfg: Config) -> int:
+    """Rows of the in-projection weight: z (d_inner), xBC (Cc), dt_raw (nheads)."""
+    return cfg.d_inner + cfg.conv_channels + cfg.nheads
+
+
+def draw_hidden(cfg: Config, d_model: int, t0: int = 0, t1: Optional[int] = None,
+                step: int = -1) -> np.ndarray:
+    """Mixer input rows [B][t1-t0][d_model] ~ N(0, 1) (the output of the layer's RMSNorm has
+    unit mean square), rounded to the config's I/O type. Decode steps use step >= 0."""
+    t0, t1, stream = _span(cfg, t0, t1, step)
+    return _tokens(cfg, _T_HID, d_model, t0, t1, _normal_fill, stream, cfg.io)
+
+
+def _weight_rows(cfg: Config, tid: int, rows: int, cols: int, scale: np.ndarray) -> np.ndarray:
+    """A [rows][cols] N(0, 1) matrix, row r scaled by scale[r], drawn in 1024-row blocks with
+    their own streams (on a thread pool), rounded to the config's I/O type."""
+    out = np.empty((rows, cols), dtype=np.float32)
+    blk = 1024
+
+    def one(k):
+        r0, r1 = k * blk, min(rows, (k + 1) * blk)
+        a = _rng(cfg.seed, tid, cols, k).standard_normal((r1 - r0, cols), dtype=np.float32)
+        out[r0:r1] = _io(a * scale[r0:r1, None], cfg.io)
+
+    nb = (rows + blk - 1) // blk
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(nb)))
+    return out
+
+
+def draw_mixer_weights(cfg: Config, d_model: int) -> Dict[str, np.ndarray]:
+    """Random-init projection weights of the mixer, in io precision, scaled so that the
+    projected features have the distributions the layer core's recipe draws directly:
+    w_in [E][d_model] ~ N(0, 1/d_model), with the B and C rows further scaled by
+    1/sqrt(d_state) (so z, x and dt_raw come out ~ N(0, 1) and B, C ~ N(0, 1)/sqrt(N));
+    w_out [d_model][d_inner] ~ N(0, 1/d_inner); the norm weight as draw_norm_weight."""
+    di, gn = cfg.d_inner, cfg.ngroups * cfg.dstate
+    E = mixer_features(cfg)
+    s_in = np.full(E, 1.0 / math.sqrt(d_model), dtype=np.float32)
+    s_in[2 * di:2 * di + 2 * gn] /= np.float32(math.sqrt(cfg.dstate))
+    w_in = _weight_rows(cfg, _T_WIN, E, d_model, s_in)
+    w_out = _weight_rows(cfg, _T_WOUT, d_model, di, np.full(d_model, 1.0 / math.sqrt(di), dtype=np.float32))
+    return {"w_in": w_in, "w_out": w_out, "norm_w": draw_norm_weight(cfg)}

@@ -21,7 +21,8 @@ __all__ = [
     "mamba2_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill",
     "mamba2_conv_ssd_prefill_workspace_bytes", "mamba2_conv_ssd_prefill_varlen",
     "mamba2_conv_ssd_prefill_varlen_workspace_bytes", "mamba2_group_rmsnorm",
-    "mamba2_state_update_slots",
+    "mamba2_state_update_slots", "mamba2_mixer_prefill", "mamba2_mixer_prefill_workspace_bytes",
+    "mamba2_mixer_step", "mamba2_mixer_step_workspace_bytes",
     "mamba2_abi_version", "mamba2_last_error",
     "MAMBA2_F32", "MAMBA2_BF16", "STATUS",
 ]
@@ -76,8 +77,17 @@ lib.mamba2_state_update.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _v
 lib.mamba2_state_update_slots.argtypes = [_dims, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _i32, _vp, _vp]
 lib.mamba2_group_rmsnorm.argtypes = [_dims, _vp, _i64, _vp, ctypes.c_float, _vp, _i64, _vp]
+lib.mamba2_mixer_prefill_workspace_bytes.argtypes = [_dims, _i32]
+lib.mamba2_mixer_prefill_workspace_bytes.restype = _sz
+lib.mamba2_mixer_prefill.argtypes = [_dims, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_float, _vp, _vp, _i64, _vp, _sz, _vp]
+lib.mamba2_mixer_step_workspace_bytes.argtypes = [_dims, _i32]
+lib.mamba2_mixer_step_workspace_bytes.restype = _sz
+lib.mamba2_mixer_step.argtypes = [_dims, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_float, _vp, _vp, _i64, _vp, _sz, _vp]
 for _f in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_varlen",
-           "mamba2_state_update", "mamba2_state_update_slots", "mamba2_group_rmsnorm"):
+           "mamba2_state_update", "mamba2_state_update_slots", "mamba2_group_rmsnorm", "mamba2_mixer_prefill",
+           "mamba2_mixer_step"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -255,3 +265,52 @@ def mamba2_group_rmsnorm(g, weight, out, *, ngroups: int, eps: float = 1e-5) -> 
     d = make_dims(B, L, W // 64, ngroups, 64, io_dtype_of(g))
     _check(lib.mamba2_group_rmsnorm(ctypes.byref(d), _ptr(g), gs, _ptr(weight), float(eps), _ptr(out),
                                     os_, _stream()))
+
+
+def _workspace(need: int, like):
+    import torch
+    return torch.empty(need, dtype=torch.uint8, device=like.device)
+
+
+def mamba2_mixer_prefill_workspace_bytes(d: Dims, d_model: int) -> int:
+    return lib.mamba2_mixer_prefill_workspace_bytes(ctypes.byref(d), int(d_model))
+
+
+def mamba2_mixer_prefill(hidden, w_in, conv_w, conv_bias, conv_state, dt_bias, A, D, h0, h_final, norm_w,
+                         w_out, out, *, ngroups: int, chunk: int, eps: float = 1e-5, workspace=None) -> None:
+    """The Mamba-2 mixer over hidden [B, L, d_model]: in-projection (w_in [E, d_model]),
+    the layer core as mamba2_conv_ssd_prefill, group RMSNorm (norm_w [H*P] or None),
+    out-projection (w_out [d_model, H*P]) into out [B, L, d_model]."""
+    B, L, DM = hidden.shape
+    H = dt_bias.shape[0]
+    d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(hidden))
+    if workspace is None:
+        workspace = _workspace(lib.mamba2_mixer_prefill_workspace_bytes(ctypes.byref(d), DM), hidden)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.mamba2_mixer_prefill(
+        ctypes.byref(d), DM, _ptr(hidden), _row_stride(hidden), _ptr(w_in), _ptr(conv_w), _ptr(conv_bias),
+        _ptr(conv_state), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(h0), _ptr(h_final), _ptr(norm_w), float(eps),
+        _ptr(w_out), _ptr(out), _row_stride(out), _ptr(workspace), ws_bytes, _stream()))
+
+
+def mamba2_mixer_step_workspace_bytes(d: Dims, d_model: int) -> int:
+    return lib.mamba2_mixer_step_workspace_bytes(ctypes.byref(d), int(d_model))
+
+
+def mamba2_mixer_step(hidden, w_in, conv_w, conv_bias, conv_state, dt_bias, A, D, ssm_state, norm_w, w_out,
+                      out, *, ngroups: int, eps: float = 1e-5, workspace=None) -> None:
+    """The mixer for T = 1 .. 6 new tokens per sequence: hidden and out [B, T, d_model] (or
+    [B, d_model] for one token); the layer core is mamba2_state_update, conv_state and
+    ssm_state are updated in place."""
+    if hidden.dim() == 2:
+        hidden, out = hidden.unsqueeze(1), out.unsqueeze(1)
+    B, T, DM = hidden.shape
+    H = dt_bias.shape[0]
+    d = make_dims(B, T, H, ngroups, 64, io_dtype_of(hidden))
+    if workspace is None:
+        workspace = _workspace(lib.mamba2_mixer_step_workspace_bytes(ctypes.byref(d), DM), hidden)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.mamba2_mixer_step(
+        ctypes.byref(d), DM, _ptr(hidden), _row_stride(hidden), _ptr(w_in), _ptr(conv_w), _ptr(conv_bias),
+        _ptr(conv_state), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(ssm_state), _ptr(norm_w), float(eps),
+        _ptr(w_out), _ptr(out), _row_stride(out), _ptr(workspace), ws_bytes, _stream()))

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmamba2.so")
-SOURCES = ["conv1d.hip", "ssd_prefill.hip", "state_update.hip", "rmsnorm.hip", "mamba2_api.cpp"]
+SOURCES = ["conv1d.hip", "ssd_prefill.hip", "state_update.hip", "rmsnorm.hip", "gemm.cpp", "mamba2_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -44,10 +44,10 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    # NEEDED libamdhip64.so.7 binds to whichever HIP runtime of that soname the
-    # process already holds (PyTorch's, when the binding imports torch first).
+    # NEEDED libamdhip64.so.7 and libhipblaslt.so.1 bind to whichever libraries of those
+    # sonames the process already holds (PyTorch's, when the binding imports torch first).
     cmd = ["/opt/rocm/llvm/bin/clang++", "-shared", "-fPIC", "-o", tmp, *objs,
-           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+           "-L/opt/rocm/lib", "-lamdhip64", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -1,0 +1,136 @@
+// The mixer's two projections as hipBLASLt GEMMs. They are plain dense products with no
+// fused epilogue, the case the vendor library already runs near the MFMA roofline, so no
+// hand-written kernel replaces them here.
+//
+// Row-major C[M][N] (row stride ldc) = A[M][K] (row stride lda) * W[N][K]^T, with W dense
+// (the [out][in] weight of a bias-free linear layer), io elements and fp32 accumulation.
+// In hipBLASLt's column-major terms this is C^T = op_T(W^T) * A^T: A^T is K x M with
+// leading dimension lda, W^T is K x N with leading dimension K, C^T is N x M with ldc.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace m2 {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct AlgoKey {
+  int io_bf16;
+  int64_t M, N, K, lda, ldc;
+  size_t ws;
+  bool operator==(const AlgoKey& o) const {
+    return io_bf16 == o.io_bf16 && M == o.M && N == o.N && K == o.K && lda == o.lda && ldc == o.ldc &&
+           ws == o.ws;
+  }
+};
+struct DeviceLt {
+  hipblasLtHandle_t handle = nullptr;
+  std::vector<std::pair<AlgoKey, hipblasLtMatmulAlgo_t>> algos;   // heuristic picks, per shape
+};
+std::mutex g_mu;
+DeviceLt g_dev[kMaxDevices];
+
+struct Descs {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+  ~Descs() {
+    if (a) hipblasLtMatrixLayoutDestroy(a);
+    if (b) hipblasLtMatrixLayoutDestroy(b);
+    if (c) hipblasLtMatrixLayoutDestroy(c);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
+};
+
+int lt_fail(std::string* err, const char* what, hipblasStatus_t s) {
+  char buf[160];
+  snprintf(buf, sizeof buf, "hipBLASLt %s: status %d", what, (int)s);
+  *err = buf;
+  return GEMM_ERR_LIB;
+}
+
+}  // namespace
+
+int gemm_nt(int io_bf16, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* W,
+            void* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t stream, std::string* err) {
+  if (M == 0 || N == 0) return GEMM_OK;
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = "hipGetDevice failed or device index out of range";
+    return GEMM_ERR_LIB;
+  }
+  const hipDataType t = io_bf16 ? HIP_R_16BF : HIP_R_32F;
+  Descs d;
+  hipblasStatus_t s = hipblasLtMatmulDescCreate(&d.op, HIPBLAS_COMPUTE_32F, HIP_R_32F);
+  if (s != HIPBLAS_STATUS_SUCCESS) return lt_fail(err, "matmul descriptor", s);
+  const int32_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+  if ((s = hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof opT)) ||
+      (s = hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof opN)))
+    return lt_fail(err, "transpose attributes", s);
+  if ((s = hipblasLtMatrixLayoutCreate(&d.a, t, K, N, K)) || (s = hipblasLtMatrixLayoutCreate(&d.b, t, K, M, lda)) ||
+      (s = hipblasLtMatrixLayoutCreate(&d.c, t, N, M, ldc)))
+    return lt_fail(err, "matrix layouts", s);
+
+  hipblasLtHandle_t h;
+  hipblasLtMatmulAlgo_t algo;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceLt& dl = g_dev[dev];
+    if (!dl.handle && (s = hipblasLtCreate(&dl.handle)) != HIPBLAS_STATUS_SUCCESS) {
+      dl.handle = nullptr;
+      return lt_fail(err, "handle creation", s);
+    }
+    h = dl.handle;
+    const AlgoKey key{io_bf16, M, N, K, lda, ldc, ws_bytes};
+    bool found = false;
+    for (auto& e : dl.algos)
+      if (e.first == key) {
+        algo = e.second;
+        found = true;
+        break;
+      }
+    if (!found) {
+      hipblasLtMatmulPreference_t pref = nullptr;
+      if ((s = hipblasLtMatmulPreferenceCreate(&pref))) return lt_fail(err, "preference", s);
+      const uint64_t cap = ws_bytes;
+      s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap, sizeof cap);
+      // the heuristic's candidates in its order of preference; the first that fits the
+      // workspace is kept
+      constexpr int kCand = 8;
+      hipblasLtMatmulHeuristicResult_t res[kCand];
+      int n = 0;
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulAlgoGetHeuristic(h, d.op, d.a, d.b, d.c, d.c, pref, kCand, res, &n);
+      hipblasLtMatmulPreferenceDestroy(pref);
+      if (s != HIPBLAS_STATUS_SUCCESS) return lt_fail(err, "algorithm heuristic", s);
+      int pick = -1;
+      for (int i = 0; i < n && pick < 0; ++i)
+        if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) pick = i;
+      if (pick < 0) {
+        char buf[240];
+        snprintf(buf, sizeof buf,
+                 "hipBLASLt has no algorithm for %s M=%lld N=%lld K=%lld within %zu workspace bytes "
+                 "(%d candidates, first needs %zu)",
+                 io_bf16 ? "bf16" : "f32", (long long)M, (long long)N, (long long)K, ws_bytes, n,
+                 n > 0 ? res[0].workspaceSize : (size_t)0);
+        *err = buf;
+        return GEMM_ERR_NO_ALGO;
+      }
+      algo = res[pick].algo;
+      dl.algos.emplace_back(key, algo);
+    }
+  }
+  const float one = 1.f, zero = 0.f;
+  s = hipblasLtMatmul(h, d.op, &one, W, d.a, A, d.b, &zero, C, d.c, C, d.c, &algo, ws, ws_bytes, stream);
+  if (s != HIPBLAS_STATUS_SUCCESS) return lt_fail(err, "matmul", s);
+  return GEMM_OK;
+}
+
+}  // namespace m2

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace m2 {
 
 hipError_t launch_conv1d(int io_bf16, const void* u, int64_t u_stride, const float* w,
@@ -22,6 +24,7 @@ struct PrefillArgs {
   void* y; int64_t y_stride;
   void* workspace;
   int B, L, H, G;
+  int64_t dt_stride = 0;   // row stride of dt_raw in elements; 0: dense (H)
 };
 hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream);
 // The conv fused into the prefill (bf16, chunk 64): x, Bm and Cm of `a` are the raw xBC
@@ -67,6 +70,8 @@ struct DecodeArgs {
   const int32_t* slots = nullptr;   // sequence -> pool entry, or NULL for entry = sequence
   int npool = 0;
   int T = 1;                        // new tokens per sequence (1 .. 6), rows b T + t
+  // row strides (elements) of u_t, z_t and dt_raw_t; 0: dense (Cc, H * 64, H)
+  int64_t u_stride = 0, z_stride = 0, dt_stride = 0;
 };
 hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t stream);
 
@@ -74,5 +79,13 @@ hipError_t launch_state_update(int io_bf16, const DecodeArgs& a, hipStream_t str
 hipError_t launch_group_rmsnorm(int io_bf16, const void* g, int64_t g_stride, const float* weight,
                                 float eps, void* out, int64_t out_stride, int64_t rows, int G,
                                 int width, hipStream_t stream);
+
+// Row-major C[M][N] (row stride ldc) = A[M][K] (row stride lda) * W[N][K]^T with W dense,
+// io elements, fp32 accumulation, on hipBLASLt. ws / ws_bytes: device workspace the
+// library may use. The first call on a device creates that device's hipBLASLt handle and
+// each new shape runs the algorithm heuristic once; both are kept until the process ends.
+enum { GEMM_OK = 0, GEMM_ERR_LIB = 1, GEMM_ERR_NO_ALGO = 2 };
+int gemm_nt(int io_bf16, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* W,
+            void* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t stream, std::string* err);
 
 }  // namespace m2

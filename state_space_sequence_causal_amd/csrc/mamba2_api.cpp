@@ -201,6 +201,39 @@ size_t conv_prefill_ws(const mamba2_dims* d, size_t* scan_part) {
   const int64_t Cc = (int64_t)d->nheads * d->headdim + 2LL * d->ngroups * d->dstate;
   return align256(ws) + (size_t)d->batch * d->seqlen * Cc * esize_of(d->io_dtype);
 }
+
+// The launches of mamba2_conv_ssd_prefill after validation; dt_stride 0 means dense dt_raw.
+int run_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stride, const float* conv_w,
+                         const float* conv_bias, void* conv_state, const void* dt_raw, int64_t dt_stride,
+                         const float* dt_bias, const float* A, const float* D, const void* z, int64_t z_stride,
+                         const float* h0, float* h_final, void* y, int64_t y_stride, void* workspace,
+                         hipStream_t s) {
+  const int io = d->io_dtype, es = esize_of(io);
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
+  const int64_t HP = H * P, Cc = HP + 2 * G * N;
+  size_t ws_scan = 0;
+  conv_prefill_ws(d, &ws_scan);
+  const char* cx = static_cast<const char*>(xBC);
+  if (conv_fused(d) || d->seqlen == 0) {
+    m2::PrefillArgs a{xBC, xbc_stride, cx ? cx + HP * es : nullptr, xbc_stride,
+                      cx ? cx + (HP + G * N) * es : nullptr, xbc_stride, dt_raw, dt_bias, A, D,
+                      z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
+                      d->nheads, d->ngroups, dt_stride};
+    if (d->seqlen == 0)   // nothing to convolve; the history is unchanged, h_final gets h0
+      return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
+    m2::ConvArgs cv{conv_w, conv_bias, conv_state, (int)Cc};
+    return hip_status(m2::launch_ssd_prefill_conv(a, cv, s), "conv_ssd_prefill launch");
+  }
+  // the conv into the workspace's tail, then the prefill from there
+  char* tail = static_cast<char*>(workspace) + align256(ws_scan);
+  hipError_t e = m2::launch_conv1d(io == MAMBA2_BF16, xBC, xbc_stride, conv_w, conv_bias, conv_state,
+                                   tail, Cc, d->batch, d->seqlen, (int)Cc, s);
+  if (e != hipSuccess) return hip_status(e, "conv_ssd_prefill conv launch");
+  m2::PrefillArgs a{tail, Cc, tail + HP * es, Cc, tail + (HP + G * N) * es, Cc, dt_raw, dt_bias, A, D,
+                    z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
+                    d->nheads, d->ngroups, dt_stride};
+  return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
+}
 }  // namespace
 
 M2_EXPORT size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
@@ -267,27 +300,8 @@ M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int
   if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
     return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const char* cx = static_cast<const char*>(xBC);
-  if (conv_fused(d) || d->seqlen == 0) {
-    m2::PrefillArgs a{xBC, xbc_stride, cx ? cx + HP * es : nullptr, xbc_stride,
-                      cx ? cx + (HP + G * N) * es : nullptr, xbc_stride, dt_raw, dt_bias, A, D,
-                      z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
-                      d->nheads, d->ngroups};
-    if (d->seqlen == 0)   // nothing to convolve; the history is unchanged, h_final gets h0
-      return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
-    m2::ConvArgs cv{conv_w, conv_bias, conv_state, (int)Cc};
-    return hip_status(m2::launch_ssd_prefill_conv(a, cv, s), "conv_ssd_prefill launch");
-  }
-  // the conv into the workspace's tail, then the prefill from there
-  char* tail = static_cast<char*>(workspace) + align256(ws_scan);
-  hipError_t e = m2::launch_conv1d(io == MAMBA2_BF16, xBC, xbc_stride, conv_w, conv_bias, conv_state,
-                                   tail, Cc, d->batch, d->seqlen, (int)Cc, s);
-  if (e != hipSuccess) return hip_status(e, "conv_ssd_prefill conv launch");
-  m2::PrefillArgs a{tail, Cc, tail + HP * es, Cc, tail + (HP + G * N) * es, Cc, dt_raw, dt_bias, A, D,
-                    z, z_stride, h0, h_final, y, y_stride, workspace, d->batch, d->seqlen,
-                    d->nheads, d->ngroups};
-  return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
+  return run_conv_ssd_prefill(d, xBC, xbc_stride, conv_w, conv_bias, conv_state, dt_raw, 0, dt_bias, A, D, z,
+                              z_stride, h0, h_final, y, y_stride, workspace, static_cast<hipStream_t>(stream));
 }
 
 namespace {
@@ -458,4 +472,202 @@ M2_EXPORT int mamba2_group_rmsnorm(const mamba2_dims* d, const void* g, int64_t 
   return hip_status(m2::launch_group_rmsnorm(io == MAMBA2_BF16, g, g_stride, weight, eps, out, out_stride,
                                              rows, d->ngroups, (int)width, static_cast<hipStream_t>(stream)),
                     "group_rmsnorm launch");
+}
+
+// ------------------------------------------------------------------------------ the mixer
+namespace {
+constexpr size_t kGemmWs = (size_t)32 << 20;   // hipBLASLt workspace of the mixer calls
+
+// Workspace of the mixer calls: the projected rows [z | xBC | dt_raw] (E features, row
+// stride Es, a multiple of 8 elements), the layer core's output y, the normalised output,
+// the core's own workspace (prefill only) and the GEMM workspace, each at a 256-byte
+// boundary. Every stage's result stays in place after the call.
+struct MixerLayout {
+  int64_t E = 0, Es = 0;
+  size_t y_off = 0, n_off = 0, core_off = 0, gemm_off = 0, total = 0;
+};
+MixerLayout mixer_layout(const mamba2_dims* d, bool prefill) {
+  MixerLayout l;
+  const int64_t H = d->nheads, HP = H * d->headdim, Cc = HP + 2LL * d->ngroups * d->dstate;
+  const int64_t rows = (int64_t)d->batch * d->seqlen;
+  const size_t es = esize_of(d->io_dtype);
+  l.E = HP + Cc + H;
+  l.Es = (l.E + 7) & ~(int64_t)7;
+  l.y_off = align256((size_t)rows * l.Es * es);
+  l.n_off = l.y_off + align256((size_t)rows * HP * es);
+  l.core_off = l.n_off + align256((size_t)rows * HP * es);
+  l.gemm_off = l.core_off + align256(prefill ? conv_prefill_ws(d, nullptr) : 0);
+  l.total = l.gemm_off + kGemmWs;
+  return l;
+}
+
+int check_model_width(int32_t d_model, int io) {
+  const int ve = 16 / esize_of(io);
+  if (d_model < 1 || d_model % ve || d_model > (1 << 20))
+    return fail(MAMBA2_ERR_SHAPE, "d_model %d must be a positive multiple of %d up to 2^20", d_model, ve);
+  return MAMBA2_OK;
+}
+
+int gemm_status(int g, const std::string& msg) {
+  if (g == m2::GEMM_OK) return ok();
+  return fail(g == m2::GEMM_ERR_NO_ALGO ? MAMBA2_ERR_UNSUPPORTED : MAMBA2_ERR_HIP, "%s", msg.c_str());
+}
+}  // namespace
+
+M2_EXPORT size_t mamba2_mixer_prefill_workspace_bytes(const mamba2_dims* d, int32_t d_model) {
+  if (check_dims(d, true) != MAMBA2_OK || !chunk_supported(d) ||
+      check_model_width(d_model, d->io_dtype) != MAMBA2_OK)
+    return 0;
+  return mixer_layout(d, true).total;
+}
+
+M2_EXPORT int mamba2_mixer_prefill(const mamba2_dims* d, int32_t d_model, const void* hidden,
+                                   int64_t hidden_stride, const void* w_in, const float* conv_w,
+                                   const float* conv_bias, void* conv_state, const float* dt_bias,
+                                   const float* A, const float* D, const float* h0, float* h_final,
+                                   const float* norm_w, float eps, const void* w_out, void* out,
+                                   int64_t out_stride, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  const int io = d->io_dtype, es = esize_of(io);
+  if (!chunk_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
+                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+  if ((st = check_model_width(d_model, io))) return st;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return fail(MAMBA2_ERR_SHAPE, "eps must be finite and >= 0");
+  if (!w_in || !w_out || !conv_w || !dt_bias || !A)
+    return fail(MAMBA2_ERR_NULL, "w_in, w_out, conv_w, dt_bias and A must not be NULL");
+  if (d->seqlen > 0 && (!hidden || !out))
+    return fail(MAMBA2_ERR_NULL, "hidden and out must not be NULL when seqlen > 0");
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, DM = d_model;
+  const int64_t HP = H * P, Cc = HP + 2 * G * N, BL = (int64_t)d->batch * d->seqlen;
+  if (Cc > (int64_t)1 << 24) return fail(MAMBA2_ERR_SHAPE, "too many xBC channels");
+  if (d->seqlen > 0) {
+    if ((st = check_stride("hidden", hidden, hidden_stride, DM, io))) return st;
+    if ((st = check_stride("out", out, out_stride, DM, io))) return st;
+  }
+  if (!aligned16(conv_w) || (conv_state && !aligned16(conv_state)) || (h0 && !aligned16(h0)) ||
+      (h_final && !aligned16(h_final)) || (norm_w && !aligned16(norm_w)))
+    return fail(MAMBA2_ERR_ALIGN, "conv_w, conv_state, h0, h_final and norm_w must be 16-byte aligned");
+  const MixerLayout lay = mixer_layout(d, true);
+  if (lay.Es > kMaxStride) return fail(MAMBA2_ERR_SHAPE, "too many projected features");
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned16(workspace)) return fail(MAMBA2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const int64_t state_elems = (int64_t)d->batch * H * N * P;
+  Range rout = span(out, BL, out_stride, DM, es), rws = span(workspace, 1, 0, (int64_t)lay.total, 1);
+  Range rcs = span(conv_state, 1, 0, (int64_t)d->batch * 3 * Cc, es);
+  Range rh0 = span(h0, 1, 0, state_elems, 4), rhf = span(h_final, 1, 0, state_elems, 4);
+  Range ins[] = {span(hidden, BL, hidden_stride, DM, es), span(w_in, 1, 0, (HP + Cc + H) * DM, es),
+                 span(w_out, 1, 0, DM * HP, es),          span(conv_w, 1, 0, Cc * 4, 4),
+                 span(conv_bias, 1, 0, Cc, 4),            span(dt_bias, 1, 0, H, 4),
+                 span(A, 1, 0, H, 4),                     span(D, 1, 0, H, 4),
+                 span(norm_w, 1, 0, HP, 4)};
+  for (const Range& r : ins)
+    for (const Range& o : {rout, rws, rcs, rhf})
+      if (overlap(o, r)) return fail(MAMBA2_ERR_ALIAS, "out, workspace, conv_state or h_final overlaps an input");
+  const Range outs[] = {rout, rws, rcs, rhf};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(MAMBA2_ERR_ALIAS, "out, workspace, conv_state and h_final must not overlap");
+  for (const Range& r : {rout, rws, rcs})
+    if (overlap(r, rh0)) return fail(MAMBA2_ERR_ALIAS, "out, workspace or conv_state overlaps h0");
+  if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
+    return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  char* zx = ws;                       // [BL][Es]: z | xBC | dt_raw
+  char* yb = ws + lay.y_off;           // [BL][HP]: the layer core's gated output
+  char* yn = ws + lay.n_off;           // [BL][HP]: its group RMSNorm
+  std::string err;
+  if (BL > 0) {
+    st = gemm_status(m2::gemm_nt(io == MAMBA2_BF16, BL, lay.E, DM, hidden, hidden_stride, w_in, zx, lay.Es,
+                                 ws + lay.gemm_off, kGemmWs, s, &err), err);
+    if (st) return st;
+  }
+  st = run_conv_ssd_prefill(d, BL ? zx + HP * es : nullptr, lay.Es, conv_w, conv_bias, conv_state,
+                            BL ? zx + (HP + Cc) * es : nullptr, lay.Es, dt_bias, A, D, BL ? zx : nullptr, lay.Es,
+                            h0, h_final, BL ? yb : nullptr, HP, ws + lay.core_off, s);
+  if (st || BL == 0) return st;
+  if ((st = hip_status(m2::launch_group_rmsnorm(io == MAMBA2_BF16, yb, HP, norm_w, eps, yn, HP, BL,
+                                                d->ngroups, (int)HP, s),
+                       "mixer norm launch")))
+    return st;
+  return gemm_status(m2::gemm_nt(io == MAMBA2_BF16, BL, DM, HP, yn, HP, w_out, out, out_stride,
+                                 ws + lay.gemm_off, kGemmWs, s, &err), err);
+}
+
+M2_EXPORT size_t mamba2_mixer_step_workspace_bytes(const mamba2_dims* d, int32_t d_model) {
+  if (check_dims(d, true) != MAMBA2_OK || d->seqlen < 1 || d->seqlen > 6 ||
+      check_model_width(d_model, d->io_dtype) != MAMBA2_OK)
+    return 0;
+  return mixer_layout(d, false).total;
+}
+
+M2_EXPORT int mamba2_mixer_step(const mamba2_dims* d, int32_t d_model, const void* hidden,
+                                int64_t hidden_stride, const void* w_in, const float* conv_w,
+                                const float* conv_bias, void* conv_state, const float* dt_bias,
+                                const float* A, const float* D, float* ssm_state, const float* norm_w,
+                                float eps, const void* w_out, void* out, int64_t out_stride,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d, true);
+  if (st) return st;
+  if (d->seqlen < 1 || d->seqlen > 6)
+    return fail(MAMBA2_ERR_SHAPE, "mixer_step takes 1 to 6 tokens per sequence (seqlen %d)", d->seqlen);
+  const int io = d->io_dtype, es = esize_of(io);
+  if ((st = check_model_width(d_model, io))) return st;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return fail(MAMBA2_ERR_SHAPE, "eps must be finite and >= 0");
+  if (!hidden || !w_in || !w_out || !conv_w || !conv_state || !dt_bias || !A || !ssm_state || !out)
+    return fail(MAMBA2_ERR_NULL,
+                "hidden, w_in, w_out, conv_w, conv_state, dt_bias, A, ssm_state and out must not be NULL");
+  const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate, DM = d_model;
+  if (H / G > 256) return fail(MAMBA2_ERR_UNSUPPORTED, "more than 256 heads per group");
+  const int64_t HP = H * P, Cc = HP + 2 * G * N, BT = (int64_t)d->batch * d->seqlen;
+  if ((st = check_stride("hidden", hidden, hidden_stride, DM, io))) return st;
+  if ((st = check_stride("out", out, out_stride, DM, io))) return st;
+  if (!aligned16(conv_w) || !aligned16(conv_state) || !aligned16(ssm_state) || (norm_w && !aligned16(norm_w)))
+    return fail(MAMBA2_ERR_ALIGN, "conv_w, conv_state, ssm_state and norm_w must be 16-byte aligned");
+  const MixerLayout lay = mixer_layout(d, false);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned16(workspace)) return fail(MAMBA2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  Range rout = span(out, BT, out_stride, DM, es), rws = span(workspace, 1, 0, (int64_t)lay.total, 1);
+  Range rcs = span(conv_state, 1, 0, (int64_t)d->batch * 3 * Cc, es);
+  Range rss = span(ssm_state, 1, 0, (int64_t)d->batch * H * N * P, 4);
+  Range ins[] = {span(hidden, BT, hidden_stride, DM, es), span(w_in, 1, 0, (HP + Cc + H) * DM, es),
+                 span(w_out, 1, 0, DM * HP, es),          span(conv_w, 1, 0, Cc * 4, 4),
+                 span(conv_bias, 1, 0, Cc, 4),            span(dt_bias, 1, 0, H, 4),
+                 span(A, 1, 0, H, 4),                     span(D, 1, 0, H, 4),
+                 span(norm_w, 1, 0, HP, 4)};
+  const Range outs[] = {rout, rws, rcs, rss};
+  for (const Range& r : ins)
+    for (const Range& o : outs)
+      if (overlap(o, r)) return fail(MAMBA2_ERR_ALIAS, "out, workspace, conv_state or ssm_state overlaps an input");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(MAMBA2_ERR_ALIAS, "out, workspace, conv_state and ssm_state must not overlap");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  char* zx = ws;
+  char* yb = ws + lay.y_off;
+  char* yn = ws + lay.n_off;
+  std::string err;
+  st = gemm_status(m2::gemm_nt(io == MAMBA2_BF16, BT, lay.E, DM, hidden, hidden_stride, w_in, zx, lay.Es,
+                               ws + lay.gemm_off, kGemmWs, s, &err), err);
+  if (st) return st;
+  m2::DecodeArgs a{zx + HP * es, conv_w, conv_bias, conv_state, zx + (HP + Cc) * es, dt_bias, A, D, zx,
+                   ssm_state, yb, d->batch, d->nheads, d->ngroups, nullptr, 0, d->seqlen};
+  a.u_stride = a.z_stride = a.dt_stride = lay.Es;
+  if ((st = hip_status(m2::launch_state_update(io == MAMBA2_BF16, a, s), "mixer state_update launch"))) return st;
+  if ((st = hip_status(m2::launch_group_rmsnorm(io == MAMBA2_BF16, yb, HP, norm_w, eps, yn, HP, BT,
+                                                d->ngroups, (int)HP, s),
+                       "mixer norm launch")))
+    return st;
+  return gemm_status(m2::gemm_nt(io == MAMBA2_BF16, BT, DM, HP, yn, HP, w_out, out, out_stride,
+                                 ws + lay.gemm_off, kGemmWs, s, &err), err);
 }

@@ -209,7 +209,7 @@ template <typename T, int Q, bool CONV, bool VARLEN = false>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void ssd_prep_kernel(
     const T* __restrict__ Bm, int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
     const T* __restrict__ dt_raw, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv, VarlenDev vd) {
+    int64_t dt_stride, unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv, VarlenDev vd) {
   static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
   using C = Cfg<T, Q>;
   constexpr int VE = C::VE;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
       for (int u = 0; u < DB; ++u) {
         const int item = i0 + u * (PREP_THREADS / 64);
         const int j = item / C::TPL, s = 64 * (item % C::TPL) + lane;
-        raw[u] = item < nitems && s < nvalid ? to_f(dt_raw[(row0 + s) * H + g * hpg + j]) : 0.f;
+        raw[u] = item < nitems && s < nvalid ? to_f(dt_raw[(row0 + s) * dt_stride + g * hpg + j]) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < DB; ++u) {
@@ -2055,6 +2055,9 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 }
 
 // ---------------------------------------------------------------------------- host side
+// row stride of dt_raw in elements: dense [rows][H] unless the caller gave one
+static int64_t dt_stride(const PrefillArgs& a) { return a.dt_stride > 0 ? a.dt_stride : a.H; }
+
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
@@ -2094,7 +2097,7 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
   if (nC > 0) {
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, false>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
+                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{}, VarlenDev{});
   }
   if constexpr (PIPE64) {
@@ -2127,7 +2130,7 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
   if (nC > 0) {
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A,
+                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv, VarlenDev{});
   }
   hipLaunchKernelGGL((ssd_scan64_kernel<true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
@@ -2193,7 +2196,7 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
                      hist, va.nseq, va.npool, maxC, K};
   hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true, true>), dim3(a.G * maxC), dim3(PREP_THREADS), prep_lds,
                      stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                     a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, ws, a.L, a.H, a.G, maxC,
+                     a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a), ws, a.L, a.H, a.G, maxC,
                      cv, vd);
   hipLaunchKernelGGL((ssd_scan64_kernel<true, true>), dim3(K * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
                      stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),

@@ -59,7 +59,8 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
   return (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
-// NT tokens per sequence (1 .. 6; rows b NT + t of u_t, dt_raw_t, z_t, y_t), applied in order: the
+// NT tokens per sequence (1 .. 6; rows b NT + t of u_t, dt_raw_t, z_t, y_t, with row strides us,
+// dtrs, zs in elements; y_t is dense), applied in order: the
 // conv over the extended sequence (cache, tokens), then for each state part NT updates in
 // registers, so the state is read and written once per call. Each token's arithmetic is the
 // one-token step's, so NT tokens give the bits of NT one-token calls.
@@ -70,7 +71,7 @@ void state_update_kernel(
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
     const float* __restrict__ A, const float* __restrict__ D, const T* __restrict__ z_t,
     float* __restrict__ ssm_state, T* __restrict__ y_t, int H, int G, const int32_t* __restrict__ slots,
-    int npool) {
+    int npool, int64_t us, int64_t zs, int64_t dtrs) {
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
   const int hpg = H / G;
@@ -137,7 +138,7 @@ void state_update_kernel(
   // for a load also waits for every load issued before it, so the conv, which gates the
   // stream, must not queue behind the state. Each conv thread owns 4 channels.
   constexpr int CV = 4;
-  const T* ub = u_t + (int64_t)b * NT * Cc;
+  const T* ub = u_t + (int64_t)b * NT * us;
   T* csb = conv_state + (int64_t)sb * (DEC_W - 1) * Cc;
   const int lc = tid * CV;
   const bool conv_thread = lc < nch;
@@ -149,7 +150,7 @@ void state_update_kernel(
 #pragma unroll
     for (int k = 0; k < 3; ++k) e[k] = ld4(csb + k * Cc + c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) e[3 + t] = ld4(ub + t * Cc + c);
+    for (int t = 0; t < NT; ++t) e[3 + t] = ld4(ub + t * us + c);
 #pragma unroll
     for (int i = 0; i < CV; ++i) wv[i] = *reinterpret_cast<const f32x4*>(w + (int64_t)(c + i) * DEC_W);
     if (bias) {
@@ -162,7 +163,7 @@ void state_update_kernel(
   if (dt_thread) {
     const int h = g * hpg + tid;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) dtr[t] = to_f(dt_raw_t[((int64_t)b * NT + t) * H + h]);
+    for (int t = 0; t < NT; ++t) dtr[t] = to_f(dt_raw_t[((int64_t)b * NT + t) * dtrs + h]);
     dtb = dt_bias[h];
     av = A[h];
   }
@@ -190,7 +191,7 @@ void state_update_kernel(
 #pragma unroll
     for (int k = 0; k < 3; ++k) a[k] = ld4(csb + k * Cc + c2);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) a[3 + t] = ld4(ub + t * Cc + c2);
+    for (int t = 0; t < NT; ++t) a[3 + t] = ld4(ub + t * us + c2);
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
       const f32x4 wq = *reinterpret_cast<const f32x4*>(w + (int64_t)(c2 + i) * DEC_W);
@@ -230,7 +231,7 @@ void state_update_kernel(
       dx[t] = dts[t * hpg + j] * x4;
       yacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
       // the gate's z is requested now and used after the head's stream, so its latency is hidden
-      zz[t] = ld4(zsrc + ((int64_t)b * NT + t) * (z_t ? di : Cc) + h * DEC_P + 4 * q);
+      zz[t] = ld4(zsrc + ((int64_t)b * NT + t) * (z_t ? zs : us) + h * DEC_P + 4 * q);
     }
     const float dh = D ? D[h] : 0.f;
 #pragma unroll 1
@@ -305,7 +306,8 @@ static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
-                     a.npool);
+                     a.npool, a.u_stride > 0 ? a.u_stride : (int64_t)a.H * DEC_P + 2 * a.G * DEC_N,
+                     a.z_stride > 0 ? a.z_stride : (int64_t)a.H * DEC_P, a.dt_stride > 0 ? a.dt_stride : a.H);
   return hipGetLastError();
 }
 

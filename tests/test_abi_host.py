@@ -28,7 +28,9 @@ def test_header_declares_the_calls():
     for n in ("mamba2_conv1d", "mamba2_ssd_prefill", "mamba2_state_update", "mamba2_group_rmsnorm",
               "mamba2_conv_ssd_prefill", "mamba2_conv_ssd_prefill_workspace_bytes",
               "mamba2_conv_ssd_prefill_varlen", "mamba2_state_update_slots",
-              "mamba2_ssd_prefill_workspace_bytes", "mamba2_last_error", "mamba2_abi_version"):
+              "mamba2_ssd_prefill_workspace_bytes", "mamba2_mixer_prefill", "mamba2_mixer_step",
+              "mamba2_mixer_prefill_workspace_bytes", "mamba2_mixer_step_workspace_bytes",
+              "mamba2_last_error", "mamba2_abi_version"):
         assert n in names
 
 
@@ -39,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 6
+    assert m2.mamba2_abi_version() == 7
 
 
 def dims(**kw):
@@ -291,3 +293,61 @@ def test_varlen_settings_and_workspace():
     rec = 4096 * 3 + 2 * 128 * 64 * 2
     assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == m * (8 * rec + 16 * 768 + 16 + 384 * 16) + 8 * 6
     assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(dims(io=m2.MAMBA2_F32)) == 0
+
+
+# ------------------------------------------------------------------ the mixer
+def mixer(d, step=False, **kw):
+    a = dict(dm=64, h=BASE, hs=64, wi=BASE + 4 * MB, w=BASE + 8 * MB, b=BASE + 9 * MB, cs=BASE + 10 * MB,
+             dtb=BASE + 11 * MB, A=BASE + 12 * MB, D=BASE + 13 * MB, h0=BASE + 16 * MB, hf=BASE + 20 * MB,
+             ss=BASE + 16 * MB, nw=BASE + 24 * MB, eps=1e-5, wo=BASE + 25 * MB, o=BASE + 32 * MB, os=64,
+             ws=BASE + 256 * MB, wsb=1 << 30)
+    a.update(kw)
+    if step:
+        return m2.lib.mamba2_mixer_step(ctypes.byref(d), a["dm"], a["h"], a["hs"], a["wi"], a["w"], a["b"],
+                                        a["cs"], a["dtb"], a["A"], a["D"], a["ss"], a["nw"], a["eps"], a["wo"],
+                                        a["o"], a["os"], a["ws"], a["wsb"], None)
+    return m2.lib.mamba2_mixer_prefill(ctypes.byref(d), a["dm"], a["h"], a["hs"], a["wi"], a["w"], a["b"],
+                                       a["cs"], a["dtb"], a["A"], a["D"], a["h0"], a["hf"], a["nw"], a["eps"],
+                                       a["wo"], a["o"], a["os"], a["ws"], a["wsb"], None)
+
+
+MIXER_REJECTS = [
+    (dict(wi=None), ENULL), (dict(wo=None), ENULL), (dict(w=None), ENULL), (dict(A=None), ENULL),
+    (dict(h=None), ENULL), (dict(o=None), ENULL),
+    (dict(dm=0), ESHAPE), (dict(dm=60), ESHAPE), (dict(hs=56), ESHAPE), (dict(os=68), EALIGN),
+    (dict(h=BASE + 8), EALIGN), (dict(nw=BASE + 24 * MB + 4), EALIGN), (dict(eps=-1.0), ESHAPE),
+    (dict(o=BASE), EALIAS), (dict(o=BASE + 4 * MB), EALIAS), (dict(ws=BASE + 4 * MB), EALIAS),
+    (dict(cs=BASE + 4 * MB), EALIAS), (dict(o=BASE + 256 * MB), EALIAS),
+    (dict(ws=None), 7), (dict(wsb=1000), 7),
+]
+
+
+@pytest.mark.parametrize("kw,code", MIXER_REJECTS + [(dict(hf=BASE + 25 * MB), EALIAS)])
+def test_mixer_prefill_rejects(kw, code):
+    assert mixer(dims(io=m2.MAMBA2_BF16), **kw) == code, m2.mamba2_last_error()
+
+
+@pytest.mark.parametrize("kw,code", MIXER_REJECTS + [(dict(ss=BASE + 25 * MB), EALIAS), (dict(cs=None), ENULL),
+                                                     (dict(ss=None), ENULL)])
+def test_mixer_step_rejects(kw, code):
+    assert mixer(dims(io=m2.MAMBA2_BF16, seqlen=2, batch=3), step=True, **kw) == code, m2.mamba2_last_error()
+
+
+def test_mixer_settings_and_workspace():
+    assert mixer(dims(io=m2.MAMBA2_BF16, chunk=48)) == EUNSUP
+    assert mixer(dims(seqlen=7), step=True) == ESHAPE
+    assert mixer(dims(seqlen=0), step=True) == ESHAPE
+    a256 = lambda v: -(-v // 256) * 256
+    for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_F32, 4, 64)):
+        d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=20, ngroups=4)
+        E = 2 * 20 * 64 + 2 * 4 * 128 + 20
+        Es = -(-E // 8) * 8
+        rows = 3 * 1000
+        core = m2.mamba2_conv_ssd_prefill_workspace_bytes(d)
+        want = a256(rows * Es * es) + 2 * a256(rows * 20 * 64 * es) + a256(core) + (32 << 20)
+        assert m2.mamba2_mixer_prefill_workspace_bytes(d, 512) == want
+        ds = dims(io=io, batch=5, seqlen=3, nheads=20, ngroups=4)
+        assert m2.mamba2_mixer_step_workspace_bytes(ds, 512) == \
+            a256(15 * Es * es) + 2 * a256(15 * 20 * 64 * es) + (32 << 20)
+    assert m2.mamba2_mixer_prefill_workspace_bytes(dims(), 62) == 0
+    assert m2.mamba2_mixer_step_workspace_bytes(dims(seqlen=9), 64) == 0
