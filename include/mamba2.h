@@ -329,7 +329,7 @@ int mamba2_group_rmsnorm(const mamba2_dims* dims, const void* g, int64_t g_strid
 
 /* mamba2_mixer_prefill_workspace_bytes -- device workspace of mamba2_mixer_prefill for
  * `dims` and d_model, 0 if they are invalid:
- *   a256(rows * Es * e) + 2 * a256(rows * HP * e) + a256(W) + 32 MiB
+ *   a256(rows * Es * e) + 2 * a256(rows * HP * e) + a256(W) + 128 MiB
  * with e the io size, Es = E rounded up to a multiple of 8, W the workspace of
  * mamba2_conv_ssd_prefill for `dims`, a256 rounding up to 256 bytes. */
 size_t mamba2_mixer_prefill_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
@@ -346,7 +346,7 @@ int mamba2_mixer_prefill(const mamba2_dims* dims, int32_t d_model, const void* h
                          void* stream);
 
 /* mamba2_mixer_step_workspace_bytes -- device workspace of mamba2_mixer_step, 0 if `dims`
- * or d_model is invalid: a256(rows * Es * e) + 2 * a256(rows * HP * e) + 32 MiB. */
+ * or d_model is invalid: a256(rows * Es * e) + 2 * a256(rows * HP * e) + 128 MiB. */
 size_t mamba2_mixer_step_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
 
 /* mamba2_mixer_step -- the mixer for dims->seqlen = 1 .. 6 new tokens per sequence: the

@@ -476,7 +476,7 @@ M2_EXPORT int mamba2_group_rmsnorm(const mamba2_dims* d, const void* g, int64_t 
 
 // ------------------------------------------------------------------------------ the mixer
 namespace {
-constexpr size_t kGemmWs = (size_t)32 << 20;   // hipBLASLt workspace of the mixer calls
+constexpr size_t kGemmWs = (size_t)128 << 20;  // hipBLASLt workspace of the mixer calls (stream-K partials)
 
 // Workspace of the mixer calls: the projected rows [z | xBC | dt_raw] (E features, row
 // stride Es, a multiple of 8 elements), the layer core's output y, the normalised output,

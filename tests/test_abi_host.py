@@ -344,10 +344,10 @@ def test_mixer_settings_and_workspace():
         Es = -(-E // 8) * 8
         rows = 3 * 1000
         core = m2.mamba2_conv_ssd_prefill_workspace_bytes(d)
-        want = a256(rows * Es * es) + 2 * a256(rows * 20 * 64 * es) + a256(core) + (32 << 20)
+        want = a256(rows * Es * es) + 2 * a256(rows * 20 * 64 * es) + a256(core) + (128 << 20)
         assert m2.mamba2_mixer_prefill_workspace_bytes(d, 512) == want
         ds = dims(io=io, batch=5, seqlen=3, nheads=20, ngroups=4)
         assert m2.mamba2_mixer_step_workspace_bytes(ds, 512) == \
-            a256(15 * Es * es) + 2 * a256(15 * 20 * 64 * es) + (32 << 20)
+            a256(15 * Es * es) + 2 * a256(15 * 20 * 64 * es) + (128 << 20)
     assert m2.mamba2_mixer_prefill_workspace_bytes(dims(), 62) == 0
     assert m2.mamba2_mixer_step_workspace_bytes(dims(seqlen=9), 64) == 0
