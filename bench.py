@@ -181,6 +181,15 @@ def run_decode(args, torch, m2, si):
         step(k)
     torch.cuda.synchronize()
     n = args.decode_steps
+    # the mean launch duration over back-to-back launches between two events (the timed
+    # region), then each launch bracketed by its own events for the median
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(n):
+        step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    mean_us = e0.elapsed_time(e1) * 1e3 / n
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for k in range(n):
         evs[k][0].record()
@@ -188,7 +197,7 @@ def run_decode(args, torch, m2, si):
         evs[k][1].record()
     torch.cuda.synchronize()
     times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    return cfg, sum(times) / n, times[n // 2]
+    return cfg, mean_us, times[n // 2]
 
 
 def run_decode_tokens(args, torch, m2, si, T=4):
@@ -450,16 +459,21 @@ def _counter_means(path: str, counter: str):
     import csv
     acc, calib = {}, 0.0
     with open(path, newline="") as f:
-        for row in csv.DictReader(f):
-            if row["Counter_Name"] != counter:
-                continue
-            v = float(row["Counter_Value"])
-            a = acc.setdefault((row["Kernel_Name"], row["Kernel_Id"]), [0.0, 0, int(row["Dispatch_Id"])])
-            a[0] += v
-            a[1] += 1
-            a[2] = min(a[2], int(row["Dispatch_Id"]))
-            if "elementwise_kernel" in row["Kernel_Name"]:
-                calib = max(calib, v)
+        rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    # the mixer runs last and launches some of the same kernels at other strides: only the
+    # dispatches before its first GEMM (a hipBLASLt "Cijk" kernel) are counted
+    gemm = [int(r["Dispatch_Id"]) for r in rows if "Cijk" in r["Kernel_Name"]]
+    cut = min(gemm) if gemm else None
+    for row in rows:
+        if cut is not None and int(row["Dispatch_Id"]) >= cut:
+            continue
+        v = float(row["Counter_Value"])
+        a = acc.setdefault((row["Kernel_Name"], row["Kernel_Id"]), [0.0, 0, int(row["Dispatch_Id"])])
+        a[0] += v
+        a[1] += 1
+        a[2] = min(a[2], int(row["Dispatch_Id"]))
+        if "elementwise_kernel" in row["Kernel_Name"]:
+            calib = max(calib, v)
     # Template instantiations can share one (demangled, argument-less) name: such names get
     # "#0", "#1", ... in the order of their first dispatch. In a bench run the one-call step
     # runs first, so "ssd_scan64_kernel#0" is its scan and "#1" the two-call path's.
