@@ -162,3 +162,43 @@ def test_12b_shape_8k_stage_by_stage():
         e1 = assert_close(yc[:, xs], y[0], "bf16", f"core y head {hh}")
         e2 = assert_close(hf[0, hh], hr[0, 0], "bf16", f"core state head {hh}", rounded=False)
         print(f"head {hh}: y {e1:.2e} state {e2:.2e}", flush=True)
+
+
+def test_prefill_seqlen_zero_and_strided_hidden():
+    """seqlen 0 carries h0 into h_final and leaves the conv history alone; a hidden tensor
+    that is a column view of a wider one (row stride 384 for d_model 256) gives the bits of
+    the same rows stored densely."""
+    t = torch()
+    c, p, w, hid, cs0, h0 = case(970, 2, 90, 8, 2, 256)
+    # seqlen 0
+    hf = t.empty((2, 8, 128, 64), dtype=t.float32, device="cuda")
+    cs = dev(cs0, "bf16")
+    out0 = empty((2, 0, 256), "bf16")
+    m2.mamba2_mixer_prefill(empty((2, 0, 256), "bf16"), dev(w["w_in"], "bf16"), dev32(p["conv_w"]),
+                            dev32(p["conv_b"]), cs, dev32(p["dt_bias"]), dev32(p["A"]), dev32(p["D"]), dev32(h0), hf,
+                            dev32(w["norm_w"]), dev(w["w_out"], "bf16"), out0, ngroups=2, chunk=64)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(host(hf), np.asarray(h0, np.float32))
+    np.testing.assert_array_equal(host(cs), cs0)
+    # strided hidden
+    dense = gpu_prefill(c, p, w, hid, cs0, h0)
+    wide = np.zeros((2, 90, 384), np.float32)
+    wide[..., 64:320] = hid
+    hv = dev(wide, "bf16")[..., 64:320]
+    cs2 = dev(cs0, "bf16")
+    hf2 = t.empty((2, 8, 128, 64), dtype=t.float32, device="cuda")
+    out2 = empty((2, 90, 256), "bf16")
+    m2.mamba2_mixer_prefill(hv, dev(w["w_in"], "bf16"), dev32(p["conv_w"]), dev32(p["conv_b"]), cs2,
+                            dev32(p["dt_bias"]), dev32(p["A"]), dev32(p["D"]), dev32(h0), hf2, dev32(w["norm_w"]),
+                            dev(w["w_out"], "bf16"), out2, ngroups=2, chunk=64)
+    t.cuda.synchronize()
+    for g, r in zip((host(out2), host(cs2), host(hf2)), dense):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_deterministic():
+    c, p, w, hid, cs0, h0 = case(971, 1, 150, 8, 2, 256)
+    a = gpu_prefill(c, p, w, hid, cs0, h0)
+    b = gpu_prefill(c, p, w, hid, cs0, h0)
+    for g, r in zip(a, b):
+        np.testing.assert_array_equal(g, r)
