@@ -356,6 +356,80 @@ def run_mixer_step(args, torch, m2, si, d_model: int = 4480):
                     "out-projection; random-init weights"}
 
 
+def run_generation(args, torch, m2, si, ring: int = 64):
+    """The 9B generation-shaped run on one layer: batch 8, an 8192-token one-call prefill
+    (chunk 64), then 16384 sequential decode steps carrying both caches. Inputs are drawn on
+    the device from a seeded generator with the recipe's distributions; the decode steps
+    cycle through a ring of 64 drawn steps (fresh values per step do not change the work).
+    Reports the prefill time, the mean decode step over all steps launched back to back,
+    the median and 99th percentile of 1000 individually timed steps, and tokens/s over the
+    whole run."""
+    cfg = si.CONFIGS[4]
+    B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    Cc, di = cfg.conv_channels, cfg.d_inner
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    bf = torch.bfloat16
+
+    def xbc(*shape):
+        a = torch.randn(*shape, Cc, generator=gen, device="cuda")
+        a[..., di:] *= 128 ** -0.5
+        return a.to(bf)
+
+    p = {k: torch.from_numpy(v).cuda() for k, v in si.draw_params(cfg).items()}
+    u = xbc(B, L)
+    z = torch.randn(B, L, di, generator=gen, device="cuda").to(bf)
+    dt = torch.randn(B, L, H, generator=gen, device="cuda").to(bf)
+    cs = torch.zeros(B, 3, Cc, dtype=bf, device="cuda")
+    h = torch.empty(B, H, cfg.dstate, cfg.headdim, dtype=torch.float32, device="cuda")
+    y = torch.empty(B, L, di, dtype=bf, device="cuda")
+    d = m2.make_dims(B, L, H, G, 64, m2.MAMBA2_BF16)
+    ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    su, sz, sdt = xbc(ring, B), torch.randn(ring, B, di, generator=gen, device="cuda").to(bf), \
+        torch.randn(ring, B, H, generator=gen, device="cuda").to(bf)
+    yt = torch.empty(B, di, dtype=bf, device="cuda")
+
+    def prefill():
+        m2.mamba2_conv_ssd_prefill(u, p["conv_w"], p["conv_b"], cs, dt, p["dt_bias"], p["A"], p["D"], z, None, h,
+                                   y, ngroups=G, chunk=64, workspace=ws)
+
+    def step(k):
+        i = k % ring
+        m2.mamba2_state_update(su[i], p["conv_w"], p["conv_b"], cs, sdt[i], p["dt_bias"], p["A"], p["D"], sz[i],
+                               h, yt, ngroups=G)
+
+    for k in range(20):
+        prefill()
+        step(k)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    prefill()
+    ev[1].record()
+    for k in range(cfg.decode_steps):
+        step(k)
+    ev[2].record()
+    torch.cuda.synchronize()
+    pre_us = ev[0].elapsed_time(ev[1]) * 1e3
+    dec_total_us = ev[1].elapsed_time(ev[2]) * 1e3
+    n = 1000
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for k in range(n):
+        evs[k][0].record()
+        step(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    tokens = B * L + B * cfg.decode_steps
+    state_bytes = B * H * cfg.dstate * cfg.headdim * 4 * 2
+    return {"workload": "9B shape, batch 8: 8192-token one-call prefill (chunk 64), then 16384 decode steps",
+            "prefill_us": pre_us, "decode_steps": cfg.decode_steps,
+            "decode_us_per_step": dec_total_us / cfg.decode_steps, "decode_us_p50": t[n // 2],
+            "decode_us_p99": t[int(n * 0.99)], "total_ms": (pre_us + dec_total_us) / 1e3,
+            "tokens_per_s": tokens / ((pre_us + dec_total_us) * 1e-6),
+            "decode_state_GB_s": state_bytes / (dec_total_us / cfg.decode_steps * 1e-6) / 1e9}
+
+
 def run_varlen(args, torch, m2, si, cfg):
     """The one-call prefill over a packed continuous batch at the 12B shape: 16 sequences of
     seeded log-uniform lengths summing to the workload's 8192 tokens, half of them continuing
@@ -574,6 +648,7 @@ def main():
     dec4 = run_decode_tokens(args, torch, m2, si, 4)
     mix_pre = run_mixer_prefill(args, torch, m2, si, cfg)
     mix_step = run_mixer_step(args, torch, m2, si)
+    gen_run = run_generation(args, torch, m2, si)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -625,6 +700,7 @@ def main():
                    "traffic": measured_traffic("state_update"),
                    "tokens4": dec4},
         "mixer": {"prefill_12b_8k": mix_pre, "step_9b_b64": mix_step},
+        "generation_9b_b8": gen_run,
         "wall_s_timed": wall,
     }
     out["kernels"]["group_rmsnorm"] = {

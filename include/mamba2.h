@@ -246,6 +246,13 @@ int mamba2_conv_ssd_prefill_varlen(const mamba2_dims* dims, const void* xBC, int
  *   z_t        [B][T][H*P] io or NULL
  *   ssm_state  [B][H][N][P] f32, updated in place
  *   y_t        [B][T][H*P] io; must not overlap any other argument
+ *
+ * With one token and fewer than (CU count / 2) (sequence, group) pairs, several
+ * workgroups share a pair; the last of them to finish reading the old conv cache writes
+ * the group's B and C columns. They count their arrivals in a small library-owned
+ * device array that is back to zero when the call ends. Two such calls must therefore
+ * not run at the same time on one device (on different streams), or their counts mix.
+ * Calls on one stream, graph replays and larger batches are unaffected.
  */
 int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w,
                         const float* bias, void* conv_state, const void* dt_raw_t,
@@ -253,7 +260,8 @@ int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w
                         float* ssm_state, void* y_t, void* stream);
 
 /*
- * mamba2_state_update_slots -- mamba2_state_update for a continuous batch whose caches
+ * mamba2_state_update_slots -- mamba2_state_update (with its rule on concurrent
+ * small-batch calls) for a continuous batch whose caches
  * live in pools (as an inference engine keeps them: neurohive, section
  * "Развертывание"): sequence b (rows b T .. b T + T - 1 of u_t, dt_raw_t, z_t, y_t)
  * updates entry slots[b] of conv_pool [npool][W-1][Cc] and ssm_pool [npool][H][N][P] in
@@ -350,7 +358,8 @@ int mamba2_mixer_prefill(const mamba2_dims* dims, int32_t d_model, const void* h
 size_t mamba2_mixer_step_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
 
 /* mamba2_mixer_step -- the mixer for dims->seqlen = 1 .. 6 new tokens per sequence: the
- * layer core is mamba2_state_update (conv_state and ssm_state updated in place). */
+ * layer core is mamba2_state_update (conv_state and ssm_state updated in place; its rule
+ * on concurrent small-batch calls applies). */
 int mamba2_mixer_step(const mamba2_dims* dims, int32_t d_model, const void* hidden,
                       int64_t hidden_stride, const void* w_in, const float* conv_w,
                       const float* conv_bias, void* conv_state, const float* dt_bias,

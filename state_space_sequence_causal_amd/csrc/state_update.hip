@@ -11,7 +11,10 @@
 //
 // One workgroup per (sequence b, group g): it owns the x channels of the
 // group's heads and the group's B and C channels, so every conv-cache column
-// has exactly one reader-writer (no cross-workgroup ordering is needed). Each of
+// has exactly one reader-writer (no cross-workgroup ordering is needed). With
+// few (sequence, group) pairs, 2 or 4 workgroups share a pair, each with its
+// share of the heads and their x channels; the shared B and C columns are then
+// written by the last of them to arrive (see SPLIT below). Each of
 // its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
 // (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of row n = 4m + rg, so one wave
 // instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
@@ -38,6 +41,11 @@ constexpr int DEC_K = 1;            // state rows per lane in one work item
 constexpr int DEC_NB = 4;           // item buffers
 constexpr int DEC_IPH = 32 / DEC_K;  // work items per head
 constexpr int DEC_MAX_HPG = 256;     // heads per group the kernel covers (one dt thread each)
+constexpr int DEC_ARRIVAL_SLOTS = 1024;  // (sequence, group) pairs a split launch may cover
+
+// Arrival counts of the workgroups that share a (sequence, group) in a split launch, zero
+// between calls: the last of them to arrive writes the group's B and C conv-cache columns.
+__device__ unsigned int dec_arrivals[DEC_ARRIVAL_SLOTS];
 static_assert(DEC_MAX_HPG <= DEC_THREADS, "one thread per head for dt");
 
 template <typename T>
@@ -64,31 +72,41 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // conv over the extended sequence (cache, tokens), then for each state part NT updates in
 // registers, so the state is read and written once per call. Each token's arithmetic is the
 // one-token step's, so NT tokens give the bits of NT one-token calls.
-template <typename T, int NT>
-__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 8 : 4, 8)))
+// SPLIT workgroups share a (sequence, group), each with hpg / SPLIT of its heads (small
+// batches, so that more CUs stream state). Each convolves B and C from the cache; the last
+// to arrive, by a device-scope count taken after every read of the old cache in its
+// workgroup, writes the shifted B and C cache columns, so no workgroup can overwrite a
+// cache row another has still to read.
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 && NB == DEC_NB ? 8 : 4, 8)))
 void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
     const float* __restrict__ A, const float* __restrict__ D, const T* __restrict__ z_t,
     float* __restrict__ ssm_state, T* __restrict__ y_t, int H, int G, const int32_t* __restrict__ slots,
     int npool, int64_t us, int64_t zs, int64_t dtrs) {
+  static_assert(DEC_IPH % NB == 0, "a head's parts fill whole rounds of the buffers");
+  static_assert(SPLIT == 1 || NT == 1, "split launches take one token");
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
   const int hpg = H / G;
   const int nblk = gridDim.x;
   const int id = xcd_local_order(blockIdx.x, nblk);
-  const int b = id / G, g = id % G;
+  const int part = id % SPLIT;
+  const int b = id / SPLIT / G, g = id / SPLIT % G;
+  const int hpp = hpg / SPLIT;         // heads of this workgroup
+  const int h0w = g * hpg + part * hpp;   // its first head
   const int di = H * DEC_P;
   const int Cc = di + 2 * G * DEC_N;
-  const int nx = hpg * DEC_P;          // x channels owned
+  const int nx = hpp * DEC_P;          // x channels owned
   const int nch = nx + 2 * DEC_N;      // plus B and C of the group
   // per token t: the conv output of x [nx], B [N], C [N] at smem + t nch; then dt and the decay
   // a = exp(dt A) per (token, head)
   auto xs = [&](int t) { return smem + t * nch; };
   auto bsm = [&](int t) { return smem + t * nch + nx; };
   auto csm = [&](int t) { return smem + t * nch + nx + DEC_N; };
-  float* dts = smem + NT * nch;        // [NT][hpg]
-  float* das = dts + NT * hpg;         // [NT][hpg]
+  float* dts = smem + NT * nch;        // [NT][hpp]
+  float* das = dts + NT * hpp;         // [NT][hpp]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -98,9 +116,9 @@ void state_update_kernel(
   if (slots) {
     sb = slots[b];
     if (sb < 0 || sb >= npool) {
-      for (int i = tid; i < NT * hpg * DEC_P / 4; i += DEC_THREADS) {
-        const int t = i / (hpg * DEC_P / 4), k = i % (hpg * DEC_P / 4);
-        store4(y_t + ((int64_t)b * NT + t) * di + g * hpg * DEC_P + 4 * k, 0.f, 0.f, 0.f, 0.f);
+      for (int i = tid; i < NT * hpp * DEC_P / 4; i += DEC_THREADS) {
+        const int t = i / (hpp * DEC_P / 4), k = i % (hpp * DEC_P / 4);
+        store4(y_t + ((int64_t)b * NT + t) * di + h0w * DEC_P + 4 * k, 0.f, 0.f, 0.f, 0.f);
       }
       return;   // the whole workgroup leaves
     }
@@ -110,12 +128,12 @@ void state_update_kernel(
   // Work items of this wave: (head j, part) for j = wave, wave + DEC_WAVES, ...; part m holds
   // the 4 DEC_K state rows n = 4 DEC_K m + rg + 4k, k < DEC_K. Item it of the wave is part
   // it % DEC_IPH of its head it / DEC_IPH.
-  const int nheads_w = (hpg - wave + DEC_WAVES - 1) / DEC_WAVES;
+  const int nheads_w = (hpp - wave + DEC_WAVES - 1) / DEC_WAVES;
   const int nitems = nheads_w * DEC_IPH;
   // the wave's state base is uniform; an item is a 32-bit byte offset from it (heads of a
   // wave are DEC_WAVES apart, parts of a head 4 DEC_K rows apart)
   const char* wbase = reinterpret_cast<const char*>(
-      ssm_state + ((int64_t)sb * H + g * hpg + wave) * DEC_N * DEC_P);
+      ssm_state + ((int64_t)sb * H + h0w + wave) * DEC_N * DEC_P);
   const uint32_t lane_off = (uint32_t)(rg * DEC_P + 4 * q) * 4u;
   auto item_off = [&](int it) -> uint32_t {
     return (uint32_t)((it / DEC_IPH) * DEC_WAVES * DEC_N * DEC_P + (it % DEC_IPH) * 4 * DEC_K * DEC_P) * 4u;
@@ -123,11 +141,11 @@ void state_update_kernel(
   auto item_ptr = [&](int it) {
     return const_cast<float*>(reinterpret_cast<const float*>(wbase + (item_off(it) + lane_off)));
   };
-  // DEC_NB buffers, item it in buffer it % DEC_NB, DEC_NB - 1 items in flight. Loads past the
+  // NB buffers, item it in buffer it % NB, NB - 1 items in flight. Loads past the
   // wave's last item re-read the last item (never used): every load is unconditional, so the
   // compiler's count of outstanding memory operations stays exact and each wait is for the
   // one item it needs.
-  f32x4 buf[DEC_NB][DEC_K];
+  f32x4 buf[NB][DEC_K];
   auto load_item = [&](int it, f32x4 (&dst)[DEC_K]) {
     const float* st = item_ptr(min(it, nitems - 1));
 #pragma unroll
@@ -142,7 +160,7 @@ void state_update_kernel(
   T* csb = conv_state + (int64_t)sb * (DEC_W - 1) * Cc;
   const int lc = tid * CV;
   const bool conv_thread = lc < nch;
-  const int c = lc < nx ? g * nx + lc
+  const int c = lc < nx ? h0w * DEC_P + lc
                         : (lc < nx + DEC_N ? di + g * DEC_N + (lc - nx) : di + G * DEC_N + g * DEC_N + (lc - nx - DEC_N));
   Raw4<T> e[NT + 3];                   // the extended sequence: 3 cached rows, then the tokens
   f32x4 wv[CV], bv = {0.f, 0.f, 0.f, 0.f};
@@ -159,9 +177,9 @@ void state_update_kernel(
     }
   }
   float dtr[NT], dtb = 0.f, av = 0.f;
-  const bool dt_thread = tid < hpg;
+  const bool dt_thread = tid < hpp;
   if (dt_thread) {
-    const int h = g * hpg + tid;
+    const int h = h0w + tid;
 #pragma unroll
     for (int t = 0; t < NT; ++t) dtr[t] = to_f(dt_raw_t[((int64_t)b * NT + t) * dtrs + h]);
     dtb = dt_bias[h];
@@ -170,7 +188,7 @@ void state_update_kernel(
   // the state does not depend on the conv: its first parts are in flight during the conv
   if (nitems > 0) {
 #pragma unroll
-    for (int k = 0; k < DEC_NB - 1; ++k) load_item(k, buf[k]);
+    for (int k = 0; k < NB - 1; ++k) load_item(k, buf[k]);
   }
   // conv steps on the owned channels; the cache shifts by NT tokens
   if (conv_thread) {
@@ -180,12 +198,14 @@ void state_update_kernel(
       for (int i = 0; i < CV; ++i)
         smem[t * nch + lc + i] = conv4_silu(wv[i], bv[i], e[t].get(i), e[t + 1].get(i), e[t + 2].get(i),
                                             e[t + 3].get(i));
+    if (SPLIT == 1 || lc < nx) {   // split launches: B and C columns after the arrival count
 #pragma unroll
-    for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
+      for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
+    }
   }
   // groups wider than DEC_THREADS * CV channels: the rest, plainly
   for (int l2 = lc + DEC_THREADS * CV; l2 < nch; l2 += DEC_THREADS * CV) {
-    const int c2 = l2 < nx ? g * nx + l2
+    const int c2 = l2 < nx ? h0w * DEC_P + l2
                            : (l2 < nx + DEC_N ? di + g * DEC_N + (l2 - nx) : di + G * DEC_N + g * DEC_N + (l2 - nx - DEC_N));
     Raw4<T> a[NT + 3];
 #pragma unroll
@@ -209,38 +229,56 @@ void state_update_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const float dt = softplus_f(dtr[t] + dtb);
-      dts[t * hpg + tid] = dt;
-      das[t * hpg + tid] = expf(dt * av);
+      dts[t * hpp + tid] = dt;
+      das[t * hpp + tid] = expf(dt * av);
     }
   }
   __syncthreads();
+  if constexpr (SPLIT > 1) {
+    // every read of the old cache in this workgroup has returned (its values were used
+    // before the barrier); count the arrival, and the last workgroup of the group writes
+    // the shifted B and C columns (the host keeps those channels out of the loop above)
+    __shared__ int last_arrival;
+    if (tid == 0) {
+      __threadfence();
+      const unsigned int before = atomicAdd(&dec_arrivals[b * G + g], 1u);
+      const bool last = before == SPLIT - 1;
+      if (last) atomicExch(&dec_arrivals[b * G + g], 0u);
+      last_arrival = last;
+    }
+    __syncthreads();
+    if (last_arrival && conv_thread && lc >= nx) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
+    }
+  }
 
-  // stream the heads: per part, request part it + DEC_NB - 1, then update part it in place
+  // stream the heads: per part, request part it + NB - 1, then update part it in place
   // (NT times, one token after the other)
   const T* zsrc = z_t ? z_t : u_t;     // without z a valid row is read and not used
   for (int hj = 0; hj < nheads_w; ++hj) {
-    const int j = wave + DEC_WAVES * hj;
-    const int h = g * hpg + j;
+    const int j = wave + DEC_WAVES * hj;   // head of this workgroup
+    const int h = h0w + j;
     float a[NT];
     f32x4 dx[NT], yacc[NT];
     Raw4<T> zz[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      a[t] = das[t * hpg + j];
+      a[t] = das[t * hpp + j];
       const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs(t) + j * DEC_P + 4 * q);
-      dx[t] = dts[t * hpg + j] * x4;
+      dx[t] = dts[t * hpp + j] * x4;
       yacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
       // the gate's z is requested now and used after the head's stream, so its latency is hidden
       zz[t] = ld4(zsrc + ((int64_t)b * NT + t) * (z_t ? zs : us) + h * DEC_P + 4 * q);
     }
     const float dh = D ? D[h] : 0.f;
 #pragma unroll 1
-    for (int m0 = 0; m0 < DEC_IPH; m0 += DEC_NB) {
+    for (int m0 = 0; m0 < DEC_IPH; m0 += NB) {
 #pragma unroll
-    for (int mm = 0; mm < DEC_NB; ++mm) {
+    for (int mm = 0; mm < NB; ++mm) {
       const int m = m0 + mm;
       const int it = hj * DEC_IPH + m;
-      load_item(it + DEC_NB - 1, buf[(mm + DEC_NB - 1) % DEC_NB]);
+      load_item(it + NB - 1, buf[(mm + NB - 1) % NB]);
       // keep the request here: the scheduler would otherwise sink it below the update
       __builtin_amdgcn_sched_barrier(0);
       float* st = item_ptr(it);
@@ -293,16 +331,16 @@ void state_update_kernel(
   }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
 static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
-  const int hpg = a.H / a.G;
-  const size_t lds = sizeof(float) * ((size_t)NT * (hpg * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpg);
+  const int hpp = a.H / a.G / SPLIT;
+  const size_t lds = sizeof(float) * ((size_t)NT * (hpp * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpp);
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_update_kernel<T, NT>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((state_update_kernel<T, NT>), dim3(a.B * a.G), dim3(DEC_THREADS), lds, stream,
+  hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT>), dim3(a.B * a.G * SPLIT), dim3(DEC_THREADS), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
@@ -311,10 +349,37 @@ static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static int num_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 template <typename T>
 static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   switch (a.T) {
-    case 1: return launch_nt<T, 1>(a, stream);
+    case 1: {
+      // few (sequence, group) pairs: split each pair's heads over 4 (or 2) workgroups, whose
+      // waves keep 7 parts in flight, so that more CUs stream state. The split keeps to one
+      // round of workgroups (one per CU at its register use): an 8-way split at 9B batch 8,
+      // two rounds, took 32 us against 18 us. The B and C channels must stay inside the
+      // single conv pass (at most 4096 channels).
+      const int hpg = a.H / a.G, bg = a.B * a.G, cus = num_cus();
+      if (bg <= DEC_ARRIVAL_SLOTS) {
+        if (hpg % 4 == 0 && hpg / 4 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 4 <= cus)
+          return launch_nt<T, 1, 2 * DEC_NB, 4>(a, stream);
+        if (hpg % 2 == 0 && hpg / 2 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 2 <= cus)
+          return launch_nt<T, 1, 2 * DEC_NB, 2>(a, stream);
+      }
+      return launch_nt<T, 1>(a, stream);
+    }
     case 2: return launch_nt<T, 2>(a, stream);
     case 3: return launch_nt<T, 3>(a, stream);
     case 4: return launch_nt<T, 4>(a, stream);
