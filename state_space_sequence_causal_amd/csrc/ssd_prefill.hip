@@ -1700,12 +1700,13 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     }
   } else {
     // ========================================================== helper waves
-    // The helpers issue ahead of the Y and H waves that share their SIMDs. Their chain (loads,
-    // the x conv, the tiles of chunk c+1) is the longest of a chunk; at equal priority the
-    // arbiter often picked the other roles first and the helpers finished last. At 12B 8k
-    // the one-call step goes from 320 to 291 us. Raising the H waves instead made it slower
-    // (339 us), and the Y waves' priority made no difference.
-    __builtin_amdgcn_s_setprio(1);
+    // With the conv, the helpers issue ahead of the Y and H waves that share their SIMDs:
+    // their chain (loads, the x conv, the tiles of chunk c+1) is then the longest of a chunk,
+    // and at equal priority the arbiter often picked the other roles first and the helpers
+    // finished last. At 12B 8k the one-call step goes from 320 to 291 us. Raising the H waves
+    // instead made it slower (339 us), the Y waves' priority made no difference, and without
+    // the conv the same priority slows the scan (240 to 260 us).
+    if constexpr (CONV) __builtin_amdgcn_s_setprio(1);
     const int htid = tid - 512, hv = wave - 8;
     const T* xb = x + h * SP;
     const T* zb = z ? z + h * SP : xb;   // without z, x is loaded in its place and not used
