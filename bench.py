@@ -158,7 +158,7 @@ def run_prefill(args, torch, m2, si, cfg, inp, chunk, fused=True):
 
 
 def run_decode(args, torch, m2, si):
-    cfg = si.CONFIGS[2]
+    cfg = si.DECODE_9B_B64
     p = si.draw_params(cfg)
     step_inp = si.draw_decode_step(cfg, 0)
     dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
@@ -205,7 +205,7 @@ def run_decode_tokens(args, torch, m2, si, T=4):
     streamed once for the T tokens), on two alternating state/cache sets like the one-token
     decode."""
     import numpy as np
-    cfg = si.CONFIGS[2]
+    cfg = si.DECODE_9B_B64
     p = si.draw_params(cfg)
     steps = si.draw_decode_steps(cfg, 0, T)
     tok = {k: np.ascontiguousarray(v.transpose(1, 0, 2)) for k, v in steps.items()}   # [B][T][...]
@@ -322,7 +322,7 @@ def run_mixer_prefill(args, torch, m2, si, cfg, d_model: int = 5120):
 def run_mixer_step(args, torch, m2, si, d_model: int = 4480):
     """mamba2_mixer_step at the 9B decode shape: batch 64, one token, hidden width 4480 (the
     pruned 9B model's), on two alternating cache sets like the decode step."""
-    cfg = si.CONFIGS[2]
+    cfg = si.DECODE_9B_B64
     t = _mixer_inputs(torch, si, cfg, d_model, si.draw_hidden(cfg, d_model, step=0))
     h0 = torch.from_numpy(si.draw_h0(cfg)).cuda()
     cs0 = torch.from_numpy(si.bf16_bits(si.draw_conv_state(cfg)).view("int16")).view(torch.bfloat16).cuda()
@@ -364,7 +364,7 @@ def run_generation(args, torch, m2, si, ring: int = 64):
     Reports the prefill time, the mean decode step over all steps launched back to back,
     the median and 99th percentile of 1000 individually timed steps, and tokens/s over the
     whole run."""
-    cfg = si.CONFIGS[4]
+    cfg = si.GENERATE_9B_B8
     B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
     Cc, di = cfg.conv_channels, cfg.d_inner
     gen = torch.Generator(device="cuda")
@@ -628,7 +628,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration(torch)
-    cfg = si.CONFIGS[1]
+    cfg = si.PREFILL_12B_8K
     inp = si.draw_prefill(cfg)
     ms_step, wall, (step_us,) = run_prefill(args, torch, m2, si, cfg, inp, args.chunk)
     _, _, (conv_us, ssd_us) = run_prefill(args, torch, m2, si, cfg, inp, args.chunk, fused=False)

@@ -26,7 +26,8 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "Config", "CONFIGS", "config", "bf16_round", "bf16_bits", "bits_to_f32",
+    "Config", "WORKLOADS", "TINY_F32", "PREFILL_12B_8K", "DECODE_9B_B64", "PREFILL_12B_128K",
+    "GENERATE_9B_B8", "config", "bf16_round", "bf16_bits", "bits_to_f32",
     "draw_params", "draw_xbc", "draw_z", "draw_dt_raw", "draw_h0",
     "draw_conv_state", "draw_prefill", "draw_decode_step", "draw_decode_steps", "TOKEN_BLOCK",
     "draw_gated", "draw_norm_weight", "draw_hidden", "draw_mixer_weights", "mixer_features",
@@ -79,7 +80,7 @@ class Config:
         return self.d_inner + 2 * self.ngroups * self.dstate
 
 
-CONFIGS: Dict[int, Config] = {
+WORKLOADS: Dict[int, Config] = {
     0: Config(0, "tiny-f32", batch=1, seqlen=256, nheads=4, ngroups=1, chunk=64, io="f32"),
     1: Config(1, "prefill-12b-8k", batch=1, seqlen=8192, nheads=160, chunk=128),
     2: Config(2, "decode-9b-b64", batch=64, seqlen=1, nheads=128, chunk=128, h0_std=0.1),
@@ -90,8 +91,16 @@ CONFIGS: Dict[int, Config] = {
 }
 
 
-def config(cid: int, **overrides) -> Config:
-    return dataclasses.replace(CONFIGS[cid], **overrides)
+TINY_F32 = WORKLOADS[0]            # small all-fp32 layer, the oracle finishes it in seconds
+PREFILL_12B_8K = WORKLOADS[1]      # 12B-shape single-layer prefill, 8192 tokens
+DECODE_9B_B64 = WORKLOADS[2]       # 9B-shape decode step, batch 64
+PREFILL_12B_128K = WORKLOADS[3]    # 12B-shape 131072-token prefill
+GENERATE_9B_B8 = WORKLOADS[4]      # 9B-shape generation run: batch 8, 8192-token prefill, 16384 steps
+
+
+def config(base, **overrides) -> Config:
+    """A workload (a Config, or its id) with some fields replaced."""
+    return dataclasses.replace(base if isinstance(base, Config) else WORKLOADS[base], **overrides)
 
 
 def _rng(*key: int) -> np.random.Generator:

@@ -119,7 +119,7 @@ def test_two_step_settings_through_workspace(io, chunk):
 
 def test_fused_12b_8k_full_size():
     """The 12B 8k prefill workload, all heads, with a conv history."""
-    check_bitwise(si.CONFIGS[1], chunk=64)
+    check_bitwise(si.PREFILL_12B_8K, chunk=64)
 
 
 def test_fused_against_oracle():

@@ -66,7 +66,7 @@ def test_prefill_12b_128k_chunk256():
     """12B shape, L = 131072, chunk 256, dt log-uniform: y on every token of one head per
     group and those heads' final states."""
     t = torch()
-    cfg = si.CONFIGS[3]
+    cfg = si.PREFILL_12B_128K
     B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
     di, gn, Cc = cfg.d_inner, G * cfg.dstate, cfg.conv_channels
     heads = one_head_per_group(cfg)
@@ -116,7 +116,7 @@ def test_generation_9b_b8_prefill_then_16k_decode_steps():
     (identical inputs per call), then runs the decode tokens as one conv + scan from its own
     prefill state and the raw conv history."""
     t = torch()
-    cfg = si.CONFIGS[4]
+    cfg = si.GENERATE_9B_B8
     B, L, H, G, K = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, cfg.decode_steps
     di, gn, Cc = cfg.d_inner, G * cfg.dstate, cfg.conv_channels
     heads = one_head_per_group(cfg)

@@ -91,7 +91,7 @@ def check_prefill(cfg, **kw):
 
 def test_prefill_tiny_f32_config():
     """All-fp32 tiny layer (B=1, L=256, 4 heads, 1 group, chunk 64)."""
-    check_prefill(si.CONFIGS[0])
+    check_prefill(si.TINY_F32)
 
 
 def test_prefill_f32_ragged_with_state():
@@ -164,7 +164,7 @@ def test_prefill_chunk_invariance_and_determinism():
 def test_prefill_12b_8k_full_size_head_subset(chunk):
     """The 12B-shape 8k prefill at full size, with the benchmark's chunk of 64 and with 128,
     checked on 9 heads spanning all 8 groups."""
-    cfg = si.CONFIGS[1]
+    cfg = si.PREFILL_12B_8K
     check_prefill(dataclasses.replace(cfg, chunk=chunk), heads=[0, 21, 40, 63, 77, 99, 118, 139, 159])
 
 
@@ -195,7 +195,7 @@ def test_conv1d(io, L, hist):
 
 
 def test_conv1d_12b_channels_no_bias():
-    cfg = si.config(1, seqlen=300)
+    cfg = si.config(si.PREFILL_12B_8K, seqlen=300)
     p = si.draw_params(cfg)
     u = si.draw_xbc(cfg)
     og, _ = gpu_conv(u, p["conv_w"], None, None, "bf16")
@@ -241,7 +241,7 @@ def check_decode(cfg, **opts):
 
 def test_decode_9b_batch64_full():
     """The 9B-shape decode step (B=64, 128 heads, 8 groups), every output checked."""
-    check_decode(si.CONFIGS[2])
+    check_decode(si.DECODE_9B_B64)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -270,7 +270,7 @@ def test_decode_optional_operands(opts):
 def test_chained_conv_then_scan_f32():
     """conv1d -> ssd_prefill on device equals the oracle's conv -> scan end to end."""
     t = torch()
-    cfg = si.CONFIGS[0]
+    cfg = si.TINY_F32
     inp = si.draw_prefill(cfg)
     cs = si.draw_conv_state(cfg)
     u = dev(inp["xbc"], "f32")

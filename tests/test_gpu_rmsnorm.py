@@ -56,7 +56,7 @@ def test_rmsnorm_small(io):
 
 def test_rmsnorm_12b_8k_full():
     """All 8192 x 10240 outputs of the 12B-shape prefill, 8 groups of 1280 channels."""
-    cfg = si.CONFIGS[1]
+    cfg = si.PREFILL_12B_8K
     og, ref = run(cfg)
     e = assert_close(og, ref, "bf16", "rmsnorm 12B")
     print(f"rmsnorm 12B: err/rms {e:.2e}")

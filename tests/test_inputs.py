@@ -9,7 +9,7 @@ import seeded_inputs as si
 
 
 def small(**kw):
-    return dataclasses.replace(si.CONFIGS[4], batch=2, seqlen=700, **kw)
+    return dataclasses.replace(si.GENERATE_9B_B8, batch=2, seqlen=700, **kw)
 
 
 def test_token_slabs_equal_whole_draw():

@@ -55,19 +55,19 @@ def scan(c, s, **kw):
 def test_golden_shapes_define_configs():
     """The config table's Mamba-2 shapes are the ones the pages state."""
     facts = {f["name"]: f["value"] for f in json.load(open(os.path.join(HERE, "golden", "mamba2_shapes.json")))["facts"]}
-    for cid, cfg in si.CONFIGS.items():
+    for cid, cfg in si.WORKLOADS.items():
         assert cfg.headdim == facts["headdim"]
         assert cfg.dstate == facts["dstate"]
         assert cfg.conv_width == facts["conv_width"]
         if cid != 0:
             assert cfg.ngroups == facts["ngroups"]
-    c1 = si.CONFIGS[1]
+    c1 = si.PREFILL_12B_8K
     assert c1.d_inner == facts["expand"] * facts["hidden_12b"]
     assert c1.seqlen == facts["pretrain_seqlen"]
-    assert si.CONFIGS[3].seqlen == facts["max_context"]
+    assert si.PREFILL_12B_128K.seqlen == facts["max_context"]
     for cid in (2, 4):
-        assert facts["mamba_heads_9b_min"] <= si.CONFIGS[cid].nheads <= facts["mamba_heads_9b_max"]
-    assert si.CONFIGS[1].conv_channels == 10240 + 2 * 8 * 128
+        assert facts["mamba_heads_9b_min"] <= si.WORKLOADS[cid].nheads <= facts["mamba_heads_9b_max"]
+    assert si.PREFILL_12B_8K.conv_channels == 10240 + 2 * 8 * 128
 
 
 # --------------------------------------------------------------------------- conv

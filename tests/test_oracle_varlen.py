@@ -162,7 +162,7 @@ def test_bf16_io_rounds_the_conv_output():
 
 
 def test_lengths_recipe_sums_to_total():
-    c = si.config(1)
+    c = si.config(si.PREFILL_12B_8K)
     lens = si.draw_lengths(c, 16, 16, 2048, 8192)
     assert lens.sum() == 8192 and lens.min() >= 1
     s = si.draw_slots(c, 16, 40)
