@@ -15,6 +15,18 @@
 
 namespace m2 {
 
+// 16-byte load and store with the non-temporal hint: each value is read once and written
+// once, so neither should displace other data in the caches (71 to 68 us over the 12B 8k
+// gated output; the same hint on the conv call's stores made it slower, 78 to 88 us)
+template <typename T> __device__ __forceinline__ Vec<T> ld16_stream(const T* p) {
+  Vec<T> r;
+  r.v = __builtin_nontemporal_load(reinterpret_cast<const decltype(r.v)*>(p));
+  return r;
+}
+template <typename T> __device__ __forceinline__ void st16_stream(T* p, const Vec<T>& r) {
+  __builtin_nontemporal_store(r.v, reinterpret_cast<decltype(r.v)*>(p));
+}
+
 constexpr int RMS_THREADS = 256;
 
 template <typename T>
@@ -43,7 +55,7 @@ __global__ __launch_bounds__(RMS_THREADS) void group_rmsnorm_kernel(
     const T* src = src_of(unit0);
     Vec<T> a[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) a[k] = ld16(src + min(lane + 64 * k, nv - 1) * VE);
+    for (int k = 0; k < K; ++k) a[k] = ld16_stream(src + min(lane + 64 * k, nv - 1) * VE);
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -66,7 +78,7 @@ __global__ __launch_bounds__(RMS_THREADS) void group_rmsnorm_kernel(
         Vec<T> o;
 #pragma unroll
         for (int i = 0; i < VE; ++i) o.set(i, a[k].get(i) * scale * wk[i]);
-        st16(dst + v * VE, o);
+        st16_stream(dst + v * VE, o);
       }
     }
   } else {
