@@ -328,9 +328,11 @@ int mamba2_group_rmsnorm(const mamba2_dims* dims, const void* g, int64_t g_strid
  * [rows][Es] (Es = E rounded up to a multiple of 8), the core's output [rows][HP] and the
  * normalised output [rows][HP] are stored in io precision at the start of the workspace,
  * in that order, each at a 256-byte boundary, and stay there after the call. The first mixer call on a
- * device creates that device's hipBLASLt handle, and each new GEMM shape runs hipBLASLt's
- * algorithm heuristic once; the handle and the chosen algorithms are kept until the
- * process ends. No tensor memory is allocated. MAMBA2_ERR_UNSUPPORTED when hipBLASLt has
+ * device creates that device's hipBLASLt handle. For each new GEMM shape, the first call
+ * times hipBLASLt's first choices for three workspace caps (all of it, 32 MiB, none) on
+ * `stream` and keeps the fastest. That call therefore waits for the stream and must not be
+ * made under graph capture. The handle and the chosen algorithms are kept until the process
+ * ends. No tensor memory is allocated. MAMBA2_ERR_UNSUPPORTED when hipBLASLt has
  * no algorithm for a shape; other hipBLASLt failures return MAMBA2_ERR_HIP.
  * out, the workspace and the updated caches must not overlap each other or an input.
  */
