@@ -430,6 +430,71 @@ def run_generation(args, torch, m2, si, ring: int = 64):
             "decode_state_GB_s": state_bytes / (dec_total_us / cfg.decode_steps * 1e-6) / 1e9}
 
 
+def run_other_prefills(args, torch, m2, si):
+    """The other prefill workloads, one call each timed over back-to-back launches: the
+    128k-token 12B-shape prefill (inputs drawn on the device from a seeded generator with
+    the recipe's distributions, dt log-uniform in [1e-3, 0.1] through dt_raw; at chunk 64,
+    the fused call, and at the listed chunk 256) and the tiny all-fp32 layer (seeded host
+    inputs, chunk 64)."""
+    import numpy as np
+    out = {}
+    cfg = si.PREFILL_12B_128K
+    B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    Cc, di = cfg.conv_channels, cfg.d_inner
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    bf = torch.bfloat16
+    u = torch.randn(B, L, Cc, generator=gen, device="cuda")
+    u[..., di:] *= 128 ** -0.5
+    u = u.to(bf)
+    z = torch.randn(B, L, di, generator=gen, device="cuda").to(bf)
+    p = {k: torch.from_numpy(v).cuda() for k, v in si.draw_params(cfg).items()}
+    step = torch.exp(torch.empty(B, L, H, device="cuda").uniform_(float(np.log(1e-3)), float(np.log(0.1)),
+                                                                    generator=gen))
+    dt = (step + torch.log(-torch.expm1(-step)) - p["dt_bias"]).to(bf)   # softplus(dt_raw + dt_bias) = step
+    h = torch.empty(B, H, cfg.dstate, cfg.headdim, dtype=torch.float32, device="cuda")
+    y = torch.empty(B, L, di, dtype=bf, device="cuda")
+    for chunk in (64, 256):
+        d = m2.make_dims(B, L, H, G, chunk, m2.MAMBA2_BF16)
+        ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+
+        def call():
+            m2.mamba2_conv_ssd_prefill(u, p["conv_w"], p["conv_b"], None, dt, p["dt_bias"], p["A"], p["D"], z,
+                                       None, h, y, ngroups=G, chunk=chunk, workspace=ws)
+        us = _time_calls(torch, call, 2, 5)
+        out[f"prefill_12b_128k_chunk{chunk}"] = {"us": us, "tokens_per_s": B * L / (us * 1e-6),
+                                                  "GB_s": prefill_bytes(cfg)["fused"] / (us * 1e-6) / 1e9}
+        del ws
+    del u, z, dt, y
+    cfg = si.TINY_F32
+    inp = si.draw_prefill(cfg)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    tu, tz, tdt = f32(inp["xbc"]), f32(inp["z"]), f32(inp["dt_raw"])
+    th = torch.empty(1, cfg.nheads, cfg.dstate, cfg.headdim, dtype=torch.float32, device="cuda")
+    ty = torch.empty(1, cfg.seqlen, cfg.d_inner, dtype=torch.float32, device="cuda")
+    tw = {k: f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D")}
+
+    def tiny():
+        m2.mamba2_conv_ssd_prefill(tu, tw["conv_w"], tw["conv_b"], None, tdt, tw["dt_bias"], tw["A"], tw["D"], tz,
+                                   None, th, ty, ngroups=cfg.ngroups, chunk=64)
+    out["prefill_tiny_f32"] = {"us": _time_calls(torch, tiny, 50, 200),
+                               "note": "batch 1, 256 tokens, 4 heads, 1 group, all fp32, chunk 64 (latency)"}
+    return out
+
+
+def _time_calls(torch, call, warm: int, n: int) -> float:
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def run_varlen(args, torch, m2, si, cfg):
     """The one-call prefill over a packed continuous batch at the 12B shape: 16 sequences of
     seeded log-uniform lengths summing to the workload's 8192 tokens, half of them continuing
@@ -649,6 +714,7 @@ def main():
     mix_pre = run_mixer_prefill(args, torch, m2, si, cfg)
     mix_step = run_mixer_step(args, torch, m2, si)
     gen_run = run_generation(args, torch, m2, si)
+    others = run_other_prefills(args, torch, m2, si)
     dby = decode_bytes(dcfg)
     dec_gbs = dby / (dec_us * 1e-6) / 1e9
 
@@ -701,6 +767,7 @@ def main():
                    "tokens4": dec4},
         "mixer": {"prefill_12b_8k": mix_pre, "step_9b_b64": mix_step},
         "generation_9b_b8": gen_run,
+        "other_prefills": others,
         "wall_s_timed": wall,
     }
     out["kernels"]["group_rmsnorm"] = {
