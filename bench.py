@@ -465,6 +465,24 @@ def run_other_prefills(args, torch, m2, si):
         out[f"prefill_12b_128k_chunk{chunk}"] = {"us": us, "tokens_per_s": B * L / (us * 1e-6),
                                                   "GB_s": prefill_bytes(cfg)["fused"] / (us * 1e-6) / 1e9}
         del ws
+    # one GPU's share of that sequence split 8 ways (context parallelism): 16384 tokens from
+    # an incoming state and conv history
+    Ls = L // 8
+    cs = torch.zeros(B, 3, Cc, dtype=bf, device="cuda")
+    h0 = 0.1 * torch.randn(B, H, cfg.dstate, cfg.headdim, generator=gen, device="cuda")
+    d = m2.make_dims(B, Ls, H, G, 64, m2.MAMBA2_BF16)
+    ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    us_, zs_, dts_, ys_ = u[:, :Ls], z[:, :Ls], dt[:, :Ls], y[:, :Ls]
+
+    def share():
+        m2.mamba2_conv_ssd_prefill(us_, p["conv_w"], p["conv_b"], cs, dts_, p["dt_bias"], p["A"], p["D"], zs_, h0,
+                                   h, ys_, ngroups=G, chunk=64, workspace=ws)
+    us = _time_calls(torch, share, 5, 20)
+    out["prefill_12b_16k_share_with_h0"] = {"us": us, "tokens_per_s": B * Ls / (us * 1e-6),
+                                             "note": "one GPU's 1/8 share of the 128k sequence, from an "
+                                                     "incoming state and history (the history is updated "
+                                                     "in place each call)"}
+    del ws
     del u, z, dt, y
     cfg = si.TINY_F32
     inp = si.draw_prefill(cfg)

@@ -1,6 +1,7 @@
-"""Full-size parity of the long workloads: the 128k-token 12B prefill (chunk 256) and the
-9B generation run (batch 8, 8192-token prefill, then 16384 decode steps carrying the conv
-and SSM states). Every call runs at its real shape on all heads; the oracle checks one head
+"""Full-size parity of the long workloads: the 128k-token 12B prefill (chunk 256), one
+GPU's 16384-token share of it with an incoming state and history (the per-GPU part of a
+context-parallel split), and the 9B generation run (batch 8, 8192-token prefill, then 16384
+decode steps carrying the conv and SSM states). Every call runs at its real shape on all heads; the oracle checks one head
 per group (the recurrence is per head, so a head's outputs depend only on its own x, z, dt
 and its group's B and C) on every token and every decode step.
 
@@ -196,3 +197,70 @@ def test_generation_9b_b8_prefill_then_16k_decode_steps():
     e4 = assert_close(h_end, hr_end, "bf16", "generation final state", rounded=False)
     print(f"generation (heads {heads}): prefill y {e1:.2e} state {e2:.2e}; "
           f"{K} decode steps y {e3:.2e}, final state {e4:.2e}")
+
+
+def test_context_parallel_share_12b_16k_with_h0():
+    """One GPU's share of the 128k-token sequence split 8 ways: 16384 tokens of the 12B
+    shape through the one-call prefill (chunk 64, the conv fused) starting from an incoming
+    state h0 ~ N(0, 0.1^2) and a conv history, as the GPU after the first would run it once
+    the exchange delivered them. y on every token of one head per group, those heads' final
+    states against the oracle's scan from the same state, on the conv outputs the library
+    computes (checked against the oracle's conv), and the new history bitwise."""
+    t = torch()
+    cfg = si.config(si.PREFILL_12B_128K, seqlen=16384, h0_std=0.1)
+    B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    di, gn, Cc = cfg.d_inner, G * cfg.dstate, cfg.conv_channels
+    heads = one_head_per_group(cfg)
+    chans = sub_channels(cfg, heads)
+    p = si.draw_params(cfg)
+    a = si.draw_xbc(cfg)
+    xbc = empty((B, L, Cc), "bf16")
+    to_dev(xbc, a)
+    sub_x = a[..., chans].astype(np.float64)
+    del a
+    zz = si.draw_z(cfg)
+    z = empty((B, L, di), "bf16")
+    to_dev(z, zz)
+    sub_z = zz[..., head_cols(heads)].astype(np.float64)
+    del zz
+    dd = si.draw_dt_raw(cfg, dt_bias=p["dt_bias"])
+    dt = empty((B, L, H), "bf16")
+    to_dev(dt, dd)
+    sub_dt = dd[..., heads].astype(np.float64)
+    h0 = si.draw_h0(cfg)
+    cs0 = si.draw_conv_state(cfg)
+    cs = empty((B, 3, Cc), "bf16")
+    to_dev(cs, cs0)
+    # the scan's inputs as the library computes them: the conv call on the same rows and
+    # history (the one call is bitwise equal to it followed by the scan), so the oracle's scan
+    # sees the exact bf16 conv outputs the kernels used
+    cs_conv = empty((B, 3, Cc), "bf16")
+    to_dev(cs_conv, cs0)
+    xconv = empty((B, L, Cc), "bf16")
+    m2.mamba2_conv1d(xbc, dev32(p["conv_w"]), dev32(p["conv_b"]), cs_conv, xconv)
+    t.cuda.synchronize()
+    conv = host(xconv.index_select(2, t.from_numpy(chans).cuda()))
+    hist_conv = host(cs_conv)
+    del xconv
+    y = empty((B, L, di), "bf16")
+    hf = t.empty((B, H, cfg.dstate, cfg.headdim), dtype=t.float32, device="cuda")
+    print("context-parallel share: 12B, 16384 tokens, h0 and history", flush=True)
+    m2.mamba2_conv_ssd_prefill(xbc, dev32(p["conv_w"]), dev32(p["conv_b"]), cs, dt, dev32(p["dt_bias"]),
+                               dev32(p["A"]), dev32(p["D"]), z, dev32(h0), hf, y, ngroups=G, chunk=64)
+    t.cuda.synchronize()
+    cols = t.from_numpy(head_cols(heads)).cuda()
+    yg = host(y.index_select(2, cols))
+    hg = host(hf[:, heads])
+    csg = host(cs)
+    del xbc, z, y
+    sp = sub_params(p, heads, chans)
+    conv_r, hist = oracle.conv1d(sub_x, sp["conv_w"], sp["conv_b"], cs0[..., chans])
+    assert_close(conv, conv_r, "bf16", "16k share conv")
+    n = len(heads)
+    yr, hr = oracle.ssd_scan(conv[..., :n * 64], conv[..., n * 64:n * 64 + gn], conv[..., n * 64 + gn:], sub_dt,
+                             sp["dt_bias"], sp["A"], sp["D"], sub_z, h0[:, heads], ngroups=G)
+    ey = assert_close(yg, yr, "bf16", "16k share y")
+    eh = assert_close(hg, hr, "bf16", "16k share h_final", rounded=False)
+    np.testing.assert_array_equal(csg[..., chans], hist)
+    np.testing.assert_array_equal(csg, hist_conv)
+    print(f"16k share (heads {heads}): y err/rms {ey:.2e}, h_final err/rms {eh:.2e}")
