@@ -23,8 +23,9 @@
  *    A, D) and SSM states are float32 in every mode.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *    null stream). Nothing synchronizes, nothing is allocated, no state is kept
- *    between calls (the mixer calls' hipBLASLt handle aside: see there). The
- *    caller owns every buffer and the stream.
+ *    between calls; the exceptions are the mixer calls' hipBLASLt handle and the
+ *    algorithm timing of their first call for a shape (see there). The caller
+ *    owns every buffer and the stream.
  *  - Validation runs on the host before anything is enqueued. On failure the
  *    call returns a nonzero status, enqueues nothing and leaves every buffer
  *    untouched; mamba2_last_error() describes the failure. Launch failures
