@@ -8,9 +8,14 @@ The arithmetic lives in ``mamba2_oracle.c`` (gcc, double precision) and in
 ``brute.py`` (numpy, unrolled products); this module only builds and marshals.
 Every input is converted to float64 from its exact stored value (bf16 or fp32).
 
-Pins (tests/test_oracle_*.py) and the one function left without its own pin
-are listed in each test module's docstring; none of the functions here is
-"parity unpinned".
+Every function here has pins of its own, listed in the docstrings of the test
+modules (tests/test_oracle_*.py); none is "parity unpinned".
+
+Two builds of the same source: ``build`` (gcc -O2, used by the tests and the smoke
+check) and ``build_native`` (gcc -O3 -march=native, compiled on the host that runs it,
+used only to time the oracle as the CPU baseline). Neither uses fast-math, and both
+keep every product and sum a separate rounding (-ffp-contract=off), so the two give
+the same bits.
 """
 from __future__ import annotations
 
@@ -31,14 +36,47 @@ _ip = ctypes.POINTER(ctypes.c_int)
 _L = ctypes.c_long
 
 
+_FLAGS = ["-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-ffp-contract=off"]
+
+
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (-O2, OpenMP, no fast-math, no -march=native)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", "-O2", *_FLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_native(out_dir: str) -> str:
+    """Compile the same source with gcc -O3 -march=native (no fast-math, no contraction)
+    into ``out_dir`` on this host, for timing the oracle where it runs. The library is
+    built fresh each time: the one that ships is built for the machine that built it."""
+    lib = os.path.join(out_dir, "liboracle_native.so")
+    subprocess.check_call(["gcc", "-O3", "-march=native", *_FLAGS, "-o", lib, _SRC, "-lm"])
+    return lib
+
+
+def load_native(out_dir: str):
+    """Builds (build_native) and loads the tuned oracle; returns a handle for ``use``."""
+    return _bind(ctypes.CDLL(build_native(out_dir)))
+
+
+class use:
+    """Context manager: the module's functions call ``lib`` (a handle from load_native)
+    instead of the default build while inside the block."""
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    def __enter__(self):
+        global _lib
+        self.saved, _lib = _load(), self.lib
+        return self.lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
 
 
 def _load():
@@ -46,20 +84,23 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        lib.oracle_threads.argtypes = [ctypes.c_int]
-        lib.oracle_threads.restype = ctypes.c_int
-        lib.oracle_conv1d.argtypes = [_L, _L, _L, _L, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
-        scan = [_L] * 6 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
-        lib.oracle_ssd_scan.argtypes = scan
-        lib.oracle_ssd_chunked.argtypes = [_L] * 7 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
-        lib.oracle_state_update.argtypes = [_L] * 6 + [_dp] * 3 + [_dp] + [_dp] * 4 + [_dp, _dp, _dp, ctypes.c_int]
-        lib.oracle_group_rmsnorm.argtypes = [_L, _L, _L, _dp, _dp, ctypes.c_double, _dp]
-        for f in ("oracle_conv1d", "oracle_ssd_scan", "oracle_ssd_chunked", "oracle_state_update",
-                  "oracle_group_rmsnorm"):
-            getattr(lib, f).restype = None
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
+
+
+def _bind(lib):
+    lib.oracle_threads.argtypes = [ctypes.c_int]
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_conv1d.argtypes = [_L, _L, _L, _L, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
+    scan = [_L] * 6 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
+    lib.oracle_ssd_scan.argtypes = scan
+    lib.oracle_ssd_chunked.argtypes = [_L] * 7 + [_dp] * 11 + [_ip, _L, ctypes.c_int]
+    lib.oracle_state_update.argtypes = [_L] * 6 + [_dp] * 3 + [_dp] + [_dp] * 4 + [_dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_group_rmsnorm.argtypes = [_L, _L, _L, _dp, _dp, ctypes.c_double, _dp]
+    for f in ("oracle_conv1d", "oracle_ssd_scan", "oracle_ssd_chunked", "oracle_state_update",
+              "oracle_group_rmsnorm"):
+        getattr(lib, f).restype = None
+    return lib
 
 
 def _d(a):
