@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MAMBA2_ABI_VERSION 7
+#define MAMBA2_ABI_VERSION 8
 
 enum mamba2_dtype { MAMBA2_F32 = 0, MAMBA2_BF16 = 1 };
 
@@ -70,7 +70,9 @@ typedef struct mamba2_dims {
   int32_t ngroups;    /* G: B/C groups, divides H                                  */
   int32_t dstate;     /* N: must be 128                                            */
   int32_t conv_width; /* W: must be 4                                              */
-  int32_t chunk;      /* Q: prefill chunk; 64, 128 or 256 for bf16, 64 for f32     */
+  int32_t chunk;      /* Q: prefill chunk, 64, 128 or 256: a tiling choice; the    */
+                      /*    kernels tile at 64 whichever is named, and the result  */
+                      /*    does not depend on it beyond rounding                  */
   int32_t io_dtype;   /* enum mamba2_dtype                                         */
 } mamba2_dims;
 
@@ -105,10 +107,10 @@ int mamba2_conv1d(const mamba2_dims* dims, int32_t channels, const void* u, int6
  * first computes, once per (sequence, group, chunk), the causal Gram tiles
  * B_s . C_t of the chunk in fp32 and B^T and C laid out as MFMA operands, which
  * every head of the group then reads, and per (sequence, head, chunk) dt, its
- * prefix sums and per-token decay weights (3 fp32 per token). With T = chunk / 32
- * and e = sizeof(io):
- *   nchunks * (batch * ngroups * (4096 T(T+1)/2 + 2 * 128 * chunk * e)
- *              + batch * nheads * 12 * chunk)           nchunks = ceil(seqlen / chunk)
+ * prefix sums (a hi and a lo part) and per-token decay weights (4 fp32 per token).
+ * The kernels tile at 64 tokens whatever chunk dims names, so with e = sizeof(io):
+ *   nchunks * (batch * ngroups * (12288 + 16384 * e) + batch * nheads * 1024)
+ *                                                       nchunks = ceil(seqlen / 64)
  * The caller owns it; its contents are scratch (nothing is kept between calls).
  */
 size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
@@ -145,10 +147,10 @@ int mamba2_ssd_prefill(const mamba2_dims* dims, const void* x, int64_t x_stride,
 
 /*
  * mamba2_conv_ssd_prefill_workspace_bytes -- device workspace mamba2_conv_ssd_prefill
- * needs for `dims` (0 if `dims` is invalid). For bf16 io at chunk 64 it equals
- * mamba2_ssd_prefill_workspace_bytes(dims); for the other supported settings it adds
- * batch * seqlen * Cc io elements (after rounding the former up to 256 bytes), where
- * the conv output is kept between the two steps.
+ * needs for `dims` (0 if `dims` is invalid). For bf16 io it equals
+ * mamba2_ssd_prefill_workspace_bytes(dims); for fp32 io it adds batch * seqlen * Cc
+ * fp32 elements (after rounding the former up to 256 bytes), where the conv output is
+ * kept between the two steps.
  */
 size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
 
@@ -156,10 +158,10 @@ size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
  * mamba2_conv_ssd_prefill -- the prefill of the layer core from the raw xBC
  * projection: mamba2_conv1d over all Cc = H*P + 2*G*N xBC channels followed by
  * mamba2_ssd_prefill on its x, B and C columns (the conv and the scan of the
- * block: hyper.ai summary, section "方法"). For bf16 io at chunk 64 the conv is
- * applied inside the scan's kernels as they stage each chunk, so the conv output
- * never goes through device memory; the results are bitwise those of the two calls
- * in sequence. Other supported settings run the two steps through the workspace.
+ * block: hyper.ai summary, section "方法"). For bf16 io the conv is applied inside
+ * the scan's kernels as they stage each chunk, so the conv output never goes through
+ * device memory; the results are bitwise those of the two calls in sequence. fp32 io
+ * runs the two steps through the workspace.
  *
  *   xBC        [B][L][Cc] io raw (pre-conv) x | B | C, row stride xbc_stride
  *   conv_w     [Cc][4] f32; conv_bias [Cc] f32 or NULL
@@ -181,10 +183,36 @@ int mamba2_conv_ssd_prefill(const mamba2_dims* dims, const void* xBC, int64_t xb
                             size_t workspace_bytes, void* stream);
 
 /*
+ * mamba2_conv_ssd_prefill_profile -- mamba2_conv_ssd_prefill (bf16 io only; results
+ * bitwise those of that call) with a cycle profile of the scan's contraction phases, the
+ * measurement behind the per-phase MFMA rates (the MFMA contractions of the SSD scan:
+ * hyper.ai summary, section "方法"). For scan workgroup k (k < batch * nheads, one per
+ * (sequence, head)) and wave v (16 per workgroup), phase_cycles[(k * 16 + v) * 4 + i] gets
+ * shader-clock cycles (s_memtime) summed over the chunk loop:
+ *   i = 0  the whole chunk loop;
+ *   i = 1  waves 0-3: the carried-state output H^T C^T of their 32x32 output tile;
+ *          waves 4-7: the state update B^T (w x) of their 32 state rows;
+ *   i = 2  waves 0-3: the intra-chunk product X^T M^T of their tile;
+ *   i = 3  bits of a value the stamps read (kept so that no phase is optimised away).
+ * A phase runs from before its first operand read to after the first read of its result.
+ * phase_cycles: device memory of batch * nheads * 64 uint64, 8-byte aligned, not
+ * overlapping any other argument (MAMBA2_ERR_NULL / _ALIGN / _ALIAS otherwise); fp32 io
+ * is MAMBA2_ERR_UNSUPPORTED. With seqlen 0 it is not written. The stamps slow the scan a
+ * little; this call is for measurement, not for production.
+ */
+int mamba2_conv_ssd_prefill_profile(const mamba2_dims* dims, const void* xBC, int64_t xbc_stride,
+                                    const float* conv_w, const float* conv_bias, void* conv_state,
+                                    const void* dt_raw, const float* dt_bias, const float* A,
+                                    const float* D, const void* z, int64_t z_stride, const float* h0,
+                                    float* h_final, void* y, int64_t y_stride, void* workspace,
+                                    size_t workspace_bytes, uint64_t* phase_cycles, void* stream);
+
+/*
  * mamba2_conv_ssd_prefill_varlen_workspace_bytes -- device workspace of
  * mamba2_conv_ssd_prefill_varlen for `dims` (batch = number of sequences, seqlen =
- * total packed rows; bf16 io, chunk 64), 0 if `dims` is invalid or another setting:
- *   M * (ngroups * R + nheads * 768 + 16 + 384 * nheads) + 8 * (batch + 1),
+ * total packed rows; bf16 io, any supported chunk: the kernels tile at 64), 0 if
+ * `dims` is invalid or another setting:
+ *   M * (ngroups * R + nheads * 1024 + 16 + 384 * nheads) + 8 * (batch + 1),
  *   M = seqlen / 64 + batch
  * with R the per-(group, chunk) record of mamba2_ssd_prefill_workspace_bytes at chunk 64
  * (4096 * 3 + 2 * 128 * 64 * 2 bytes).
@@ -197,7 +225,7 @@ size_t mamba2_conv_ssd_prefill_varlen_workspace_bytes(const mamba2_dims* dims);
  * with continuous batching keeps them (the deployment of the hyper.ai / neurohive pages
  * serves the model through such an engine with an fp32 Mamba cache: neurohive, section
  * "Развертывание"). dims->batch is the number of sequences S, dims->seqlen the number of
- * packed rows; only bf16 io at chunk 64 is supported (MAMBA2_ERR_UNSUPPORTED otherwise).
+ * packed rows; only bf16 io is supported (MAMBA2_ERR_UNSUPPORTED otherwise).
  *
  *   xBC        [seqlen][Cc] io raw rows, row stride xbc_stride; sequence i is rows
  *              cu_seqlens[i] .. cu_seqlens[i+1]
@@ -249,11 +277,9 @@ int mamba2_conv_ssd_prefill_varlen(const mamba2_dims* dims, const void* xBC, int
  *   y_t        [B][T][H*P] io; must not overlap any other argument
  *
  * With one token and fewer than (CU count / 2) (sequence, group) pairs, several
- * workgroups share a pair; the last of them to finish reading the old conv cache writes
- * the group's B and C columns. They count their arrivals in a small library-owned
- * device array that is back to zero when the call ends. Two such calls must therefore
- * not run at the same time on one device (on different streams), or their counts mix.
- * Calls on one stream, graph replays and larger batches are unaffected.
+ * workgroups share a pair, and a second small kernel on the same stream shifts the
+ * groups' B and C cache columns once they have all read them. The call keeps no device
+ * state of its own: calls on different streams (on different caches) are independent.
  */
 int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w,
                         const float* bias, void* conv_state, const void* dt_raw_t,
@@ -261,8 +287,7 @@ int mamba2_state_update(const mamba2_dims* dims, const void* u_t, const float* w
                         float* ssm_state, void* y_t, void* stream);
 
 /*
- * mamba2_state_update_slots -- mamba2_state_update (with its rule on concurrent
- * small-batch calls) for a continuous batch whose caches
+ * mamba2_state_update_slots -- mamba2_state_update for a continuous batch whose caches
  * live in pools (as an inference engine keeps them: neurohive, section
  * "Развертывание"): sequence b (rows b T .. b T + T - 1 of u_t, dt_raw_t, z_t, y_t)
  * updates entry slots[b] of conv_pool [npool][W-1][Cc] and ssm_pool [npool][H][N][P] in
@@ -361,8 +386,7 @@ int mamba2_mixer_prefill(const mamba2_dims* dims, int32_t d_model, const void* h
 size_t mamba2_mixer_step_workspace_bytes(const mamba2_dims* dims, int32_t d_model);
 
 /* mamba2_mixer_step -- the mixer for dims->seqlen = 1 .. 6 new tokens per sequence: the
- * layer core is mamba2_state_update (conv_state and ssm_state updated in place; its rule
- * on concurrent small-batch calls applies). */
+ * layer core is mamba2_state_update (conv_state and ssm_state updated in place). */
 int mamba2_mixer_step(const mamba2_dims* dims, int32_t d_model, const void* hidden,
                       int64_t hidden_stride, const void* w_in, const float* conv_w,
                       const float* conv_bias, void* conv_state, const float* dt_bias,

@@ -27,7 +27,7 @@ struct PrefillArgs {
   int64_t dt_stride = 0;   // row stride of dt_raw in elements; 0: dense (H)
 };
 hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream);
-// The conv fused into the prefill (bf16, chunk 64): x, Bm and Cm of `a` are the raw xBC
+// The conv fused into the prefill (bf16 io): x, Bm and Cm of `a` are the raw xBC
 // columns; w [Cc][4], bias [Cc] (or NULL) and the [B][3][Cc] history (or NULL; updated to
 // the last 3 raw tokens) cover all Cc xBC channels.
 struct ConvArgs {
@@ -35,8 +35,11 @@ struct ConvArgs {
   void* state;
   int Cc;
 };
-hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream);
-// Packed variable-length sequences with states in slot pools (bf16, chunk 64, conv fused):
+// phase_cycles: NULL, or [B * H][16 waves][4] uint64 that receive the scan's phase profile
+// (cycles of the chunk loop and of each wave's contraction phases, summed over chunks).
+hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream,
+                                   uint64_t* phase_cycles = nullptr);
+// Packed variable-length sequences with states in slot pools (bf16 io, conv fused):
 // sequence i covers packed rows cu[i] .. cu[i+1] of x / Bm / Cm / dt_raw / z / y (a.L is
 // the total row count, a.B the sequence count); it starts from ssm_pool / conv_pool entry
 // slots[i] when has_init[i] != 0 (else from zeros) and leaves its final state and conv

@@ -117,10 +117,9 @@ M2_EXPORT int mamba2_conv1d(const mamba2_dims* d, int32_t channels, const void* 
 }
 
 namespace {
-bool chunk_supported(const mamba2_dims* d) {
-  return d->io_dtype == MAMBA2_BF16 ? (d->chunk == 64 || d->chunk == 128 || d->chunk == 256)
-                                    : d->chunk == 64;
-}
+// The chunk length is a tiling choice that leaves the result unchanged up to rounding; every
+// supported value runs the same chunk-64 kernels.
+bool chunk_supported(const mamba2_dims* d) { return d->chunk == 64 || d->chunk == 128 || d->chunk == 256; }
 }  // namespace
 
 M2_EXPORT size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
@@ -139,8 +138,7 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
   if (st) return st;
   const int io = d->io_dtype, es = esize_of(io);
   if (!chunk_supported(d))
-    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
-                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported (64, 128, 256)", d->chunk);
   const size_t ws_need = m2::ssd_prefill_workspace(io == MAMBA2_BF16, d->chunk, d->batch,
                                                    d->seqlen, d->nheads, d->ngroups);
   if (!dt_bias || !A) return fail(MAMBA2_ERR_NULL, "dt_bias and A must not be NULL");
@@ -189,9 +187,9 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
 }
 
 namespace {
-// The conv is fused into the prefill's kernels for bf16 io at chunk 64; other supported
-// settings run the conv into the tail of the workspace first.
-bool conv_fused(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && d->chunk == 64; }
+// The conv is fused into the prefill's kernels for bf16 io; fp32 io runs the conv into the
+// tail of the workspace first.
+bool conv_fused(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t conv_prefill_ws(const mamba2_dims* d, size_t* scan_part) {
   const size_t ws = m2::ssd_prefill_workspace(d->io_dtype == MAMBA2_BF16, d->chunk, d->batch,
@@ -207,7 +205,7 @@ int run_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stri
                          const float* conv_bias, void* conv_state, const void* dt_raw, int64_t dt_stride,
                          const float* dt_bias, const float* A, const float* D, const void* z, int64_t z_stride,
                          const float* h0, float* h_final, void* y, int64_t y_stride, void* workspace,
-                         hipStream_t s) {
+                         hipStream_t s, uint64_t* phase_cycles = nullptr) {
   const int io = d->io_dtype, es = esize_of(io);
   const int64_t H = d->nheads, G = d->ngroups, P = d->headdim, N = d->dstate;
   const int64_t HP = H * P, Cc = HP + 2 * G * N;
@@ -222,7 +220,7 @@ int run_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stri
     if (d->seqlen == 0)   // nothing to convolve; the history is unchanged, h_final gets h0
       return hip_status(m2::launch_ssd_prefill(io == MAMBA2_BF16, d->chunk, a, s), "conv_ssd_prefill launch");
     m2::ConvArgs cv{conv_w, conv_bias, conv_state, (int)Cc};
-    return hip_status(m2::launch_ssd_prefill_conv(a, cv, s), "conv_ssd_prefill launch");
+    return hip_status(m2::launch_ssd_prefill_conv(a, cv, s, phase_cycles), "conv_ssd_prefill launch");
   }
   // the conv into the workspace's tail, then the prefill from there
   char* tail = static_cast<char*>(workspace) + align256(ws_scan);
@@ -241,18 +239,18 @@ M2_EXPORT size_t mamba2_conv_ssd_prefill_workspace_bytes(const mamba2_dims* d) {
   return conv_prefill_ws(d, nullptr);
 }
 
-M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stride,
-                                      const float* conv_w, const float* conv_bias, void* conv_state,
-                                      const void* dt_raw, const float* dt_bias, const float* A,
-                                      const float* D, const void* z, int64_t z_stride,
-                                      const float* h0, float* h_final, void* y, int64_t y_stride,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// mamba2_conv_ssd_prefill, validated; phase_cycles non-NULL runs the scan's phase profile
+int conv_ssd_prefill_checked(const mamba2_dims* d, const void* xBC, int64_t xbc_stride, const float* conv_w,
+                             const float* conv_bias, void* conv_state, const void* dt_raw, const float* dt_bias,
+                             const float* A, const float* D, const void* z, int64_t z_stride, const float* h0,
+                             float* h_final, void* y, int64_t y_stride, void* workspace, size_t workspace_bytes,
+                             void* stream, uint64_t* phase_cycles) {
   int st = check_dims(d, true);
   if (st) return st;
   const int io = d->io_dtype, es = esize_of(io);
   if (!chunk_supported(d))
-    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
-                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported (64, 128, 256)", d->chunk);
   if (!dt_bias || !A || !conv_w) return fail(MAMBA2_ERR_NULL, "dt_bias, A and conv_w must not be NULL");
   if (d->seqlen > 0 && (!xBC || !dt_raw || !y))
     return fail(MAMBA2_ERR_NULL, "xBC, dt_raw and y must not be NULL when seqlen > 0");
@@ -300,12 +298,46 @@ M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int
   if (h0 && h_final && overlap(rh0, rhf) && rh0.lo != rhf.lo)
     return fail(MAMBA2_ERR_ALIAS, "h_final partially overlaps h0 (only exact in-place is allowed)");
 
+  if (phase_cycles) {
+    if (io != MAMBA2_BF16) return fail(MAMBA2_ERR_UNSUPPORTED, "the phase profile covers bf16 io");
+    if (reinterpret_cast<uintptr_t>(phase_cycles) & 7u) return fail(MAMBA2_ERR_ALIGN, "phase_cycles must be 8-byte aligned");
+    const Range rpc = span(phase_cycles, 1, 0, (int64_t)d->batch * H * 64, 8);
+    for (const Range& r : ins)
+      if (overlap(rpc, r)) return fail(MAMBA2_ERR_ALIAS, "phase_cycles overlaps an input");
+    for (const Range& r : {ry, rcs, rhf, rws, rh0})
+      if (overlap(rpc, r)) return fail(MAMBA2_ERR_ALIAS, "phase_cycles overlaps an output, h0 or the workspace");
+  }
   return run_conv_ssd_prefill(d, xBC, xbc_stride, conv_w, conv_bias, conv_state, dt_raw, 0, dt_bias, A, D, z,
-                              z_stride, h0, h_final, y, y_stride, workspace, static_cast<hipStream_t>(stream));
+                              z_stride, h0, h_final, y, y_stride, workspace, static_cast<hipStream_t>(stream),
+                              phase_cycles);
+}
+}  // namespace
+
+M2_EXPORT int mamba2_conv_ssd_prefill(const mamba2_dims* d, const void* xBC, int64_t xbc_stride,
+                                      const float* conv_w, const float* conv_bias, void* conv_state,
+                                      const void* dt_raw, const float* dt_bias, const float* A,
+                                      const float* D, const void* z, int64_t z_stride,
+                                      const float* h0, float* h_final, void* y, int64_t y_stride,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return conv_ssd_prefill_checked(d, xBC, xbc_stride, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z,
+                                  z_stride, h0, h_final, y, y_stride, workspace, workspace_bytes, stream, nullptr);
+}
+
+M2_EXPORT int mamba2_conv_ssd_prefill_profile(const mamba2_dims* d, const void* xBC, int64_t xbc_stride,
+                                              const float* conv_w, const float* conv_bias, void* conv_state,
+                                              const void* dt_raw, const float* dt_bias, const float* A,
+                                              const float* D, const void* z, int64_t z_stride,
+                                              const float* h0, float* h_final, void* y, int64_t y_stride,
+                                              void* workspace, size_t workspace_bytes, uint64_t* phase_cycles,
+                                              void* stream) {
+  if (!phase_cycles) return fail(MAMBA2_ERR_NULL, "phase_cycles must not be NULL");
+  return conv_ssd_prefill_checked(d, xBC, xbc_stride, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z,
+                                  z_stride, h0, h_final, y, y_stride, workspace, workspace_bytes, stream,
+                                  phase_cycles);
 }
 
 namespace {
-bool varlen_supported(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && d->chunk == 64; }
+bool varlen_supported(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && chunk_supported(d); }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 }  // namespace
 
@@ -324,7 +356,7 @@ M2_EXPORT int mamba2_conv_ssd_prefill_varlen(
   if (st) return st;
   const int io = d->io_dtype, es = esize_of(io);
   if (!varlen_supported(d))
-    return fail(MAMBA2_ERR_UNSUPPORTED, "the packed prefill runs with bf16 io at chunk 64 (got chunk %d, %s)",
+    return fail(MAMBA2_ERR_UNSUPPORTED, "the packed prefill runs with bf16 io, chunk 64, 128 or 256 (got chunk %d, %s)",
                 d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
   if (!cu_seqlens || !dt_bias || !A || !conv_w)
     return fail(MAMBA2_ERR_NULL, "cu_seqlens, dt_bias, A and conv_w must not be NULL");
@@ -532,8 +564,7 @@ M2_EXPORT int mamba2_mixer_prefill(const mamba2_dims* d, int32_t d_model, const 
   if (st) return st;
   const int io = d->io_dtype, es = esize_of(io);
   if (!chunk_supported(d))
-    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported for %s (bf16: 64, 128, 256; f32: 64)",
-                d->chunk, io == MAMBA2_BF16 ? "bf16" : "f32");
+    return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported (64, 128, 256)", d->chunk);
   if ((st = check_model_width(d_model, io))) return st;
   if (!(eps >= 0.f) || eps > 3.4e38f) return fail(MAMBA2_ERR_SHAPE, "eps must be finite and >= 0");
   if (!w_in || !w_out || !conv_w || !dt_bias || !A)

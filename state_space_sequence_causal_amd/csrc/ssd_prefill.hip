@@ -18,20 +18,22 @@
 //    instruction; these are shared by all heads of the group. For each head of the group
 //    it writes dt = softplus(dt_raw + dt_bias), the inclusive prefix pi of dt*A*log2(e)
 //    inside 32-token blocks, and v_s = exp2(pi_end - pi_s) dt_s (decay from token s to the
-//    end of its block, times dt_s).
-//  * ssd_scan, one workgroup of 8 waves per (b, h). The fp32 state stays on chip for the
-//    whole sequence. Waves 0-3 ("Y waves") own 32-token blocks of the chunk: they build
-//    the masked decay matrix M from the Gram tiles and compute Y^T = X^T M^T + H^T C^T
-//    and the gated epilogue. Waves 4-7 ("H waves") own 32x32 tiles of the state and run
-//    H = exp(l_end) H + B^T (w x). Each SIMD hosts one wave of each kind; the state tiles
-//    are dealt so that the MFMA work per SIMD is balanced. Per chunk: stage (x, z, decay
-//    vectors) | barrier | compute | barrier | publish the new state.
+//    end of its block, times dt_s). The prefix is summed in fp64 and kept as an fp32 pair
+//    pi = pi_hi + pi_lo: after a token whose decay is very strong the prefix values of a
+//    block are large, and the decay between two later tokens, a difference of two of them,
+//    would otherwise carry the rounding of their size rather than of its own.
+//  * ssd_scan64, one workgroup of 16 waves per (b, h), described at its definition. The fp32
+//    state stays on chip for the whole sequence.
+//
+// The chunk length a call names (64, 128 or 256) is a tiling choice: the result does not
+// depend on it up to rounding, and both kernels always tile at 64 tokens.
 //
 // Decay factors are formed in log2 units from prefix sums taken inside 32-token blocks, so
 // no factor is the difference of two large prefix sums: inside a block exp2(pi_t - pi_s);
-// across blocks the factor splits into a per-row part F[s] and a per-column part U[t],
-// both <= 1, so off-diagonal tiles need no exponentials. D is added to the diagonal of M,
-// so the skip term D x_t comes out of the same MFMAs.
+// across the two blocks of a chunk the factor splits into a per-source part v_s and a
+// per-target part exp2(pi_t), both <= 1, so the off-diagonal tile needs no exponential per
+// element. D is added to the diagonal of M, so the skip term D x_t comes out of the same
+// MFMAs.
 //
 // Precision: x, B, C, z and dt enter exactly (bf16 inputs). The three computed MFMA
 // operands -- M, the state H and the decay-weighted x -- are passed as hi + lo bf16 pairs
@@ -49,7 +51,6 @@ namespace m2 {
 constexpr int SP = 64;   // head dim
 constexpr int SN = 128;  // state dim
 constexpr int PREP_THREADS = 256;
-constexpr int SCAN_THREADS = 512;
 
 template <typename T, int Q>
 struct Cfg {
@@ -61,51 +62,23 @@ struct Cfg {
   static constexpr int KS_Q = Q / 16;
   static constexpr int PAD = VE;
   static constexpr int LDN = SN + PAD;         // LDS rows with n contiguous
-  static constexpr int LDQ = Q + PAD;          // LDS rows with tokens contiguous
   static constexpr size_t FB = sizeof(Frag<T>);
   // workspace record per (b, g, chunk): Gram tiles | B^T operand frags | C operand frags
   static constexpr size_t G_BYTES = (size_t)NTILES * 64 * 16 * sizeof(float);
   static constexpr size_t BT_BYTES = (size_t)(SN / 32) * KS_Q * 64 * FB;
   static constexpr size_t CF_BYTES = (size_t)NTB * KS_N * 64 * FB;
   static constexpr size_t REC_BYTES = G_BYTES + BT_BYTES + CF_BYTES;
-  // workspace record per (b, h, chunk): dt[Q] | pi[Q] | v[Q]
-  static constexpr size_t HREC_BYTES = 3 * Q * sizeof(float);
-  static constexpr int XV = Q * SP / VE / SCAN_THREADS;     // 16-byte x vectors per thread
-  static constexpr bool PAIRS = XV % 2 == 0;                // two tokens per transposed write
+  // workspace record per (b, h, chunk): dt[Q] | pi_hi[Q] | v[Q] | pi_lo[Q]
+  static constexpr int HREC_WORDS = 4 * Q;
+  static constexpr size_t HREC_BYTES = HREC_WORDS * sizeof(float);
   static constexpr int TPL = Q / 64;                        // decay tokens per lane (lane + 64 k)
-  static constexpr int NBD = Q == 128 ? 2 : 1;              // distinct state row blocks per H wave
-  static constexpr bool STAGE_Z = Q <= 128;                 // z / y through LDS (LDS budget)
-  static_assert(Q * SP % (VE * SCAN_THREADS) == 0, "x staging");
 };
-
-// Token position of (row p, token s) in the transposed LDS tiles x^T and (w x)^T. The
-// staging writes of a wave cover 8 rows p = 8 cv + e (cv = 0..7) with 8 consecutive token
-// pairs each; XOR-ing the token index with 16 (cv mod 8) puts the 8 rows on distinct
-// banks. Readers only touch aligned runs of 4 or 8 tokens, which the XOR keeps intact.
-template <int Q>
-__device__ __forceinline__ int xsw(int p, int s) {
-  constexpr int MASK = Q >= 128 ? 7 : Q / 16 - 1;
-  return s ^ (16 * ((p >> 3) & MASK));
-}
 
 __device__ __forceinline__ int tile_tb(int k) {  // column block of lower-triangle tile k < 36
   int tb = 0;
 #pragma unroll
   for (int t = 1; t < 8; ++t) tb += k >= t * (t + 1) / 2;
   return tb;
-}
-
-// frag_accrows on a swizzled row: the two 4-token runs are looked up separately.
-template <int Q, typename T>
-__device__ __forceinline__ Frag<T> frag_accrows_sw(const T* row, int p, int k0, int g) {
-  Frag<T> f;
-  const int a = xsw<Q>(p, k0 + 4 * g), b = xsw<Q>(p, k0 + 8 + 4 * g);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f.v[e] = row[a + e];
-    f.v[4 + e] = row[b + e];
-  }
-  return f;
 }
 
 template <typename T>
@@ -316,17 +289,20 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
         const int h = g * hpg + j;
         const int s = 64 * k + lane;
         const float dt = s < nvalid ? softplus_f(raw[u] + dt_bias[h]) : 0.f;
-        float run = dt * A[h] * kLog2e;
+        // the block prefix in fp64 (each step dt*A*log2e rounded once, in fp32)
+        double run = (double)(dt * A[h] * kLog2e);
 #pragma unroll
         for (int d = 1; d < 32; d <<= 1) {
-          float o = __shfl_up(run, d, 32);
+          const double o = __shfl_up(run, d, 32);
           if ((lane & 31) >= d) run += o;
         }
-        const float tot = __shfl(run, (lane & 32) + 31);   // the block's total
+        const double tot = __shfl(run, (lane & 32) + 31);   // the block's total
+        const float hi = (float)run;
         float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
         hr[s] = dt;
-        hr[Q + s] = run;
-        hr[2 * Q + s] = exp2_hw(tot - run) * dt;   // decay from s to the end of its block, times dt
+        hr[Q + s] = hi;
+        hr[2 * Q + s] = exp2_hw((float)(tot - run)) * dt;   // decay from s to the end of its block, times dt
+        hr[3 * Q + s] = (float)(run - (double)hi);
       }
     }
   }
@@ -375,20 +351,41 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
     }
   }
   __syncthreads();
-  // Gram tiles: wave w computes lower-triangle tiles k = w, w+4, ...
-  for (int k = wave; k < C::NTILES; k += 4) {
-    const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
-    f32x16 acc = (f32x16){};
+  // Gram tiles, stored as [q][lane][4]: accumulator registers 4q .. 4q+3 of every lane, so
+  // that each of the reader's four 16-byte loads covers 1 KiB contiguously
+  if constexpr (C::SPLIT) {
+    // bf16 inputs: their products are exact in fp32; MFMA, wave w computes lower-triangle
+    // tiles k = w, w+4, ...
+    for (int k = wave; k < C::NTILES; k += 4) {
+      const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
+      f32x16 acc = (f32x16){};
 #pragma unroll
-    for (int j = 0; j < C::KS_N; ++j)
-      mma(acc, frag_contig(&sB[si * 32 + col][16 * j], g2), frag_contig(&sC[tb * 32 + col][16 * j], g2));
-    // stored as [q][lane][4]: accumulator registers 4q .. 4q+3 of every lane, so that each
-    // of the reader's four 16-byte loads covers 1 KiB contiguously
-    float* dst = gout + (size_t)k * 1024 + 4 * lane;
+      for (int j = 0; j < C::KS_N; ++j)
+        mma(acc, frag_contig(&sB[si * 32 + col][16 * j], g2), frag_contig(&sC[tb * 32 + col][16 * j], g2));
+      float* dst = gout + (size_t)k * 1024 + 4 * lane;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(dst + 256 * q) =
-          (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(dst + 256 * q) =
+            (f32x4){acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+  } else {
+    // fp32 inputs: each entry B_s . C_t is a 128-term dot product in fp64 (the products are
+    // exact there), rounded once to fp32, so the all-fp32 mode's Gram carries no summation
+    // error. Item (k, q, l) holds accumulator registers 4q .. 4q+3 of lane l of tile k.
+    for (int it = tid; it < C::NTILES * 4 * 64; it += PREP_THREADS) {
+      const int k = it / 256, q = (it / 64) % 4, l = it % 64;
+      const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
+      const int t = tb * 32 + (l & 31);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sr = si * 32 + acc_row(4 * q + e, l);
+        double dot = 0.0;
+        for (int n = 0; n < SN; ++n) dot = fma((double)sB[sr][n], (double)sC[t][n], dot);
+        v[e] = (float)dot;
+      }
+      *reinterpret_cast<f32x4*>(gout + (size_t)k * 1024 + 256 * q + 4 * l) = v;
+    }
   }
   // B^T operand frags (row n = nb*32 + col, k = s): record (nb, j), lane
   for (int idx = tid; idx < (SN / 32) * C::KS_Q * 64; idx += PREP_THREADS) {
@@ -408,976 +405,10 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
-// ---------------------------------------------------------------------------- scan kernel, chunk 256
-// One role per wave for the whole chunk: 4 Y waves build the masked decay tiles M^T of their
-// token blocks in registers and compute Y^T, 4 H waves update the state (two barriers per
-// chunk). z is read straight from HBM (the chunk does not fit LDS alongside the rest).
-template <typename T, int Q>
-struct WideSmem {
-  using C = Cfg<T, Q>;
-  T sXt[SP][C::LDQ];                       // x^T (k = s): A operand of Y_diag
-  T sXW[SP][C::LDQ];                       // (w x)^T hi: B operand of the state update
-  T sXWlo[C::SPLIT ? SP : 1][C::LDQ];      //        lo
-  T sHt[SP][C::LDN];                       // H^T hi: A operand of Y_off
-  T sHtlo[C::SPLIT ? SP : 1][C::LDN];      //     lo
-  float sG[C::STAGE_Z ? Q : 1][SP + 4];    // SiLU(z) of the chunk in fp32, then y (fp32)
-  float sPi[Q];                            // inclusive prefix of dt*A*log2e inside 32-token blocks
-  float sDt[Q];
-  float sE[Q];                             // exp2(lambda_t), lambda from the chunk start
-  float sF[C::NTB][Q];                     // sF[tb][s] = exp2(lambda_{32tb-1} - lambda_s) dt_s, s < 32 tb
-};
-
-// State tiles (32x32 of H[n][p], nb = n / 32, pb = p / 32) updated by H wave hw, dealt so
-// that each SIMD (one Y wave + one H wave) gets about the same number of MFMAs. slot[i]
-// indexes the distinct row blocks nbs[] whose B^T operands the wave keeps in registers.
-struct HList { int n; int nb[4]; int pb[4]; int slot[4]; int nbs[2]; };
-template <int Q> __device__ __forceinline__ HList hlist(int hw);
-template <> __device__ __forceinline__ HList hlist<64>(int hw) {
-  return {2, {hw, hw, 0, 0}, {0, 1, 0, 0}, {0, 0, 0, 0}, {hw, hw}};
-}
-template <> __device__ __forceinline__ HList hlist<128>(int hw) {
-  switch (hw) {
-    case 0: return {3, {0, 0, 1, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 1}};
-    case 1: return {2, {1, 2, 0, 0}, {1, 0, 0, 0}, {0, 1, 0, 0}, {1, 2}};
-    case 2: return {2, {2, 3, 0, 0}, {1, 0, 0, 0}, {0, 1, 0, 0}, {2, 3}};
-    default: return {1, {3, 0, 0, 0}, {1, 0, 0, 0}, {0, 0, 0, 0}, {3, 3}};
-  }
-}
-template <> __device__ __forceinline__ HList hlist<256>(int hw) {
-  return {2, {hw, hw, 0, 0}, {0, 1, 0, 0}, {0, 0, 0, 0}, {hw, hw}};
-}
-// Token blocks and p-blocks owned by Y wave y: Q=64: one (tb, pb) each; Q=128: block y,
-// both p-blocks; Q=256: blocks y and 7-y (light + heavy), both p-blocks.
-template <int Q> struct YPlan;
-template <> struct YPlan<64> {
-  static constexpr int NT = 1, NPB = 1;
-  __device__ static int tb(int y, int) { return y & 1; }
-  __device__ static int pb(int y, int) { return y >> 1; }
-};
-template <> struct YPlan<128> {
-  static constexpr int NT = 1, NPB = 2;
-  __device__ static int tb(int y, int) { return y; }
-  __device__ static int pb(int, int i) { return i; }
-};
-template <> struct YPlan<256> {
-  static constexpr int NT = 2, NPB = 2;
-  __device__ static int tb(int y, int k) { return k == 0 ? y : 7 - y; }
-  __device__ static int pb(int, int i) { return i; }
-};
-
-template <typename T>
-__device__ __forceinline__ void split_set(Frag<T>& hi, Frag<T>& lo, int e, float v) {
-  frag_set<T>(hi, e, v);
-  if constexpr (sizeof(T) == 2) frag_set<T>(lo, e, v - frag_get(hi, e));
-}
-
-// one Gram tile (1024 floats, [q][lane][4]) into this lane's accumulator-order registers
-__device__ __forceinline__ f32x16 load_tile16(const float* tile, int lane) {
-  f32x16 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(tile + 256 * q + 4 * lane);
-    r[4 * q] = v[0];
-    r[4 * q + 1] = v[1];
-    r[4 * q + 2] = v[2];
-    r[4 * q + 3] = v[3];
-  }
-  return r;
-}
-
-template <typename T, int Q>
-__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ssd_scan_wide_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
-                     const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
-                     T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                     int L, int H, int G) {
-  using C = Cfg<T, Q>;
-  using YP = YPlan<Q>;
-  constexpr int VE = C::VE;
-  extern __shared__ __align__(16) unsigned char scan_smem[];
-  WideSmem<T, Q>& S = *reinterpret_cast<WideSmem<T, Q>*>(scan_smem);
-
-  const int id = xcd_local_order(blockIdx.x, gridDim.x);
-  const int b = id / H, h = id % H;
-  const int g = h / (H / G);
-  const int nC = (L + Q - 1) / Q;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, g2 = lane >> 5;
-  const bool ywave = wave < 4;
-  const int hw = ywave ? 0 : wave - 4;
-
-  const int64_t row0 = (int64_t)b * L;
-  const T* xb = x + h * SP;
-  const T* zb = z ? z + h * SP : nullptr;
-  T* yb = y + h * SP;
-  const float Dh = D ? D[h] : 0.f;
-  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
-  const float* hrec = reinterpret_cast<const float*>(
-      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
-      ((size_t)b * H + h) * nC * C::HREC_BYTES);
-
-  // ------------------------------------------------------------ staging registers
-  // x: XV 16-byte vectors per thread. With PAIRS, vectors 2i and 2i+1 are tokens 2sp and
-  // 2sp+1 of one 16-byte column, 8 lanes per token row (coalesced loads), so x^T and
-  // (w x)^T go to LDS as 32-bit token pairs. z: the same row-major mapping, 16-byte
-  // vectors straight into sZ.
-  Vec<T> rX[C::XV], rZ[C::XV];
-  float rdt[C::TPL], rpi[C::TPL];
-  auto xcoord = [&](int i, int& s, int& cv) {
-    constexpr int VPR = SP / VE;  // vectors per token row
-    if constexpr (C::PAIRS) {
-      const int u = tid + SCAN_THREADS * (i >> 1);
-      s = 2 * (u / VPR) + (i & 1);
-      cv = u % VPR;
-    } else {
-      const int v = tid + SCAN_THREADS * i;
-      s = v / VPR;
-      cv = v % VPR;
-    }
-  };
-  auto load_chunk = [&](int c) {
-    const int t0 = c * Q;
-#pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      int s_, cv;
-      xcoord(i, s_, cv);
-      const int t = t0 + s_;
-      const bool ok = t < L;
-      rX[i] = ok ? ld16(xb + (row0 + t) * x_stride + cv * VE) : zero16<T>();
-      if constexpr (C::STAGE_Z) {
-        if (zb) rZ[i] = ok ? ld16(zb + (row0 + t) * z_stride + cv * VE) : zero16<T>();
-      }
-    }
-    const float* hr = hrec + (size_t)c * (3 * Q);
-#pragma unroll
-    for (int k = 0; k < C::TPL; ++k) {
-      rdt[k] = hr[lane + 64 * k];
-      rpi[k] = hr[Q + lane + 64 * k];
-    }
-  };
-
-  // ------------------------------------------------------------ chunk phase S1
-  // y of the previous chunk out of sZ (coalesced), z of this chunk in; decay vectors
-  // (every wave derives them, so staging threads get w_s by a cross-lane shuffle); x^T and
-  // (w x)^T into LDS; prefetch of the next chunk.
-  auto phase_s1 = [&](int c) {
-    if constexpr (C::STAGE_Z) {
-#pragma unroll
-      for (int i = 0; i < C::XV; ++i) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        float* grow = &S.sG[s_][cv * VE];
-        if (c > 0) {
-          const int t = (c - 1) * Q + s_;
-          if (t < L) {
-            Vec<T> o;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o.set(e, grow[e]);
-            st16(yb + (row0 + t) * y_stride + cv * VE, o);
-          }
-        }
-        if (zb) {
-#pragma unroll
-          for (int e = 0; e < VE; e += 4)
-            *reinterpret_cast<f32x4*>(grow + e) =
-                (f32x4){silu_fast(rZ[i].get(e)), silu_fast(rZ[i].get(e + 1)),
-                        silu_fast(rZ[i].get(e + 2)), silu_fast(rZ[i].get(e + 3))};
-        }
-      }
-    }
-    float tot[C::NTB];
-#pragma unroll
-    for (int k = 0; k < C::TPL; ++k) {
-      tot[2 * k] = __shfl(rpi[k], 31);
-      tot[2 * k + 1] = __shfl(rpi[k], 63);
-    }
-    float wv[C::TPL];
-#pragma unroll
-    for (int k = 0; k < C::TPL; ++k) {
-      const int blk = 2 * k + (lane >> 5);
-      float before = 0.f, after = 0.f;
-#pragma unroll
-      for (int bb = 0; bb < C::NTB; ++bb) {
-        if (bb < blk) before += tot[bb];
-        if (bb > blk) after += tot[bb];
-      }
-      const float tail = tot[blk] - rpi[k];  // lambda_{end of blk} - lambda_t
-      wv[k] = exp2_hw(tail + after) * rdt[k];
-      if (wave == 0) {
-        const int t = lane + 64 * k;
-        S.sPi[t] = rpi[k];
-        S.sDt[t] = rdt[k];
-        S.sE[t] = exp2_hw(before + rpi[k]);
-        float acc = tail;
-#pragma unroll
-        for (int tb = 1; tb < C::NTB; ++tb) {
-          if (tb > blk) {
-            S.sF[tb][t] = exp2_hw(acc) * rdt[k];
-            acc += tot[tb];
-          }
-        }
-      }
-    }
-    // w of token s lives in lane s % 64, register s / 64
-    auto w_of = [&](int s_) {
-      float r = 0.f;
-#pragma unroll
-      for (int k = 0; k < C::TPL; ++k) {
-        const float o = __shfl(wv[k], s_ & 63);
-        if ((s_ >> 6) == k) r = o;
-      }
-      return r;
-    };
-    if constexpr (C::PAIRS) {
-#pragma unroll
-      for (int i = 0; i < C::XV; i += 2) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        const float w0 = w_of(s_), w1 = w_of(s_ + 1);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const T x0 = rX[i].v[e], x1 = rX[i + 1].v[e];
-          const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
-          const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
-          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
-          st_pair(&S.sXt[p][sw], x0, x1);
-          st_pair(&S.sXW[p][sw], h0_, h1_);
-          if constexpr (C::SPLIT)
-            st_pair(&S.sXWlo[p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::XV; ++i) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        const float w0 = w_of(s_);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const T x0 = rX[i].v[e];
-          const float v0 = to_f(x0) * w0;
-          const T h0_ = from_f<T>(v0);
-          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
-          S.sXt[p][sw] = x0;
-          S.sXW[p][sw] = h0_;
-          if constexpr (C::SPLIT) S.sXWlo[p][sw] = from_f<T>(v0 - to_f(h0_));
-        }
-      }
-    }
-    if (c + 1 < nC) load_chunk(c + 1);
-  };
-
-  // The two roles run separate chunk loops with the same barrier sequence (two barriers
-  // per chunk), so each role's registers are allocated on their own.
-  if (ywave) {
-    // ========================================================== Y waves: outputs
-    Frag<T> cf[C::KS_N];                // C operand frags of the token block
-    f32x16 gq0, gq1;                    // Gram tiles, fetched two ahead
-    Raw4<T> ze[YP::NPB][4];             // z when it is not staged through LDS
-    auto yfetch = [&](int c, int tb) {
-      const unsigned char* rec = wsg + (size_t)c * C::REC_BYTES;
-      const unsigned char* cfp = rec + C::G_BYTES + C::BT_BYTES;
-#pragma unroll
-      for (int j = 0; j < C::KS_N; ++j)
-        cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
-      const float* gt = reinterpret_cast<const float*>(rec);
-      const int k0 = tb * (tb + 1) / 2;
-      gq0 = load_tile16(gt + (size_t)k0 * 1024, lane);
-      if (tb > 0) gq1 = load_tile16(gt + (size_t)(k0 + 1) * 1024, lane);
-      if constexpr (!C::STAGE_Z) {
-        const int t = c * Q + tb * 32 + col;
-        if (zb && t < L) {
-#pragma unroll
-          for (int i = 0; i < YP::NPB; ++i)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              ze[i][r4] = ld4(zb + (row0 + t) * z_stride + YP::pb(wave, i) * 32 + 8 * r4 + 4 * g2);
-        }
-      }
-    };
-    if (nC > 0) load_chunk(0);
-    for (int c = 0; c < nC; ++c) {
-      const int t0 = c * Q;
-      const float* gt = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES);
-      yfetch(c, YP::tb(wave, 0));
-      phase_s1(c);
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < YP::NT; ++k) {
-        const int tb = YP::tb(wave, k);
-        if (k > 0) yfetch(c, tb);
-        const int tl = tb * 32 + col;
-        const int t = t0 + tl;
-        f32x16 yoff[YP::NPB], yd[YP::NPB];
-        // carried state: Y^T = H^T C^T (scaled by exp2(lambda_t) in the epilogue)
-#pragma unroll
-        for (int i = 0; i < YP::NPB; ++i) {
-          const int prow = YP::pb(wave, i) * 32 + col;
-          yoff[i] = (f32x16){};
-          yd[i] = (f32x16){};
-#pragma unroll
-          for (int j = 0; j < C::KS_N; ++j) {
-            mma(yoff[i], frag_contig(&S.sHt[prow][16 * j], g2), cf[j]);
-            if constexpr (C::SPLIT) mma(yoff[i], frag_contig(&S.sHtlo[prow][16 * j], g2), cf[j]);
-          }
-        }
-        // off-diagonal source blocks si < tb: M = G * F[s]; the column factor U[t] after
-        const int k0 = tb * (tb + 1) / 2;
-        for (int si = 0; si < tb; ++si) {
-          const f32x16 gcur = gq0;
-          gq0 = gq1;
-          if (si + 2 <= tb) gq1 = load_tile16(gt + (size_t)(k0 + si + 2) * 1024, lane);
-          Frag<T> mh[2], ml[2];
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 fs = *reinterpret_cast<const f32x4*>(&S.sF[tb][si * 32 + 8 * r4 + 4 * g2]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = 4 * r4 + q;
-              split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gcur[r] * fs[q]);
-            }
-          }
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-            for (int i = 0; i < YP::NPB; ++i) {
-              const int prow = YP::pb(wave, i) * 32 + col;
-              Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, si * 32 + 16 * m2, g2);
-              mma(yd[i], xa, mh[m2]);
-              if constexpr (C::SPLIT) mma(yd[i], xa, ml[m2]);
-            }
-        }
-        const float pit = S.sPi[tl];
-        if (tb > 0) {
-          const float ut = exp2_hw(pit);  // exp2(lambda_t - lambda_{32tb-1})
-#pragma unroll
-          for (int i = 0; i < YP::NPB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) yd[i][r] *= ut;
-        }
-        // diagonal block: exp2(pi_t - pi_s) dt_s for s <= t, plus D on the diagonal (the
-        // skip term); its Gram tile is in gq0
-        {
-          Frag<T> mh[2], ml[2];
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int s0 = tb * 32 + 8 * r4 + 4 * g2;
-            const f32x4 ps = *reinterpret_cast<const f32x4*>(&S.sPi[s0]);
-            const f32x4 ds = *reinterpret_cast<const f32x4*>(&S.sDt[s0]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = 4 * r4 + q;
-              float v = (s0 + q <= tl) ? gq0[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
-              if (s0 + q == tl) v += Dh;
-              split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
-            }
-          }
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-            for (int i = 0; i < YP::NPB; ++i) {
-              const int prow = YP::pb(wave, i) * 32 + col;
-              Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, tb * 32 + 16 * m2, g2);
-              mma(yd[i], xa, mh[m2]);
-              if constexpr (C::SPLIT) mma(yd[i], xa, ml[m2]);
-            }
-        }
-        // epilogue: y = (E_t Y_off + Y_diag) SiLU(z)
-        const float et = S.sE[tl];
-#pragma unroll
-        for (int i = 0; i < YP::NPB; ++i)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int p0 = YP::pb(wave, i) * 32 + 8 * r4 + 4 * g2;
-            float o[4];
-            if constexpr (C::STAGE_Z) {
-              f32x4 gg = {1.f, 1.f, 1.f, 1.f};
-              if (zb) gg = *reinterpret_cast<const f32x4*>(&S.sG[tl][p0]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) o[q] = (et * yoff[i][4 * r4 + q] + yd[i][4 * r4 + q]) * gg[q];
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float v = et * yoff[i][4 * r4 + q] + yd[i][4 * r4 + q];
-                if (zb) v *= silu_fast(ze[i][r4].get(q));
-                o[q] = v;
-              }
-            }
-            if constexpr (C::STAGE_Z) {
-              *reinterpret_cast<f32x4*>(&S.sG[tl][p0]) = (f32x4){o[0], o[1], o[2], o[3]};
-            } else {
-              if (t < L) st4(yb + (row0 + t) * y_stride + p0, o[0], o[1], o[2], o[3]);
-            }
-          }
-      }
-      __syncthreads();
-    }
-  } else {
-    // ========================================================== H waves: state
-    const HList hl = hlist<Q>(hw);
-    f32x16 hacc[4];
-    Frag<T> af[C::NBD][C::KS_Q];        // B^T operand frags of the chunk
-    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i < hl.n) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int n = hl.nb[i] * 32 + acc_row(r, lane), p = hl.pb[i] * 32 + col;
-          hacc[i][r] = h0 ? h0[sbase + n * SP + p] : 0.f;
-        }
-      }
-    auto write_state = [&]() {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < hl.n) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            int n = hl.nb[i] * 32 + 8 * r4 + 4 * g2, p = hl.pb[i] * 32 + col;
-            float v[4], lo[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              v[k] = hacc[i][4 * r4 + k];
-              lo[k] = v[k] - to_f(from_f<T>(v[k]));
-            }
-            st4(&S.sHt[p][n], v[0], v[1], v[2], v[3]);
-            if constexpr (C::SPLIT) st4(&S.sHtlo[p][n], lo[0], lo[1], lo[2], lo[3]);
-          }
-        }
-    };
-    write_state();
-    if (nC > 0) load_chunk(0);
-    for (int c = 0; c < nC; ++c) {
-      const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
-#pragma unroll
-      for (int d = 0; d < C::NBD; ++d)
-#pragma unroll
-        for (int j = 0; j < C::KS_Q; ++j)
-          af[d][j] = ld_frag<T>(btf + ((size_t)(hl.nbs[d] * C::KS_Q + j) * 64 + lane) * C::FB);
-      phase_s1(c);
-      __syncthreads();
-      const float eend = S.sE[Q - 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < hl.n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
-#pragma unroll
-      for (int j = 0; j < C::KS_Q; ++j) {
-        Frag<T> bh[2], bl[2];
-#pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
-          const int prow = pb * 32 + col, k0 = xsw<Q>(prow, 16 * j + 8 * g2);
-          bh[pb] = frag_contig(&S.sXW[prow][k0], 0);
-          if constexpr (C::SPLIT) bl[pb] = frag_contig(&S.sXWlo[prow][k0], 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i < hl.n) {
-            const Frag<T>& a = (C::NBD > 1 && hl.slot[i]) ? af[C::NBD - 1][j] : af[0][j];
-            mma(hacc[i], a, hl.pb[i] ? bh[1] : bh[0]);
-            if constexpr (C::SPLIT) mma(hacc[i], a, hl.pb[i] ? bl[1] : bl[0]);
-          }
-      }
-      __syncthreads();
-      write_state();
-    }
-    if (h_final) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i < hl.n) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int n = hl.nb[i] * 32 + acc_row(r, lane), p = hl.pb[i] * 32 + col;
-            h_final[sbase + n * SP + p] = hacc[i][r];
-          }
-        }
-    }
-  }
-
-  // y of the last chunk out of sZ
-  if constexpr (C::STAGE_Z) {
-    if (nC > 0) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < C::XV; ++i) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        const int t = (nC - 1) * Q + s_;
-        if (t < L) {
-          Vec<T> o;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) o.set(e, S.sG[s_][cv * VE + e]);
-          st16(yb + (row0 + t) * y_stride + cv * VE, o);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------- scan kernel
-// Chunk sizes 64 and 128. Per chunk, three phases separated by barriers:
-//  S1 (all waves) stage the chunk: y of the previous chunk out of LDS (coalesced), raw z
-//     in, x^T and (w x)^T hi/lo, the chunk's dt / pi / v record; prefetch the next chunk.
-//  S2 Y waves: Y^T = H^T C^T for their tiles, scaled by exp2(lambda_t), and SiLU(z) into
-//     registers. H waves: the masked decay tiles M^T of the chunk (hi/lo) into LDS, each
-//     built once for all Y waves.
-//  S3 Y waves: Y^T += X^T M^T and the gated epilogue into LDS. H waves: H = exp2(lambda_end)
-//     H + B^T (w x), then the new state (bf16 hi/lo) into LDS for the next chunk.
-// Ownership: Y wave y holds two Y^T tiles (token blocks tb, one p-block) whose triangle
-// work adds up to the same amount on every wave; H wave w holds two state tiles of one
-// p-block. Each SIMD runs one Y wave and one H wave.
-//
-// Decay bookkeeping (log2 units, lambda_t = sum of dt*A*log2e from the chunk start through
-// t, blocks of 32 tokens with totals tot_k and in-block prefixes pi_t):
-//   exp2(lambda_t) = exp2(sum_{k<blk(t)} tot_k + pi_t)
-//   w_s = exp2(lambda_end - lambda_s) dt_s = v_s exp2(sum_{k>blk(s)} tot_k)
-//   decay s -> t across blocks si < tb = v_s exp2(sum_{si<k<tb} tot_k) exp2(pi_t)
-template <int Q> struct Own;
-template <> struct Own<64> {
-  static constexpr int NY = 1;
-  static constexpr int NB = 1;   // M tiles built per H wave (at most)
-  __device__ static int tb(int y, int) { return y >> 1; }
-  __device__ static int build(int w, int) { return w < 3 ? w : -1; }
-};
-template <> struct Own<128> {
-  static constexpr int NY = 2;
-  static constexpr int NB = 3;
-  __device__ static int tb(int y, int i) { return y < 2 ? (i ? 3 : 0) : (i ? 2 : 1); }
-  // lower-triangle tile k = tb (tb + 1) / 2 + si: H wave w builds diagonal tile w and one
-  // or two of the off-diagonal tiles 1, 3, 4, 6, 7, 8
-  __device__ static int build(int w, int i) {
-    if (i == 0) return w * (w + 3) / 2;
-    if (i == 1) return w == 0 ? 1 : w == 1 ? 3 : w == 2 ? 4 : 6;
-    return w == 0 ? 8 : w == 1 ? 7 : -1;
-  }
-};
-
-template <typename T, int Q>
-struct ScanSmem {
-  using C = Cfg<T, Q>;
-  T sXt[SP][C::LDQ];                        // x^T (k = s): A operand of Y^T += X^T M^T
-  T sXW[SP][C::LDQ];                        // (w x)^T hi: B operand of the state update
-  T sXWlo[C::SPLIT ? SP : 1][C::LDQ];       //        lo
-  T sHt[SP][C::LDN];                        // H^T hi: A operand of Y^T = H^T C^T
-  T sHtlo[C::SPLIT ? SP : 1][C::LDN];       //     lo
-  T sZ[Q][SP];                              // z of the chunk, then y (zpos layout)
-  Frag<T> sM[C::NTILES][2][64];             // M^T tiles in B-operand order [tile][k step][lane]
-  Frag<T> sMlo[C::SPLIT ? C::NTILES : 1][2][64];
-  float sRec[3 * Q];                        // dt | pi | v of the chunk
-};
-
-// Element (t, p) of the z / y tile sits at column zpos(t, p): 4-element groups XOR-ed with a
-// key of the token, so that the epilogue's 4-element accesses (32 tokens x one column group
-// per instruction) hit distinct banks. 16-byte staging vectors stay whole; with bf16 the two
-// halves of a vector trade places when bit 2 of the key is set.
-template <typename T>
-__device__ __forceinline__ int zkey(int t) {
-  return 4 * ((sizeof(T) == 2 ? t >> 1 : t) & 15);
-}
-template <typename T>
-__device__ __forceinline__ int zpos(int t, int p) { return p ^ zkey<T>(t); }
-
-template <typename T>
-__device__ __forceinline__ Vec<T> half_swap(const Vec<T>& v, bool swap) {
-  if constexpr (sizeof(T) == 2) {
-    Vec<T> r;
-    r.v = swap ? __builtin_shufflevector(v.v, v.v, 4, 5, 6, 7, 0, 1, 2, 3) : v.v;
-    return r;
-  } else {
-    return v;
-  }
-}
-
-template <typename T, int Q>
-__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
-                     const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
-                     T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                     int L, int H, int G) {
-  using C = Cfg<T, Q>;
-  using OW = Own<Q>;
-  constexpr int VE = C::VE;
-  constexpr int NTB = C::NTB;
-  extern __shared__ __align__(16) unsigned char scan_smem[];
-  ScanSmem<T, Q>& S = *reinterpret_cast<ScanSmem<T, Q>*>(scan_smem);
-  const float* sDt = S.sRec;
-  const float* sPi = S.sRec + Q;
-  const float* sV = S.sRec + 2 * Q;
-
-  const int id = xcd_local_order(blockIdx.x, gridDim.x);
-  const int b = id / H, h = id % H;
-  const int g = h / (H / G);
-  const int nC = (L + Q - 1) / Q;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, g2 = lane >> 5;
-  const bool ywave = wave < 4;
-
-  const int64_t row0 = (int64_t)b * L;
-  const T* xb = x + h * SP;
-  const T* zb = z ? z + h * SP : nullptr;
-  T* yb = y + h * SP;
-  const float Dh = D ? D[h] : 0.f;
-  const unsigned char* wsg = ws + (size_t)(b * G + g) * nC * C::REC_BYTES;
-  const float* hrec = reinterpret_cast<const float*>(
-      ws + (size_t)G * nC * C::REC_BYTES * (size_t)(gridDim.x / H) +
-      ((size_t)b * H + h) * nC * C::HREC_BYTES);
-
-  // ------------------------------------------------------------ staging registers
-  // x and z: XV 16-byte vectors per thread. With PAIRS, vectors 2i and 2i+1 are tokens
-  // 2sp and 2sp+1 of one 16-byte column, 8 lanes per token row (coalesced loads), so x^T
-  // and (w x)^T go to LDS as 32-bit token pairs.
-  Vec<T> rX[C::XV], rZ[C::XV];
-  float rV[C::XV];                  // v of each staged token
-  float rRec;                       // one word of the dt | pi | v record (threads < 3Q)
-  float tot[NTB];                   // block totals of the chunk (wave-uniform)
-  auto xcoord = [&](int i, int& s, int& cv) {
-    constexpr int VPR = SP / VE;  // vectors per token row
-    if constexpr (C::PAIRS) {
-      const int u = tid + SCAN_THREADS * (i >> 1);
-      s = 2 * (u / VPR) + (i & 1);
-      cv = u % VPR;
-    } else {
-      const int v = tid + SCAN_THREADS * i;
-      s = v / VPR;
-      cv = v % VPR;
-    }
-  };
-  auto load_chunk = [&](int c) {
-    const int t0 = c * Q;
-    const float* hr = hrec + (size_t)c * (3 * Q);
-    // Rows past the end of the sequence load the last row instead (finite values; their
-    // dt and v are zero, so they add nothing), which keeps the loads unconditional: a
-    // guarded load makes the compiler wait for it on the spot.
-#pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      int s_, cv;
-      xcoord(i, s_, cv);
-      const int t = min(t0 + s_, L - 1);
-      rX[i] = ld16(xb + (row0 + t) * x_stride + cv * VE);
-      if (zb) rZ[i] = ld16(zb + (row0 + t) * z_stride + cv * VE);
-      rV[i] = hr[2 * Q + s_];
-    }
-    if (tid < 3 * Q) rRec = hr[tid];
-#pragma unroll
-    for (int k = 0; k < NTB; ++k) tot[k] = hr[Q + 32 * k + 31];
-  };
-  // y of chunk c-1 out of sZ, thread by thread over the same vectors it then refills
-  auto flush_y = [&](int c, int s_, int cv) {
-    const int t = (c - 1) * Q + s_;
-    const int key = zkey<T>(s_);
-    const Vec<T> v = ld16(&S.sZ[s_][(cv * VE) ^ (key & ~(VE - 1))]);
-    if (t < L) st16(yb + (row0 + t) * y_stride + cv * VE, half_swap<T>(v, (key & 4) && VE == 8));
-  };
-
-  // ------------------------------------------------------------ phase S1
-  // Leaves the chunk's block totals in `ctot` for the rest of the chunk.
-  float ctot[NTB];
-  auto stage = [&](int c) {
-#pragma unroll
-    for (int k = 0; k < NTB; ++k) ctot[k] = tot[k];
-#pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      int s_, cv;
-      xcoord(i, s_, cv);
-      if (c > 0) flush_y(c, s_, cv);
-      if (zb) {
-        const int key = zkey<T>(s_);
-        st16(&S.sZ[s_][(cv * VE) ^ (key & ~(VE - 1))], half_swap<T>(rZ[i], (key & 4) && VE == 8));
-      }
-    }
-    if (tid < 3 * Q) S.sRec[tid] = rRec;
-    // w_s = v_s exp2(decay from the end of s's block to the end of the chunk); written as
-    // a sum of selects (a table of the per-block factors indexed by the lane's block would
-    // go through scratch memory)
-    auto w_of = [&](int i, int s_) {
-      const int blk = s_ >> 5;
-      float after = 0.f;
-#pragma unroll
-      for (int k = 1; k < NTB; ++k) after += k > blk ? ctot[k] : 0.f;
-      return rV[i] * exp2_hw(after);
-    };
-    if constexpr (C::PAIRS) {
-#pragma unroll
-      for (int i = 0; i < C::XV; i += 2) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        const float w0 = w_of(i, s_), w1 = w_of(i + 1, s_ + 1);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const T x0 = rX[i].v[e], x1 = rX[i + 1].v[e];
-          const float v0 = to_f(x0) * w0, v1 = to_f(x1) * w1;
-          const T h0_ = from_f<T>(v0), h1_ = from_f<T>(v1);
-          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
-          st_pair(&S.sXt[p][sw], x0, x1);
-          st_pair(&S.sXW[p][sw], h0_, h1_);
-          if constexpr (C::SPLIT)
-            st_pair(&S.sXWlo[p][sw], from_f<T>(v0 - to_f(h0_)), from_f<T>(v1 - to_f(h1_)));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::XV; ++i) {
-        int s_, cv;
-        xcoord(i, s_, cv);
-        const float w0 = w_of(i, s_);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const T x0 = rX[i].v[e];
-          const float v0 = to_f(x0) * w0;
-          const T h0_ = from_f<T>(v0);
-          const int p = cv * VE + e, sw = xsw<Q>(p, s_);
-          S.sXt[p][sw] = x0;
-          S.sXW[p][sw] = h0_;
-          if constexpr (C::SPLIT) S.sXWlo[p][sw] = from_f<T>(v0 - to_f(h0_));
-        }
-      }
-    }
-    if (c + 1 < nC) load_chunk(c + 1);
-  };
-
-  // The two roles run separate chunk loops with the same barrier sequence (three barriers
-  // per chunk), so each role's registers are allocated on their own.
-  if (ywave) {
-    // ========================================================== Y waves: outputs
-    const int pb = wave & 1;
-    const int prow = pb * 32 + col;
-    Frag<T> cf[OW::NY][C::KS_N];        // C operand frags of the owned token blocks
-    auto fetch = [&](int c) {
-      const unsigned char* cfp = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES;
-#pragma unroll
-      for (int i = 0; i < OW::NY; ++i)
-#pragma unroll
-        for (int j = 0; j < C::KS_N; ++j)
-          cf[i][j] = ld_frag<T>(cfp + ((size_t)(OW::tb(wave, i) * C::KS_N + j) * 64 + lane) * C::FB);
-    };
-    if (nC > 0) {
-      load_chunk(0);
-      fetch(0);
-    }
-    for (int c = 0; c < nC; ++c) {
-      stage(c);
-      __syncthreads();
-      // ---- S2: carried state, scaled by exp2(lambda_t); gate values
-      f32x16 acc[OW::NY];
-      float gz[OW::NY][16];
-#pragma unroll
-      for (int i = 0; i < OW::NY; ++i) {
-        acc[i] = (f32x16){};
-#pragma unroll
-        for (int j = 0; j < C::KS_N; ++j) {
-          mma(acc[i], frag_contig(&S.sHt[prow][16 * j], g2), cf[i][j]);
-          if constexpr (C::SPLIT) mma(acc[i], frag_contig(&S.sHtlo[prow][16 * j], g2), cf[i][j]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < OW::NY; ++i) {
-        const int tb = OW::tb(wave, i);
-        const int tl = tb * 32 + col;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          if (zb) {
-            const Raw4<T> zz = ld4(&S.sZ[tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gz[i][4 * r4 + q] = silu_fast(zz.get(q));
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gz[i][4 * r4 + q] = 1.f;
-          }
-        }
-        float before = 0.f;
-#pragma unroll
-        for (int k = 0; k < NTB - 1; ++k)
-          if (k < tb) before += ctot[k];
-        const float et = exp2_hw(before + sPi[tl]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= et;
-      }
-      __syncthreads();
-      if (c + 1 < nC) fetch(c + 1);
-      // ---- S3: intra-chunk part from the M^T tiles, then y = acc * SiLU(z) into sZ
-#pragma unroll
-      for (int i = 0; i < OW::NY; ++i) {
-        const int tb = OW::tb(wave, i);
-        const int k0 = tb * (tb + 1) / 2;
-        for (int si = 0; si <= tb; ++si) {
-#pragma unroll
-          for (int m2 = 0; m2 < 2; ++m2) {
-            const Frag<T> xa = frag_accrows_sw<Q>(S.sXt[prow], prow, si * 32 + 16 * m2, g2);
-            mma(acc[i], xa, S.sM[k0 + si][m2][lane]);
-            if constexpr (C::SPLIT) mma(acc[i], xa, S.sMlo[k0 + si][m2][lane]);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < OW::NY; ++i) {
-        const int tl = OW::tb(wave, i) * 32 + col;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int r = 4 * r4;
-          st4(&S.sZ[tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[i][r] * gz[i][r],
-              acc[i][r + 1] * gz[i][r + 1], acc[i][r + 2] * gz[i][r + 2], acc[i][r + 3] * gz[i][r + 3]);
-        }
-      }
-      __syncthreads();
-    }
-  } else {
-    // ========================================================== H waves: M^T and state
-    const int hw = wave - 4;
-    const int pb = hw & 1;
-    const int prow = pb * 32 + col;
-    const int nb0 = hw >> 1;            // row blocks nb0 and nb0 + 2
-    f32x16 hacc[2];
-    Frag<T> af[2][C::KS_Q];             // B^T operand frags of the two row blocks
-    f32x16 gram[OW::NB];                // Gram tiles of the M^T tiles this wave builds
-    const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
-        hacc[i][r] = h0 ? h0[sbase + n * SP + prow] : 0.f;
-      }
-    auto fetch_bt = [&](int c) {
-      const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < C::KS_Q; ++j)
-          af[i][j] = ld_frag<T>(btf + ((size_t)((nb0 + 2 * i) * C::KS_Q + j) * 64 + lane) * C::FB);
-    };
-    auto fetch_gram = [&](int c) {
-      const float* gt = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES);
-#pragma unroll
-      for (int s = 0; s < OW::NB; ++s) {
-        const int k = OW::build(hw, s);
-        if (k >= 0) gram[s] = load_tile16(gt + (size_t)k * 1024, lane);
-      }
-    };
-    auto write_state = [&]() {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = (nb0 + 2 * i) * 32 + 8 * r4 + 4 * g2;
-          float v[4], lo[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k] = hacc[i][4 * r4 + k];
-            lo[k] = v[k] - to_f(from_f<T>(v[k]));
-          }
-          st4(&S.sHt[prow][n], v[0], v[1], v[2], v[3]);
-          if constexpr (C::SPLIT) st4(&S.sHtlo[prow][n], lo[0], lo[1], lo[2], lo[3]);
-        }
-    };
-    // M^T tile k = (tb, si) in B-operand order: Gram tile G^T[s][t] times the decay from
-    // token s to token t and dt_s, zero above the diagonal, D on the diagonal.
-    auto build = [&](int k, const f32x16& gt) {
-      const int tb = tile_tb(k), si = k - tb * (tb + 1) / 2;
-      const int tl = tb * 32 + col;
-      Frag<T> mh[2], ml[2];
-      if (si < tb) {
-        float mid = 0.f;
-#pragma unroll
-        for (int kk = 1; kk < NTB - 1; ++kk)
-          if (kk > si && kk < tb) mid += ctot[kk];
-        const float ut = exp2_hw(mid + sPi[tl]);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 vs = *reinterpret_cast<const f32x4*>(&sV[si * 32 + 8 * r4 + 4 * g2]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, gt[r] * (vs[q] * ut));
-          }
-        }
-      } else {
-        const float pit = sPi[tl];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int s0 = tb * 32 + 8 * r4 + 4 * g2;
-          const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[s0]);
-          const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[s0]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * r4 + q;
-            float v = (s0 + q <= tl) ? gt[r] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
-            if (s0 + q == tl) v += Dh;
-            split_set<T>(mh[r >> 3], ml[r >> 3], r & 7, v);
-          }
-        }
-      }
-#pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        S.sM[k][m2][lane] = mh[m2];
-        if constexpr (C::SPLIT) S.sMlo[k][m2][lane] = ml[m2];
-      }
-    };
-    write_state();
-    if (nC > 0) load_chunk(0);
-    for (int c = 0; c < nC; ++c) {
-      fetch_gram(c);
-      stage(c);
-      __syncthreads();
-      // ---- S2: the chunk's M^T tiles
-#pragma unroll
-      for (int s = 0; s < OW::NB; ++s) {
-        const int k = OW::build(hw, s);
-        if (k >= 0) build(k, gram[s]);
-      }
-      fetch_bt(c);
-      __syncthreads();
-      // ---- S3: state update, then publish it for the next chunk
-      float lam = 0.f;
-#pragma unroll
-      for (int k = 0; k < NTB; ++k) lam += ctot[k];
-      const float eend = exp2_hw(lam);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
-#pragma unroll
-      for (int j = 0; j < C::KS_Q; ++j) {
-        const int k0 = xsw<Q>(prow, 16 * j + 8 * g2);
-        const Frag<T> bh = frag_contig(&S.sXW[prow][k0], 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) mma(hacc[i], af[i][j], bh);
-        if constexpr (C::SPLIT) {
-          const Frag<T> bl = frag_contig(&S.sXWlo[prow][k0], 0);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) mma(hacc[i], af[i][j], bl);
-        }
-      }
-      write_state();
-      __syncthreads();
-    }
-    if (h_final) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = (nb0 + 2 * i) * 32 + acc_row(r, lane);
-          h_final[sbase + n * SP + prow] = hacc[i][r];
-        }
-    }
-  }
-
-  // y of the last chunk out of sZ
-  if (nC > 0) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      int s_, cv;
-      xcoord(i, s_, cv);
-      flush_y(nC, s_, cv);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------- pipelined scan, chunk 64
-// bf16 io, chunk 64, 16 waves. One barrier per chunk. In iteration c:
+// The one scan of the library: bf16 or fp32 io, whatever chunk length the call names (the
+// chunk is a tiling choice that does not change the result; the scan tiles at 64 tokens).
+// 16 waves, one barrier per chunk. In iteration c:
 //   Y waves 0..3:   chunk c's outputs, Y^T tile (token block y >> 1, p-block y & 1):
 //                   H^T C^T scaled by exp2(lambda_t), plus X^T M^T, gated, into sZ.
 //   H waves 4..7:   the state to H_c (H wave w: state rows 32 w .. 32 w + 31, both p-blocks),
@@ -1391,23 +422,38 @@ void ssd_scan_kernel(const T* __restrict__ x, int64_t x_stride, const float* __r
 // ahead (three buffers). Four waves per SIMD (one of each kind plus two helpers) hide each
 // other's latencies. LDS tiles are unpadded, with XOR swizzles that keep the 16-byte MFMA
 // operand reads of H^T and (w x)^T (32 rows per instruction) free of bank conflicts.
+// fp32 io runs the same roles with fp32 MFMAs (32x32x2, no hi/lo split). Its z and y move
+// between HBM and the Y waves' registers (fp32 z and y tiles would not fit LDS beside the
+// rest), and each chunk's contribution to the state is summed in an accumulator of its own
+// before it is added to the decayed state, so that the state's rounding error grows with
+// the number of chunks rather than with the number of tokens.
 constexpr int P64 = 64;
 constexpr int P64_THREADS = 1024;
 __device__ __forceinline__ int xs64(int p, int s) { return s ^ (8 * ((p ^ (p >> 2)) & 7)); }
 __device__ __forceinline__ int hsw(int p, int n) { return n ^ (8 * (p & 15)); }
 
+// Element (t, p) of the bf16 z / y tile sits at column zpos(t, p): 4-element groups XOR-ed
+// with a key of the token, so that the epilogue's 4-element accesses (32 tokens x one column
+// group per instruction) hit distinct banks; the staging's 4-element groups stay whole.
+__device__ __forceinline__ int zpos(int t, int p) { return p ^ (4 * ((t >> 1) & 15)); }
+
+// LDS of the scan; the lo halves and the z / y tile exist only for bf16 io (a token-sized
+// placeholder otherwise).
+template <typename T>
 struct Pipe64Smem {
-  bf16 sXt[2][SP][P64];                     // x^T by chunk parity (xs64)
-  bf16 sXW[2][SP][P64];                     // (w x)^T hi (xs64)
-  bf16 sXWlo[2][SP][P64];                   //         lo
-  bf16 sZ[2][P64][SP];                      // z, then y (zpos)
-  Frag<bf16> sM[2][3][2][64];               // M^T tiles [parity][tile][k step][lane]
-  Frag<bf16> sMlo[2][3][2][64];
-  bf16 sHt[2][SP][SN];                      // H^T hi by chunk parity (hsw)
-  bf16 sHtlo[2][SP][SN];                    //     lo
-  float sRec[3][3 * P64];                   // dt | pi | v, chunk c in slot c % 3
-  int4 sInfo[5];                            // packed batch: chunk info, chunk c in slot c % 5
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  T sXt[2][SP][P64];                                            // x^T by chunk parity (xs64)
+  T sXW[2][SP][P64];                                            // (w x)^T (bf16: hi) (xs64)
+  bf16 sXWlo[SPLIT ? 2 : 1][SPLIT ? SP : 1][SPLIT ? P64 : 8];   //         lo
+  bf16 sZ[SPLIT ? 2 : 1][SPLIT ? P64 : 1][SPLIT ? SP : 8];      // z, then y (zpos)
+  Frag<T> sM[2][3][2][64];                     // M^T tiles [parity][tile][k step][lane]
+  Frag<bf16> sMlo[SPLIT ? 2 : 1][3][2][SPLIT ? 64 : 1];
+  T sHt[2][SP][SN];                                             // H^T (bf16: hi) by parity (hsw)
+  bf16 sHtlo[SPLIT ? 2 : 1][SPLIT ? SP : 1][SPLIT ? SN : 8];    //     lo
+  float sRec[3][4 * P64];                      // dt | pi_hi | v | pi_lo, chunk c in slot c % 3
+  int4 sInfo[5];                               // packed batch: chunk info, chunk c in slot c % 5
 };
+static_assert(sizeof(Pipe64Smem<float>) <= 160 * 1024 && sizeof(Pipe64Smem<bf16>) <= 160 * 1024, "LDS");
 
 // With CONV, x is the raw xBC tensor (x_stride its row stride): the helper waves apply the
 // conv to the head's x channels as they stage them, and at the end write the new conv
@@ -1419,18 +465,34 @@ struct Pipe64Smem {
 // initial state, which they publish in place of the carried one; the helper waves take
 // each chunk's rows from the per-chunk info and, at a sequence start, the conv history
 // from the pool. The new conv histories are written at the end.
-template <bool CONV, bool VARLEN = false>
+// The phase profile (STAMP): s_memtime at phase boundaries, held in program order by
+// scheduling barriers. Per wave: [0] cycles of the whole chunk loop, [1] cycles of the
+// wave's first contraction phase summed over chunks (Y waves: H^T C^T; H waves:
+// B^T (w x)), [2] of its second (Y waves: X^T M^T), [3] a sink that keeps the values read
+// to close a phase alive. A phase runs from before its first operand read to after the
+// first read of its accumulator.
+__device__ __forceinline__ uint64_t phase_stamp() {
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t t = __builtin_amdgcn_s_memtime();
+  __builtin_amdgcn_sched_barrier(0);
+  return t;
+}
+constexpr int STAMP_SLOTS = 4;
+
+template <typename T, bool CONV, bool VARLEN = false, bool STAMP = false>
 __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
-                       const bf16* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
-                       bf16* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                       int Lrows, int H, int G, ConvArgs cv, VarlenDev vd) {
+void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
+                       const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
+                       T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
+                       int Lrows, int H, int G, ConvArgs cv, VarlenDev vd, uint64_t* __restrict__ stamps) {
   static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
-  using T = bf16;
+  static_assert(!CONV || sizeof(T) == 2, "the conv runs inside the scan for bf16 io");
+  static_assert(!STAMP || (CONV && !VARLEN), "the phase profile covers the one-call prefill");
   using C = Cfg<T, P64>;
   constexpr int Q = P64;
+  constexpr bool SPLIT = C::SPLIT;
   extern __shared__ __align__(16) unsigned char scan_smem[];
-  Pipe64Smem& S = *reinterpret_cast<Pipe64Smem*>(scan_smem);
+  Pipe64Smem<T>& S = *reinterpret_cast<Pipe64Smem<T>*>(scan_smem);
 
   const int id = xcd_local_order(blockIdx.x, gridDim.x);
   const int b = id / H, h = id % H;
@@ -1504,56 +566,91 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
   // ring, which holds chunks c - 1 .. c + 2 during iteration c (a global read in the loop would
   // be a scalar load, and a pending scalar load makes every LDS wait a full drain)
   [[maybe_unused]] auto info_at = [&](int c, bool ring) -> int4 { return ring ? S.sInfo[c % 5] : cinfo[c]; };
+  [[maybe_unused]] uint64_t st_loop = 0, st_a = 0, st_b = 0;
+  [[maybe_unused]] float st_sink = 0.f;
+  [[maybe_unused]] auto stamps_out = [&]() {
+    if constexpr (STAMP) {
+      if (lane == 0) {
+        uint64_t* o = stamps + ((size_t)blockIdx.x * (P64_THREADS / 64) + wave) * STAMP_SLOTS;
+        o[0] = st_loop;
+        o[1] = st_a;
+        o[2] = st_b;
+        o[3] = __float_as_uint(st_sink);
+      }
+    }
+  };
 
   if (wave < 4) {
     // ========================================================== Y waves
     const int tb = wave >> 1, pb = wave & 1;
     const int prow = pb * 32 + col, tl = tb * 32 + col;
-    Frag<T> cf[C::KS_N];
+    // the chunk's C fragments: bf16 holds them in registers, requested a chunk ahead; fp32
+    // (twice the registers) loads each k step's fragment where it is used
+    auto cf_at = [&](int c, int j) {
+      return wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES +
+             ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB;
+    };
+    Frag<T> cf[SPLIT ? C::KS_N : 1];
     auto fetch_c = [&](int c) {
-      const unsigned char* cfp = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES;
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int j = 0; j < C::KS_N; ++j)
-        cf[j] = ld_frag<T>(cfp + ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB);
+        for (int j = 0; j < C::KS_N; ++j) cf[j] = ld_frag<T>(cf_at(c, j));
+      }
     };
     if (nC > 0) fetch_c(0);
     __syncthreads();
     __syncthreads();
+    if constexpr (STAMP) st_loop = phase_stamp();
     for (int c = 0; c < nC; ++c) {
       const int cur = c & 1, prv = cur ^ 1;
+      [[maybe_unused]] uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+      if constexpr (STAMP) s0 = phase_stamp();
       // ---- carried state, scaled by exp2(lambda_t)
       f32x16 acc = {};
       {
-        // four k steps of H^T hi / lo in flight
-        Frag<T> ha[4], la[4];
+        // four k steps of H^T (hi / lo) in flight
+        Frag<T> ha[4];
+        Frag<bf16> la[SPLIT ? 4 : 1];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = hsw(prow, 16 * j + 8 * g2);
           ha[j] = frag_contig(&S.sHt[prv][prow][n], 0);
-          la[j] = frag_contig(&S.sHtlo[prv][prow][n], 0);
+          if constexpr (SPLIT) la[j] = frag_contig(&S.sHtlo[prv][prow][n], 0);
         }
 #pragma unroll
         for (int j = 0; j < C::KS_N; ++j) {
-          mma(acc, ha[j & 3], cf[j]);
-          mma(acc, la[j & 3], cf[j]);
+          if constexpr (SPLIT) {
+            mma(acc, ha[j & 3], cf[j]);
+            mma(acc, la[j & 3], cf[j]);
+          } else {
+            mma(acc, ha[j & 3], ld_frag<T>(cf_at(c, j)));
+          }
           if (j + 4 < C::KS_N) {
             const int n = hsw(prow, 16 * (j + 4) + 8 * g2);
             ha[j & 3] = frag_contig(&S.sHt[prv][prow][n], 0);
-            la[j & 3] = frag_contig(&S.sHtlo[prv][prow][n], 0);
+            if constexpr (SPLIT) la[j & 3] = frag_contig(&S.sHtlo[prv][prow][n], 0);
           }
         }
       }
       const float et = exp2_hw((tb ? tot_of(c, 0) : 0.f) + S.sRec[c % 3][Q + tl]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] *= et;
+      if constexpr (STAMP) s1 = phase_stamp();
       fetch_c(min(c + 1, nC - 1));
-      // z of this wave's outputs, read ahead of the intra-chunk MFMAs
+      // z of this wave's outputs, read ahead of the intra-chunk MFMAs (fp32: from HBM, the
+      // rows past the end of the sequence clamped to its last)
       Raw4<T> zz[4];
+      [[maybe_unused]] const int nval = Lrows - c * Q;
+      [[maybe_unused]] const int64_t yrow = row0 + (int64_t)c * Q + min(tl, nval - 1);
       if (z) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) zz[r4] = ld4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          if constexpr (SPLIT) zz[r4] = ld4(&S.sZ[cur][tl][zpos(tl, pb * 32 + 8 * r4 + 4 * g2)]);
+          else zz[r4] = ld4(z + yrow * z_stride + h * SP + pb * 32 + 8 * r4 + 4 * g2);
+        }
       }
       // ---- intra-chunk part: Y^T += X^T M^T over source blocks si <= tb
+      if constexpr (STAMP) s2 = phase_stamp();
 #pragma unroll
       for (int si = 0; si < 2; ++si) {
         if (si <= tb) {
@@ -1564,28 +661,42 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
             const Frag<T> xa = frag_accrows2(&S.sXt[cur][prow][xs64(prow, sa)],
                                              &S.sXt[cur][prow][xs64(prow, sa + 8)]);
             mma(acc, xa, S.sM[cur][k][m2][lane]);
-            mma(acc, xa, S.sMlo[cur][k][m2][lane]);
+            if constexpr (SPLIT) mma(acc, xa, S.sMlo[cur][k][m2][lane]);
           }
         }
       }
-      // ---- gate and y into sZ[cur] (in place of z)
+      if constexpr (STAMP) {
+        st_sink += acc[0];
+        s3 = phase_stamp();
+      }
+      // ---- gate; y into sZ[cur] in place of z (bf16), or to HBM (fp32)
       if (z) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int r = 4 * r4;
-          st4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[r] * silu_fast(zz[r4].get(0)),
-              acc[r + 1] * silu_fast(zz[r4].get(1)), acc[r + 2] * silu_fast(zz[r4].get(2)),
-              acc[r + 3] * silu_fast(zz[r4].get(3)));
-        }
-      } else {
+        for (int r = 0; r < 16; ++r) acc[r] *= silu_fast(zz[r >> 2].get(r & 3));
+      }
+      if constexpr (SPLIT) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int r = 4 * r4;
-          st4(&S.sZ[cur][tl][zpos<T>(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[r], acc[r + 1], acc[r + 2],
-              acc[r + 3]);
+          st4(&S.sZ[cur][tl][zpos(tl, pb * 32 + 8 * r4 + 4 * g2)], acc[r], acc[r + 1], acc[r + 2], acc[r + 3]);
+        }
+      } else if (tl < nval) {
+        T* yr = y + yrow * y_stride + h * SP + pb * 32 + 4 * g2;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * r4;
+          st4(yr + 8 * r4, acc[r], acc[r + 1], acc[r + 2], acc[r + 3]);
         }
       }
+      if constexpr (STAMP) {
+        st_a += s1 - s0;
+        st_b += s3 - s2;
+      }
       __syncthreads();
+    }
+    if constexpr (STAMP) {
+      st_loop = phase_stamp() - st_loop;
+      stamps_out();
     }
   } else if (wave < 8) {
     // ========================================================== H waves
@@ -1627,10 +738,15 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int n = hsw(prow, hw * 32 + 8 * r4 + 4 * g2);
-          const Split2 a = split2(hacc[i][4 * r4], hacc[i][4 * r4 + 1]);
-          const Split2 d = split2(hacc[i][4 * r4 + 2], hacc[i][4 * r4 + 3]);
-          *reinterpret_cast<uint2*>(&S.sHt[buf][prow][n]) = make_uint2(a.hi, d.hi);
-          *reinterpret_cast<uint2*>(&S.sHtlo[buf][prow][n]) = make_uint2(a.lo, d.lo);
+          if constexpr (SPLIT) {
+            const Split2 a = split2(hacc[i][4 * r4], hacc[i][4 * r4 + 1]);
+            const Split2 d = split2(hacc[i][4 * r4 + 2], hacc[i][4 * r4 + 3]);
+            *reinterpret_cast<uint2*>(&S.sHt[buf][prow][n]) = make_uint2(a.hi, d.hi);
+            *reinterpret_cast<uint2*>(&S.sHtlo[buf][prow][n]) = make_uint2(a.lo, d.lo);
+          } else {
+            *reinterpret_cast<f32x4*>(&S.sHt[buf][prow][n]) =
+                (f32x4){hacc[i][4 * r4], hacc[i][4 * r4 + 1], hacc[i][4 * r4 + 2], hacc[i][4 * r4 + 3]};
+          }
         }
       }
     };
@@ -1638,23 +754,47 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     if (nC > 0) fetch_bt(0);
     __syncthreads();
     __syncthreads();
+    if constexpr (STAMP) st_loop = phase_stamp();
     for (int c = 0; c < nC; ++c) {
       const int cur = c & 1;
+      [[maybe_unused]] uint64_t s0 = 0;
+      if constexpr (STAMP) s0 = phase_stamp();
       // ---- state update to H_c, published into sHt[cur]
       const float eend = exp2_hw(tot_of(c, 0) + tot_of(c, 1));
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
+          for (int r = 0; r < 16; ++r) hacc[i][r] *= eend;
 #pragma unroll
-      for (int j = 0; j < C::KS_Q; ++j) {
+        for (int j = 0; j < C::KS_Q; ++j) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int prow = i * 32 + col;
-          const int k0 = xs64(prow, 16 * j + 8 * g2);
-          mma(hacc[i], af[j], frag_contig(&S.sXW[cur][prow][k0], 0));
-          mma(hacc[i], af[j], frag_contig(&S.sXWlo[cur][prow][k0], 0));
+          for (int i = 0; i < 2; ++i) {
+            const int prow = i * 32 + col;
+            const int k0 = xs64(prow, 16 * j + 8 * g2);
+            mma(hacc[i], af[j], frag_contig(&S.sXW[cur][prow][k0], 0));
+            mma(hacc[i], af[j], frag_contig(&S.sXWlo[cur][prow][k0], 0));
+          }
         }
+      } else {
+        // the chunk's contribution in its own accumulator, then H = eend H + S_c
+        f32x16 sacc[2] = {};
+#pragma unroll
+        for (int j = 0; j < C::KS_Q; ++j) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int prow = i * 32 + col;
+            mma(sacc[i], af[j], frag_contig(&S.sXW[cur][prow][xs64(prow, 16 * j + 8 * g2)], 0));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) hacc[i][r] = fmaf(hacc[i][r], eend, sacc[i][r]);
+      }
+      if constexpr (STAMP) {
+        st_sink += hacc[0][0] + hacc[1][0];
+        st_a += phase_stamp() - s0;
       }
       if constexpr (VARLEN) {
         // the next chunk starts a sequence: store this sequence's state in its entry, then take
@@ -1671,6 +811,10 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       publish(cur);
       fetch_bt(min(c + 1, nC - 1));
       __syncthreads();
+    }
+    if constexpr (STAMP) {
+      st_loop = phase_stamp() - st_loop;
+      stamps_out();
     }
     if constexpr (VARLEN) {
       if (nC > 0) {
@@ -1731,8 +875,8 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     // M^T tiles: helper waves 0, 1 build tile 0 (diagonal 0) in halves (k steps hm of 16
     // source tokens), waves 2, 3 tile 2 (diagonal 1); waves 4..7 build tile 1 (block 1 from
     // block 0, no exponentials) in quarters of 8 source tokens. Helper wave v runs on SIMD
-    // v % 4, so every SIMD gets half a diagonal tile and a quarter of the other. Waves 0..2
-    // also carry the dt / pi / v records (3Q words, a word a thread).
+    // v % 4, so every SIMD gets half a diagonal tile and a quarter of the other. Waves 0..3
+    // also carry the dt / pi_hi / v / pi_lo records (4Q words, a word a thread).
     const int kb = hv < 2 ? 0 : hv < 4 ? 2 : 1;
     const int hm = hv & 1, hq = hv & 3;
     // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
@@ -1755,7 +899,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
       // by the HIST role with each chunk's rows, from the chunk's place in the history area
       Raw4<T> rH[3];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) rH[k].v = (bf16x4){};
+      for (int k = 0; k < 3; ++k) rH[k].v = decltype(rH[k].v){};
       // VARLEN: ci is the info of chunk c (from the workspace in the prologue, from the ring in
       // the loop, read at the top of the iteration)
       auto load_set = [&](int c, int4 ci) {   // x and z of this thread's tokens
@@ -1781,7 +925,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         for (int k = 0; k < 2; ++k) {
           const uint32_t s = (uint32_t)min(s0 + k, lim);
           if constexpr (!CONV) rX[k] = ld4(xc + (s * xs + p0));
-          rZ[k] = ld4(zc + (s * zs + p0));
+          if constexpr (SPLIT) rZ[k] = ld4(zc + (s * zs + p0));
         }
         if constexpr (CONV) {
           // raw rows s0 - 3 .. s0 + 1 of the chunk, addressed from a base 3 rows back; past the
@@ -1803,12 +947,12 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         }
       };
       auto load_rec = [&](int c) {
-        if constexpr (REC) rRec = hrec[(size_t)c * (3 * Q) + htid];
+        if constexpr (REC) rRec = hrec[(size_t)c * C::HREC_WORDS + htid];
       };
       auto put_rec = [&](int c) {
         if constexpr (REC) S.sRec[c % 3][htid] = rRec;
       };
-      auto flush_y = [&](int c, bool full, int4 cf) {   // y of chunk c out of sZ[c & 1]
+      auto flush_y = [&](int c, bool full, int4 cf) {   // y of chunk c out of sZ[c & 1] (bf16)
         int64_t r0;
         int nval;
         if constexpr (VARLEN) {
@@ -1822,7 +966,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int s = s0 + k;
-          const Raw4<T> v = ld4(&S.sZ[c & 1][s][zpos<T>(s, p0)]);
+          const Raw4<bf16> v = ld4(&S.sZ[c & 1][s][zpos(s, p0)]);
           if (full || s < nval) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
         }
       };
@@ -1840,10 +984,12 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         bool first = decltype(first_tag)::value;
         if constexpr (VARLEN) first = (cs.y & INFO_FIRST) != 0;
         const int buf = c & 1;
-        if (z) {
+        if constexpr (SPLIT) {
+          if (z) {
 #pragma unroll
-          for (int k = 0; k < 2; ++k)
-            *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos<T>(s0 + k, p0)]) = rZ[k].v;
+            for (int k = 0; k < 2; ++k)
+              *reinterpret_cast<bf16x4*>(&S.sZ[buf][s0 + k][zpos(s0 + k, p0)]) = rZ[k].v;
+          }
         }
         // w_s = v_s exp2(decay from the end of s's block to the chunk end): block 0 -> tot_1
         const float* rec = S.sRec[c % 3];
@@ -1876,11 +1022,15 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const T x0 = xv[0][e], x1 = xv[1][e];
-          const Split2 v = split2(to_f(x0) * w0, to_f(x1) * w1);
           const int p = p0 + e, sw = xs64(p, s0);
           st_pair(&S.sXt[buf][p][sw], x0, x1);
-          *reinterpret_cast<uint32_t*>(&S.sXW[buf][p][sw]) = v.hi;
-          *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
+          if constexpr (SPLIT) {
+            const Split2 v = split2(to_f(x0) * w0, to_f(x1) * w1);
+            *reinterpret_cast<uint32_t*>(&S.sXW[buf][p][sw]) = v.hi;
+            *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
+          } else {
+            st_pair(&S.sXW[buf][p][sw], to_f(x0) * w0, to_f(x1) * w1);
+          }
         }
       };
       auto fetch_gram = [&](int c) {   // quads 2 hm, 2 hm + 1 (or quad hq) of the stored tile
@@ -1903,37 +1053,53 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
           const float* rec = S.sRec[c % 3];
           const float ut = exp2_hw(rec[Q + 32 + col]);
           const f32x4 vq = *reinterpret_cast<const f32x4*>(&rec[2 * Q + 8 * hq + 4 * g2]);
-          const Split2 a = split2(gram[0][0] * (vq[0] * ut), gram[0][1] * (vq[1] * ut));
-          const Split2 d = split2(gram[0][2] * (vq[2] * ut), gram[0][3] * (vq[3] * ut));
-          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sM[c & 1][1][hq >> 1][lane]) +
-                                    8 * (hq & 1)) = make_uint2(a.hi, d.hi);
-          *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sMlo[c & 1][1][hq >> 1][lane]) +
-                                    8 * (hq & 1)) = make_uint2(a.lo, d.lo);
+          if constexpr (SPLIT) {
+            const Split2 a = split2(gram[0][0] * (vq[0] * ut), gram[0][1] * (vq[1] * ut));
+            const Split2 d = split2(gram[0][2] * (vq[2] * ut), gram[0][3] * (vq[3] * ut));
+            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sM[c & 1][1][hq >> 1][lane]) +
+                                      8 * (hq & 1)) = make_uint2(a.hi, d.hi);
+            *reinterpret_cast<uint2*>(reinterpret_cast<unsigned char*>(&S.sMlo[c & 1][1][hq >> 1][lane]) +
+                                      8 * (hq & 1)) = make_uint2(a.lo, d.lo);
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&S.sM[c & 1][1][hq >> 1][lane]) + 4 * (hq & 1)) =
+                (f32x4){gram[0][0] * (vq[0] * ut), gram[0][1] * (vq[1] * ut), gram[0][2] * (vq[2] * ut),
+                        gram[0][3] * (vq[3] * ut)};
+          }
         } else {
           const float* rec = S.sRec[c % 3];
           const float* sDt = rec;
           const float* sPi = rec + Q;
-          // half hm of a diagonal tile (token block tb onto itself)
+          const float* sPl = rec + 3 * Q;
+          // half hm of a diagonal tile (token block tb onto itself); the decay from s to t is
+          // (pi_hi t - pi_hi s) + (pi_lo t - pi_lo s), accurate to the rounding of its own size
           const int tb = kb == 0 ? 0 : 1;
           const int tl = tb * 32 + col;
           float mv[8];
-          const float pit = sPi[tl];
+          const float pit = sPi[tl], plt = sPl[tl];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
             const f32x4 ps = *reinterpret_cast<const f32x4*>(&sPi[sr]);
+            const f32x4 pl = *reinterpret_cast<const f32x4*>(&sPl[sr]);
             const f32x4 ds = *reinterpret_cast<const f32x4*>(&sDt[sr]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              float v = (sr + q <= tl) ? gram[j][q] * exp2_hw(pit - ps[q]) * ds[q] : 0.f;
+              float v = (sr + q <= tl) ? gram[j][q] * exp2_hw((pit - ps[q]) + (plt - pl[q])) * ds[q] : 0.f;
               if (sr + q == tl) v += Dh;
               mv[4 * j + q] = v;
             }
           }
-          Frag<T> mh, ml;
-          frag_split(mv, mh, ml);
-          S.sM[c & 1][kb][hm][lane] = mh;
-          S.sMlo[c & 1][kb][hm][lane] = ml;
+          if constexpr (SPLIT) {
+            Frag<bf16> mh, ml;
+            frag_split(mv, mh, ml);
+            S.sM[c & 1][kb][hm][lane] = mh;
+            S.sMlo[c & 1][kb][hm][lane] = ml;
+          } else {
+            Frag<T> mf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mf.v[e] = mv[e];
+            S.sM[c & 1][kb][hm][lane] = mf;
+          }
         }
       };
       // prologue: records 0 and 1 into LDS; then chunk 0 staged and its tiles built, chunk 1's
@@ -1975,6 +1141,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         fetch_gram(min(1, nC - 1));
       }
       __syncthreads();
+      if constexpr (STAMP) st_loop = phase_stamp();
       for (int c = 0; c < nC; ++c) {
         // packed batch: the infos this iteration uses (chunks c - 1, c + 1, c + 2), read from
         // the ring now so that their latency hides behind the tile build
@@ -1988,7 +1155,9 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         // issues the same memory operations (the last stages a copy nobody reads).
         build(c + 1);
         fetch_gram(min(c + 2, nC - 1));
-        if (c >= 1) flush_y(c - 1, !VARLEN, im1);   // one sequence: chunk c - 1 < nC - 1 is full
+        if constexpr (SPLIT) {
+          if (c >= 1) flush_y(c - 1, !VARLEN, im1);   // one sequence: chunk c - 1 < nC - 1 is full
+        }
         stage(c + 1, std::false_type{}, ip1);
         put_rec(c + 2);
         load_set(min(c + 2, nC - 1), ip2);
@@ -1999,7 +1168,13 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
         }
         __syncthreads();
       }
-      if (nC > 0) flush_y(nC - 1, false, VARLEN ? S.sInfo[(nC - 1) % 5] : int4{});   // y of the last chunk
+      if constexpr (STAMP) {
+        st_loop = phase_stamp() - st_loop;
+        stamps_out();
+      }
+      if constexpr (SPLIT) {
+        if (nC > 0) flush_y(nC - 1, false, VARLEN ? S.sInfo[(nC - 1) % 5] : int4{});   // y of the last chunk
+      }
       if constexpr (CONV) {
         // the new history: the last 3 raw inputs of (history, sequence). One thread per 4
         // channels reads all 3 before writing any, so an in-place shift (L < 3) is safe; every
@@ -2054,8 +1229,7 @@ void ssd_scan64_kernel(const bf16* __restrict__ x, int64_t x_stride, const float
     using Hist = std::integral_constant<int, 1>;
     using Ring = std::integral_constant<int, 2>;
     if (VARLEN && hv == 0) helpers(Half{}, std::true_type{}, Hist{});
-    else if (hv < 3) helpers(Half{}, std::true_type{}, NoDuty{});
-    else if (hv < 4) helpers(Half{}, std::false_type{}, NoDuty{});
+    else if (hv < 4) helpers(Half{}, std::true_type{}, NoDuty{});
     else if (VARLEN && hv == 4) helpers(Quarter{}, std::false_type{}, Ring{});
     else helpers(Quarter{}, std::false_type{}, NoDuty{});
   }
@@ -2069,34 +1243,16 @@ static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename T, int Q>
-static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
+template <typename T>
+static hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int Q = P64;
   using C = Cfg<T, Q>;
   const size_t prep_lds = 2 * sizeof(T) * Q * C::LDN;
-  constexpr bool WIDE = Q > 128;
-  constexpr bool PIPE64 = Q == 64 && sizeof(T) == 2;
-  using ScanFn = void (*)(const T*, int64_t, const float*, const T*, int64_t, const float*, float*, T*,
-                          int64_t, const unsigned char*, int, int, int);
-  size_t scan_lds;
-  const void* scan_fn;
-  ScanFn scan = nullptr;
-  if constexpr (PIPE64) {
-    scan_lds = sizeof(Pipe64Smem);
-    scan_fn = reinterpret_cast<const void*>(&ssd_scan64_kernel<false>);
-  } else {
-    if constexpr (WIDE) {
-      scan_lds = sizeof(WideSmem<T, Q>);
-      scan = &ssd_scan_wide_kernel<T, Q>;
-    } else {
-      scan_lds = sizeof(ScanSmem<T, Q>);
-      scan = &ssd_scan_kernel<T, Q>;
-    }
-    scan_fn = reinterpret_cast<const void*>(scan);
-  }
+  const size_t scan_lds = sizeof(Pipe64Smem<T>);
   static bool configured = false;
   if (!configured) {
     hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, false>), prep_lds);
-    if (e == hipSuccess) e = set_lds(scan_fn, scan_lds);
+    if (e == hipSuccess) e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<T, false>), scan_lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -2107,21 +1263,15 @@ static hipError_t launch_tq(const PrefillArgs& a, hipStream_t stream) {
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{}, VarlenDev{});
   }
-  if constexpr (PIPE64) {
-    hipLaunchKernelGGL((ssd_scan64_kernel<false>), dim3(a.B * a.H), dim3(P64_THREADS), scan_lds, stream,
-                       static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
-                       a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{}, VarlenDev{});
-  } else {
-    hipLaunchKernelGGL(scan, dim3(a.B * a.H), dim3(SCAN_THREADS), scan_lds, stream,
-                       static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
-                       a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G);
-  }
+  hipLaunchKernelGGL((ssd_scan64_kernel<T, false>), dim3(a.B * a.H), dim3(P64_THREADS), scan_lds, stream,
+                     static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                     a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{}, VarlenDev{}, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream) {
+hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream,
+                                   uint64_t* phase_cycles) {
   using T = bf16;
   constexpr int Q = P64;
   using C = Cfg<T, Q>;
@@ -2129,7 +1279,10 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
   static bool configured = false;
   if (!configured) {
     hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, true>), prep_lds);
-    if (e == hipSuccess) e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<true>), sizeof(Pipe64Smem));
+    if (e == hipSuccess)
+      e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<T, true>), sizeof(Pipe64Smem<T>));
+    if (e == hipSuccess)
+      e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<T, true, false, true>), sizeof(Pipe64Smem<T>));
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -2140,10 +1293,17 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
                        a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
                        static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv, VarlenDev{});
   }
-  hipLaunchKernelGGL((ssd_scan64_kernel<true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
-                     stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
-                     a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{});
+  if (phase_cycles) {
+    hipLaunchKernelGGL((ssd_scan64_kernel<T, true, false, true>), dim3(a.B * a.H), dim3(P64_THREADS),
+                       sizeof(Pipe64Smem<T>), stream, static_cast<const T*>(a.x), a.x_stride, a.D,
+                       static_cast<const T*>(a.z), a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, phase_cycles);
+  } else {
+    hipLaunchKernelGGL((ssd_scan64_kernel<T, true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem<T>),
+                       stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
+                       a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -2186,7 +1346,7 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
   if (!configured) {
     hipError_t e = set_lds(reinterpret_cast<const void*>(&ssd_prep_kernel<T, Q, true, true>), prep_lds);
     if (e == hipSuccess)
-      e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<true, true>), sizeof(Pipe64Smem));
+      e = set_lds(reinterpret_cast<const void*>(&ssd_scan64_kernel<T, true, true>), sizeof(Pipe64Smem<T>));
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -2205,9 +1365,10 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
                      stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
                      a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a), ws, a.L, a.H, a.G, maxC,
                      cv, vd);
-  hipLaunchKernelGGL((ssd_scan64_kernel<true, true>), dim3(K * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem),
+  hipLaunchKernelGGL((ssd_scan64_kernel<T, true, true>), dim3(K * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem<T>),
                      stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
-                     a.z_stride, nullptr, nullptr, static_cast<T*>(a.y), a.y_stride, ws, a.L, a.H, a.G, cv, vd);
+                     a.z_stride, nullptr, nullptr, static_cast<T*>(a.y), a.y_stride, ws, a.L, a.H, a.G, cv, vd,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -2218,26 +1379,14 @@ static size_t ws_bytes(int B, int L, int H, int G) {
   return nC * ((size_t)B * G * C::REC_BYTES + (size_t)B * H * C::HREC_BYTES);
 }
 
-size_t ssd_prefill_workspace(int io_bf16, int chunk, int B, int L, int H, int G) {
-  if (io_bf16) {
-    if (chunk == 64) return ws_bytes<bf16, 64>(B, L, H, G);
-    if (chunk == 128) return ws_bytes<bf16, 128>(B, L, H, G);
-    if (chunk == 256) return ws_bytes<bf16, 256>(B, L, H, G);
-  } else if (chunk == 64) {
-    return ws_bytes<float, 64>(B, L, H, G);
-  }
-  return 0;
+// The chunk a call names does not change the tiling: every supported chunk runs at 64.
+size_t ssd_prefill_workspace(int io_bf16, int, int B, int L, int H, int G) {
+  return io_bf16 ? ws_bytes<bf16, P64>(B, L, H, G) : ws_bytes<float, P64>(B, L, H, G);
 }
 
-hipError_t launch_ssd_prefill(int io_bf16, int chunk, const PrefillArgs& a, hipStream_t stream) {
-  if (io_bf16) {
-    if (chunk == 64) return launch_tq<bf16, 64>(a, stream);
-    if (chunk == 128) return launch_tq<bf16, 128>(a, stream);
-    if (chunk == 256) return launch_tq<bf16, 256>(a, stream);
-  } else if (chunk == 64) {
-    return launch_tq<float, 64>(a, stream);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_ssd_prefill(int io_bf16, int, const PrefillArgs& a, hipStream_t stream) {
+  return io_bf16 ? launch_t<bf16>(a, stream) : launch_t<float>(a, stream);
 }
+
 
 }  // namespace m2

@@ -14,7 +14,8 @@
 // has exactly one reader-writer (no cross-workgroup ordering is needed). With
 // few (sequence, group) pairs, 2 or 4 workgroups share a pair, each with its
 // share of the heads and their x channels; the shared B and C columns are then
-// written by the last of them to arrive (see SPLIT below). Each of
+// shifted by a second, small kernel on the same stream, which the stream starts
+// only after every read of the old cache is done (see SPLIT below). Each of
 // its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
 // (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of row n = 4m + rg, so one wave
 // instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
@@ -41,11 +42,6 @@ constexpr int DEC_K = 1;            // state rows per lane in one work item
 constexpr int DEC_NB = 4;           // item buffers
 constexpr int DEC_IPH = 32 / DEC_K;  // work items per head
 constexpr int DEC_MAX_HPG = 256;     // heads per group the kernel covers (one dt thread each)
-constexpr int DEC_ARRIVAL_SLOTS = 1024;  // (sequence, group) pairs a split launch may cover
-
-// Arrival counts of the workgroups that share a (sequence, group) in a split launch, zero
-// between calls: the last of them to arrive writes the group's B and C conv-cache columns.
-__device__ unsigned int dec_arrivals[DEC_ARRIVAL_SLOTS];
 static_assert(DEC_MAX_HPG <= DEC_THREADS, "one thread per head for dt");
 
 template <typename T>
@@ -73,10 +69,8 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // registers, so the state is read and written once per call. Each token's arithmetic is the
 // one-token step's, so NT tokens give the bits of NT one-token calls.
 // SPLIT workgroups share a (sequence, group), each with hpg / SPLIT of its heads (small
-// batches, so that more CUs stream state). Each convolves B and C from the cache; the last
-// to arrive, by a device-scope count taken after every read of the old cache in its
-// workgroup, writes the shifted B and C cache columns, so no workgroup can overwrite a
-// cache row another has still to read.
+// batches, so that more CUs stream state). Each convolves B and C from the cache and leaves
+// the B and C cache columns alone: conv_shift_bc_kernel, next on the stream, shifts them.
 template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 && NB == DEC_NB ? 8 : 4, 8)))
 void state_update_kernel(
@@ -234,24 +228,6 @@ void state_update_kernel(
     }
   }
   __syncthreads();
-  if constexpr (SPLIT > 1) {
-    // every read of the old cache in this workgroup has returned (its values were used
-    // before the barrier); count the arrival, and the last workgroup of the group writes
-    // the shifted B and C columns (the host keeps those channels out of the loop above)
-    __shared__ int last_arrival;
-    if (tid == 0) {
-      __threadfence();
-      const unsigned int before = atomicAdd(&dec_arrivals[b * G + g], 1u);
-      const bool last = before == SPLIT - 1;
-      if (last) atomicExch(&dec_arrivals[b * G + g], 0u);
-      last_arrival = last;
-    }
-    __syncthreads();
-    if (last_arrival && conv_thread && lc >= nx) {
-#pragma unroll
-      for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
-    }
-  }
 
   // stream the heads: per part, request part it + NB - 1, then update part it in place
   // (NT times, one token after the other)
@@ -331,6 +307,33 @@ void state_update_kernel(
   }
 }
 
+// The B and C columns of the conv cache after a split one-token launch: for sequence b
+// (entry slots[b] of the pool, skipped when out of range), rows (1, 2, the new token) become
+// rows (0, 1, 2). One thread per 16-byte vector of the 2 G N channels reads all three
+// before it writes, and the launch before it on the stream has finished every read of the
+// old rows, so nothing is overwritten before it is used.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_shift_bc_kernel(const T* __restrict__ u_t, T* __restrict__ conv_state,
+                                                            int B, int H, int G, const int32_t* __restrict__ slots,
+                                                            int npool, int64_t us) {
+  constexpr int VE = Vec<T>::VE;
+  const int di = H * DEC_P, nbc = 2 * G * DEC_N, Cc = di + nbc;
+  const int per_seq = nbc / VE;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * per_seq) return;
+  const int b = i / per_seq, c = di + (i % per_seq) * VE;
+  int sb = b;
+  if (slots) {
+    sb = slots[b];
+    if (sb < 0 || sb >= npool) return;
+  }
+  T* cs = conv_state + (int64_t)sb * (DEC_W - 1) * Cc + c;
+  const Vec<T> r1 = ld16(cs + Cc), r2 = ld16(cs + 2 * Cc), u = ld16(u_t + (int64_t)b * us + c);
+  st16(cs, r1);
+  st16(cs + Cc, r2);
+  st16(cs + 2 * Cc, u);
+}
+
 template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
 static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int hpp = a.H / a.G / SPLIT;
@@ -346,6 +349,14 @@ static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
                      a.npool, a.u_stride > 0 ? a.u_stride : (int64_t)a.H * DEC_P + 2 * a.G * DEC_N,
                      a.z_stride > 0 ? a.z_stride : (int64_t)a.H * DEC_P, a.dt_stride > 0 ? a.dt_stride : a.H);
+  if constexpr (SPLIT > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n = a.B * 2 * a.G * DEC_N / Vec<T>::VE;
+    hipLaunchKernelGGL((conv_shift_bc_kernel<T>), dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<const T*>(a.u_t), static_cast<T*>(a.conv_state), a.B, a.H, a.G, a.slots, a.npool,
+                       a.u_stride > 0 ? a.u_stride : (int64_t)a.H * DEC_P + 2 * a.G * DEC_N);
+  }
   return hipGetLastError();
 }
 
@@ -372,12 +383,10 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
       // two rounds, took 32 us against 18 us. The B and C channels must stay inside the
       // single conv pass (at most 4096 channels).
       const int hpg = a.H / a.G, bg = a.B * a.G, cus = num_cus();
-      if (bg <= DEC_ARRIVAL_SLOTS) {
-        if (hpg % 4 == 0 && hpg / 4 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 4 <= cus)
-          return launch_nt<T, 1, 2 * DEC_NB, 4>(a, stream);
-        if (hpg % 2 == 0 && hpg / 2 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 2 <= cus)
-          return launch_nt<T, 1, 2 * DEC_NB, 2>(a, stream);
-      }
+      if (hpg % 4 == 0 && hpg / 4 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 4 <= cus)
+        return launch_nt<T, 1, 2 * DEC_NB, 4>(a, stream);
+      if (hpg % 2 == 0 && hpg / 2 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 2 <= cus)
+        return launch_nt<T, 1, 2 * DEC_NB, 2>(a, stream);
       return launch_nt<T, 1>(a, stream);
     }
     case 2: return launch_nt<T, 2>(a, stream);

@@ -76,5 +76,15 @@ def assert_close(got, ref, io: str, what: str = "", rounded: bool = True):
     (y, conv output); fp32 states are compared without slack."""
     e = compute_err(got, ref, io, rounded)
     raw = rel_err(got, ref)
-    assert e <= TOL[io], f"{what}: error/rms = {e:.3e} (raw {raw:.3e}) > {TOL[io]:.0e}"
+    if e > TOL[io]:
+        got_a, ref_a = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        d = np.abs(got_a - ref_a)
+        if rounded:
+            d = np.maximum(d - half_ulp(np.maximum(np.abs(got_a), np.abs(ref_a)), io), 0.0)
+        i = np.unravel_index(int(np.argmax(d)), d.shape)
+        where = f"; worst at {tuple(int(v) for v in i)}: got {got_a[i]:.9g}, ref {ref_a[i]:.9g}, " \
+                f"max|ref|/rms {np.max(np.abs(ref_a)) / rms(ref_a):.3g}"
+    else:
+        where = ""
+    assert e <= TOL[io], f"{what}: error/rms = {e:.3e} (raw {raw:.3e}) > {TOL[io]:.0e}{where}"
     return e

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert m2.mamba2_abi_version() == 7
+    assert m2.mamba2_abi_version() == 8
 
 
 def dims(**kw):
@@ -84,7 +84,7 @@ def decode(d, **kw):
     (dict(io=7), EDTYPE), (dict(batch=0), ESHAPE), (dict(seqlen=-1), ESHAPE),
     (dict(nheads=6, ngroups=4), ESHAPE), (dict(nheads=0), ESHAPE),
     (dict(headdim=32), EUNSUP), (dict(dstate=64), EUNSUP), (dict(conv_width=3), EUNSUP),
-    (dict(chunk=128), EUNSUP), (dict(chunk=512, io=m2.MAMBA2_BF16), EUNSUP), (dict(chunk=48), EUNSUP),
+    (dict(chunk=512), EUNSUP), (dict(chunk=512, io=m2.MAMBA2_BF16), EUNSUP), (dict(chunk=48), EUNSUP),
 ])
 def test_prefill_rejects_dims(kw, code):
     assert prefill(dims(**kw)) == code
@@ -144,15 +144,15 @@ def test_decode_token_count():
 
 
 def test_workspace_size_formula():
-    """Per (sequence, group, chunk): fp32 causal Gram tiles + B^T and C operand tiles;
-    per (sequence, head, chunk): dt, its prefix sums and per-token decay weights."""
-    for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_BF16, 2, 256),
-                          (m2.MAMBA2_F32, 4, 64)):
-        d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
-        t = chunk // 32
-        rec = 4 * 1024 * t * (t + 1) // 2 + 2 * 128 * chunk * es
-        nc = -(-1000 // chunk)
-        assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 12 * chunk)
+    """Per (sequence, group, 64-token chunk): fp32 causal Gram tiles + B^T and C operand
+    tiles; per (sequence, head, chunk): dt, its prefix sums (hi and lo) and per-token decay
+    weights. The named chunk is a tiling choice: every supported one tiles at 64."""
+    for io, es in ((m2.MAMBA2_BF16, 2), (m2.MAMBA2_F32, 4)):
+        for chunk in (64, 128, 256):
+            d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
+            rec = 4 * 1024 * 3 + 2 * 128 * 64 * es
+            nc = -(-1000 // 64)
+            assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 16 * 64)
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(chunk=100)) == 0
     assert m2.lib.mamba2_ssd_prefill_workspace_bytes(None) == 0
@@ -218,19 +218,19 @@ def test_conv_prefill_rejects(kw, code):
 
 
 def test_conv_prefill_rejects_dims():
-    assert conv_prefill(dims(chunk=128)) == EUNSUP
+    assert conv_prefill(dims(chunk=512)) == EUNSUP
     assert conv_prefill(dims(io=m2.MAMBA2_BF16, chunk=48)) == EUNSUP
     assert conv_prefill(dims(nheads=6, ngroups=4)) == ESHAPE
 
 
 def test_conv_prefill_workspace_size():
-    """Fused (bf16, chunk 64): the prefill's workspace; otherwise that (rounded up to 256 bytes)
+    """Fused (bf16, any chunk): the prefill's workspace; fp32: that (rounded up to 256 bytes)
     plus the conv output of all xBC channels."""
     for io, es, chunk in ((m2.MAMBA2_BF16, 2, 64), (m2.MAMBA2_BF16, 2, 128), (m2.MAMBA2_BF16, 2, 256),
-                          (m2.MAMBA2_F32, 4, 64)):
+                          (m2.MAMBA2_F32, 4, 64), (m2.MAMBA2_F32, 4, 256)):
         d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
         base = m2.mamba2_ssd_prefill_workspace_bytes(d)
-        want = base if (io == m2.MAMBA2_BF16 and chunk == 64) else \
+        want = base if io == m2.MAMBA2_BF16 else \
             -(-base // 256) * 256 + 3 * 1000 * (16 * 64 + 2 * 8 * 128) * es
         assert m2.mamba2_conv_ssd_prefill_workspace_bytes(d) == want
     assert m2.mamba2_conv_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
@@ -287,11 +287,13 @@ def test_varlen_rejects(kw, code):
 
 def test_varlen_settings_and_workspace():
     assert varlen(dims(io=m2.MAMBA2_F32, batch=3)) == EUNSUP
-    assert varlen(dims(io=m2.MAMBA2_BF16, chunk=128, batch=3)) == EUNSUP
-    d = dims(io=m2.MAMBA2_BF16, batch=5, seqlen=1000, nheads=16, ngroups=8)
+    assert varlen(dims(io=m2.MAMBA2_BF16, chunk=512, batch=3)) == EUNSUP
     m = 1000 // 64 + 5
     rec = 4096 * 3 + 2 * 128 * 64 * 2
-    assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == m * (8 * rec + 16 * 768 + 16 + 384 * 16) + 8 * 6
+    for chunk in (64, 128, 256):
+        d = dims(io=m2.MAMBA2_BF16, batch=5, seqlen=1000, nheads=16, ngroups=8, chunk=chunk)
+        assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == \
+            m * (8 * rec + 16 * 1024 + 16 + 384 * 16) + 8 * 6
     assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(dims(io=m2.MAMBA2_F32)) == 0
 
 

@@ -165,3 +165,28 @@ def test_fused_is_deterministic():
     b = run_fused(cfg, inp, cs)
     for g, r in zip(a, b):
         np.testing.assert_array_equal(g, r)
+
+
+def test_profile_call_bitwise_and_cycles():
+    """mamba2_conv_ssd_prefill_profile gives the one call's results bit for bit and fills the
+    cycle profile: every wave's chunk-loop count is positive, and each phase of a Y or H wave
+    is a positive part of its loop."""
+    t = torch()
+    cfg = small(560, seqlen=700)
+    inp = si.draw_prefill(cfg)
+    cs0 = si.draw_conv_state(cfg)
+    y0, h0_, c0 = run_fused(cfg, inp, cs0)
+    o = _operands(cfg, inp, cs0, True, True, True, True, 0)
+    d = m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, 64, m2.MAMBA2_BF16)
+    ws = t.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=t.uint8, device="cuda")
+    cyc = t.zeros(cfg.batch * cfg.nheads * 64, dtype=t.int64, device="cuda")
+    m2.mamba2_conv_ssd_prefill_profile(o["u"], o["w"], o["b"], o["cs"], o["dt"], o["dtb"], o["A"], o["D"], o["z"],
+                                       o["h0"], o["hf"], o["y"], cyc, ngroups=cfg.ngroups, chunk=64, workspace=ws)
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(host(o["y"]), y0)
+    np.testing.assert_array_equal(host(o["hf"]), h0_)
+    np.testing.assert_array_equal(host(o["cs"]), c0)
+    c = cyc.view(cfg.batch * cfg.nheads, 16, 4).cpu().numpy()
+    assert (c[:, :, 0] > 0).all()
+    assert (c[:, 0:8, 1] > 0).all() and (c[:, 0:8, 1] < c[:, 0:8, 0]).all()
+    assert (c[:, 0:4, 2] > 0).all() and (c[:, 0:4, 2] < c[:, 0:4, 0]).all()

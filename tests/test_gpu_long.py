@@ -264,3 +264,118 @@ def test_context_parallel_share_12b_16k_with_h0():
     np.testing.assert_array_equal(csg[..., chans], hist)
     np.testing.assert_array_equal(csg, hist_conv)
     print(f"16k share (heads {heads}): y err/rms {ey:.2e}, h_final err/rms {eh:.2e}")
+
+
+def test_fused_prefill_12b_128k_chunk64():
+    """The call the benchmark times for the 128k-token workload: mamba2_conv_ssd_prefill at
+    chunk 64 (the conv inside the scan's kernels) over the raw xBC of the 12B shape, from a
+    zero conv history. Each step is checked on identical inputs: the conv call's output on the
+    same rows (bitwise what the one call convolves, as test_gpu_conv_prefill shows) against the
+    oracle's conv, then y on every token of one head per group and those heads' final states
+    against the oracle's scan of that conv output; the new history bitwise."""
+    t = torch()
+    cfg = si.PREFILL_12B_128K
+    B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    di, gn, Cc = cfg.d_inner, G * cfg.dstate, cfg.conv_channels
+    heads = one_head_per_group(cfg)
+    chans = sub_channels(cfg, heads)
+    p = si.draw_params(cfg)
+    u = empty((B, L, Cc), "bf16")
+    z = empty((B, L, di), "bf16")
+    dt = empty((B, L, H), "bf16")
+    sub_u = np.empty((B, L, len(chans)))
+    sub_z = np.empty((B, L, len(heads) * 64))
+    sub_dt = np.empty((B, L, len(heads)))
+    for t0 in range(0, L, SLAB):
+        t1 = min(L, t0 + SLAB)
+        a = si.draw_xbc(cfg, t0, t1)
+        to_dev(u[:, t0:t1], a)
+        sub_u[:, t0:t1] = a[..., chans]
+        a = si.draw_z(cfg, t0, t1)
+        to_dev(z[:, t0:t1], a)
+        sub_z[:, t0:t1] = a[..., head_cols(heads)]
+        a = si.draw_dt_raw(cfg, t0, t1, dt_bias=p["dt_bias"])
+        to_dev(dt[:, t0:t1], a)
+        sub_dt[:, t0:t1] = a[..., heads]
+        del a
+    last3 = host(u[:, L - 3:])
+    w, b = dev32(p["conv_w"]), dev32(p["conv_b"])
+    xconv = empty((B, L, Cc), "bf16")
+    m2.mamba2_conv1d(u, w, b, None, xconv)
+    cs = t.zeros((B, 3, Cc), dtype=t.bfloat16, device="cuda")
+    y = empty((B, L, di), "bf16")
+    hf = t.empty((B, H, cfg.dstate, cfg.headdim), dtype=t.float32, device="cuda")
+    print("fused prefill: 12B, 131072 tokens, chunk 64", flush=True)
+    m2.mamba2_conv_ssd_prefill(u, w, b, cs, dt, dev32(p["dt_bias"]), dev32(p["A"]), dev32(p["D"]), z, None, hf,
+                               y, ngroups=G, chunk=64)
+    t.cuda.synchronize()
+    cols = t.from_numpy(head_cols(heads)).cuda()
+    yg = host(y.index_select(2, cols))
+    hg = host(hf[:, heads])
+    conv = host(xconv.index_select(2, t.from_numpy(chans).cuda()))
+    np.testing.assert_array_equal(host(cs), last3)
+    del u, z, dt, y, xconv
+    sp = sub_params(p, heads, chans)
+    n = len(heads)
+    xr, _ = oracle.conv1d(sub_u, sp["conv_w"], sp["conv_b"], None)
+    del sub_u
+    ec = assert_close(conv, xr, "bf16", "128k conv")
+    del xr
+    yr, hr = oracle.ssd_scan(conv[..., :n * 64], conv[..., n * 64:n * 64 + gn], conv[..., n * 64 + gn:], sub_dt,
+                             sp["dt_bias"], sp["A"], sp["D"], sub_z, None, ngroups=G)
+    ey = assert_close(yg, yr, "bf16", "128k fused y")
+    eh = assert_close(hg, hr, "bf16", "128k fused h_final", rounded=False)
+    print(f"128k fused chunk 64 (heads {heads}): conv {ec:.2e}, y err/rms {ey:.2e}, h_final err/rms {eh:.2e}")
+
+
+def test_fused_prefill_9b_b8_8k_chunk64():
+    """The prefill of the generation-shaped run as the benchmark times it: 9B shape, batch 8,
+    8192 tokens, mamba2_conv_ssd_prefill at chunk 64 from a zero conv history. On identical
+    inputs per step: the conv call's output against the oracle's conv, then y on every token
+    of one head per group in all 8 sequences and those heads' final states against the
+    oracle's scan of that conv output; the new history bitwise."""
+    t = torch()
+    cfg = si.GENERATE_9B_B8
+    B, L, H, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups
+    di, gn, Cc = cfg.d_inner, G * cfg.dstate, cfg.conv_channels
+    heads = one_head_per_group(cfg)
+    chans = sub_channels(cfg, heads)
+    n = len(heads)
+    p = si.draw_params(cfg)
+    inp = si.draw_prefill(cfg)
+    u = empty((B, L, Cc), "bf16")
+    to_dev(u, inp["xbc"])
+    z = empty((B, L, di), "bf16")
+    to_dev(z, inp["z"])
+    dt = empty((B, L, H), "bf16")
+    to_dev(dt, inp["dt_raw"])
+    sub_u = inp["xbc"][..., chans].astype(np.float64)
+    sub_z = inp["z"][..., head_cols(heads)].astype(np.float64)
+    sub_dt = inp["dt_raw"][..., heads].astype(np.float64)
+    last3 = inp["xbc"][:, L - 3:].astype(np.float64)
+    del inp
+    w, b = dev32(p["conv_w"]), dev32(p["conv_b"])
+    xconv = empty((B, L, Cc), "bf16")
+    m2.mamba2_conv1d(u, w, b, None, xconv)
+    cs = t.zeros((B, 3, Cc), dtype=t.bfloat16, device="cuda")
+    y = empty((B, L, di), "bf16")
+    hf = t.empty((B, H, cfg.dstate, cfg.headdim), dtype=t.float32, device="cuda")
+    print("fused prefill: 9B, batch 8, 8192 tokens, chunk 64", flush=True)
+    m2.mamba2_conv_ssd_prefill(u, w, b, cs, dt, dev32(p["dt_bias"]), dev32(p["A"]), dev32(p["D"]), z, None, hf,
+                               y, ngroups=G, chunk=64)
+    t.cuda.synchronize()
+    cols = t.from_numpy(head_cols(heads)).cuda()
+    yg = host(y.index_select(2, cols))
+    hg = host(hf[:, heads])
+    conv = host(xconv.index_select(2, t.from_numpy(chans).cuda()))
+    np.testing.assert_array_equal(host(cs), last3)
+    del u, z, dt, y, xconv
+    sp = sub_params(p, heads, chans)
+    xr, _ = oracle.conv1d(sub_u, sp["conv_w"], sp["conv_b"], None)
+    ec = assert_close(conv, xr, "bf16", "9B b8 conv")
+    yr, hr = oracle.ssd_scan(conv[..., :n * 64], conv[..., n * 64:n * 64 + gn], conv[..., n * 64 + gn:], sub_dt,
+                             sp["dt_bias"], sp["A"], sp["D"], sub_z, None, ngroups=G)
+    ey = assert_close(yg, yr, "bf16", "9B b8 fused y")
+    eh = assert_close(hg, hr, "bf16", "9B b8 fused h_final", rounded=False)
+    print(f"9B batch 8 fused chunk 64 (heads {heads}): conv {ec:.2e}, y err/rms {ey:.2e}, "
+          f"h_final err/rms {eh:.2e}")
