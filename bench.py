@@ -71,6 +71,35 @@ def measured_traffic(name: str, chunk: int | None = None):
     return t.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------------------------ clock settle
+SETTLE_MS = {}     # workload -> GPU milliseconds spent settling the clocks before its warm-up
+
+
+def settle(torch, name: str, step, min_ms: float):
+    """Runs ``step(k)`` (k = 0, 1, ...) in growing batches until at least ``min_ms`` of GPU
+    time has passed between two events on the current stream, so that the clocks have
+    ramped up to the workload's steady state before its warm-up and timed steps (the first
+    tens of milliseconds after an idle gap run at lower clocks). Records the time spent."""
+    if min_ms <= 0:
+        SETTLE_MS[name] = 0.0
+        return
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    k, batch = 0, 4
+    while True:
+        for _ in range(batch):
+            step(k)
+            k += 1
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        if ms >= min_ms:
+            break
+        batch = min(batch * 2, 256)
+    SETTLE_MS[name] = ms
+
+
 # ------------------------------------------------------------------------------ workloads
 def prefill_bytes(cfg) -> dict:
     """Algorithmic HBM bytes of one prefill pass (inputs once, outputs once)."""
@@ -139,6 +168,7 @@ def run_prefill(args, torch, m2, si, cfg, inp, chunk, fused=True):
         if evs:
             evs[-1].record()
 
+    settle(torch, f"prefill_chunk{chunk}" + ("" if fused else "_two_call"), lambda k: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -155,6 +185,69 @@ def run_prefill(args, torch, m2, si, cfg, inp, chunk, fused=True):
     total_ms = t_start.elapsed_time(t_end)
     per_call = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / args.steps for i in range(len(calls))]
     return total_ms / args.steps, wall, per_call
+
+
+CU_PEAK_FLOP_PER_CYCLE = BF16_PEAK_TFLOPS * 1e12 / (256 * 2.4e9)   # dense bf16 MFMA per CU per cycle
+
+
+def run_phase_profile(args, torch, m2, si, cfg, inp):
+    """Per-phase MFMA rates of the step's scan kernel, from its cycle profile
+    (mamba2_conv_ssd_prefill_profile: s_memtime around each contraction phase of every wave,
+    summed over the chunk loop). For each phase: the algorithmic flops of one (head, chunk),
+    the cycles the phase takes per chunk on the CU (the slowest of the four waves that share
+    it, one per SIMD, averaged over workgroups), and their ratio against the CU's dense bf16
+    MFMA peak. Phases: the carried-state output H^T C^T (2 Q N P flops per chunk), the chunk
+    state B^T (w x) (2 Q N P) and the intra-chunk product X^T M^T ((Q + 1) Q P, the causal
+    half). The computed operands enter as hi + lo bf16 pairs, so the MFMAs execute twice the
+    algorithmic flops of the first two and of the third."""
+    dev = lambda a: torch.from_numpy(si.bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+    f32 = lambda a: torch.from_numpy(a).cuda()
+    u, z, dt = dev(inp["xbc"]), dev(inp["z"]), dev(inp["dt_raw"])
+    w, bias, dtb, A, D = (f32(inp[k]) for k in ("conv_w", "conv_b", "dt_bias", "A", "D"))
+    B, L, H, Q, N, P = cfg.batch, cfg.seqlen, cfg.nheads, 64, cfg.dstate, cfg.headdim
+    cs = torch.zeros((B, 3, cfg.conv_channels), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((B, L, cfg.d_inner), dtype=torch.bfloat16, device="cuda")
+    hf = torch.empty((B, H, N, P), dtype=torch.float32, device="cuda")
+    dims = m2.make_dims(B, L, H, cfg.ngroups, Q, m2.MAMBA2_BF16)
+    ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    cyc = torch.zeros(B * H * 16 * 4, dtype=torch.int64, device="cuda")
+
+    def plain(k=0):
+        m2.mamba2_conv_ssd_prefill(u, w, bias, cs, dt, dtb, A, D, z, None, hf, y, ngroups=cfg.ngroups,
+                                   chunk=Q, workspace=ws)
+
+    def profiled():
+        m2.mamba2_conv_ssd_prefill_profile(u, w, bias, cs, dt, dtb, A, D, z, None, hf, y, cyc,
+                                           ngroups=cfg.ngroups, chunk=Q, workspace=ws)
+
+    settle(torch, "phase_profile", plain, args.settle_ms)
+    for _ in range(3):
+        profiled()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    profiled()
+    e1.record()
+    torch.cuda.synchronize()
+    prof_us = e0.elapsed_time(e1) * 1e3
+    c = cyc.view(B * H, 16, 4).cpu().numpy().astype("float64")
+    nC = (L + Q - 1) // Q
+    loop = float(c[:, 0, 0].mean()) / nC
+    phases = {
+        "A6_carried_state_output": (c[:, 0:4, 1].max(axis=1).mean() / nC, 2.0 * Q * N * P),
+        "A4_chunk_state": (c[:, 4:8, 1].max(axis=1).mean() / nC, 2.0 * Q * N * P),
+        "A3_intra_chunk": (c[:, 0:4, 2].max(axis=1).mean() / nC, float((Q + 1) * Q * P)),
+    }
+    busy = min(B * H, 256) / 256.0
+    out = {"method": "cycle stamps around each phase in the scan kernel (mamba2_conv_ssd_prefill_profile), "
+                     "12B 8k one-call step",
+           "cu_peak_flop_per_cycle": CU_PEAK_FLOP_PER_CYCLE, "chunk_loop_cycles_per_chunk": loop,
+           "profiled_call_us": prof_us, "busy_cu_share": busy, "target_frac": 0.5}
+    for name, (cycles, flops) in phases.items():
+        frac = flops / (cycles * CU_PEAK_FLOP_PER_CYCLE)
+        out[name] = {"cycles_per_chunk": float(cycles), "algorithmic_flops_per_chunk": flops,
+                     "frac_of_cu_peak": frac, "executed_frac_of_cu_peak": 2 * frac,
+                     "frac_of_chip_peak": frac * busy, "share_of_chunk_loop": float(cycles) / loop}
+    return out
 
 
 def run_decode(args, torch, m2, si):
@@ -177,6 +270,7 @@ def run_decode(args, torch, m2, si):
         m2.mamba2_state_update(u, w, bias, caches[k & 1], dt, dtb, A, D, z, states[k & 1], y,
                                ngroups=cfg.ngroups)
 
+    settle(torch, "decode", step, args.settle_ms)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -222,6 +316,7 @@ def run_decode_tokens(args, torch, m2, si, T=4):
         m2.mamba2_state_update(u, w, bias, caches[k & 1], dt, dtb, A, D, z, states[k & 1], y,
                                ngroups=cfg.ngroups)
 
+    settle(torch, f"decode_tokens{T}", step, args.settle_ms)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -255,6 +350,7 @@ def run_rmsnorm(args, torch, m2, si, cfg):
         turn[0] ^= 1
         m2.mamba2_group_rmsnorm(gi, w, oi, ngroups=cfg.ngroups)
 
+    settle(torch, "group_rmsnorm", lambda k: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -301,6 +397,7 @@ def run_mixer_prefill(args, torch, m2, si, cfg, d_model: int = 5120):
                                 workspace=ws)
 
     n = max(1, args.steps // 4)
+    settle(torch, "mixer_prefill", lambda k: step(), args.settle_ms)
     for _ in range(max(1, args.warmup // 10)):
         step()
     torch.cuda.synchronize()
@@ -336,6 +433,7 @@ def run_mixer_step(args, torch, m2, si, d_model: int = 4480):
                              t["D"], states[k & 1], t["norm_w"], t["w_out"], out, ngroups=cfg.ngroups,
                              workspace=ws)
 
+    settle(torch, "mixer_step", step, args.settle_ms)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -398,9 +496,13 @@ def run_generation(args, torch, m2, si, ring: int = 64):
         m2.mamba2_state_update(su[i], p["conv_w"], p["conv_b"], cs, sdt[i], p["dt_bias"], p["A"], p["D"], sz[i],
                                h, yt, ngroups=G)
 
-    for k in range(20):
+    def pair(k):
         prefill()
         step(k)
+
+    settle(torch, "generation", pair, args.settle_ms)
+    for k in range(20):
+        pair(k)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     ev[0].record()
@@ -461,7 +563,7 @@ def run_other_prefills(args, torch, m2, si):
         def call():
             m2.mamba2_conv_ssd_prefill(u, p["conv_w"], p["conv_b"], None, dt, p["dt_bias"], p["A"], p["D"], z,
                                        None, h, y, ngroups=G, chunk=chunk, workspace=ws)
-        us = _time_calls(torch, call, 2, 5)
+        us = _time_calls(torch, call, 2, 5, f"prefill_12b_128k_chunk{chunk}", args.settle_ms)
         out[f"prefill_12b_128k_chunk{chunk}"] = {"us": us, "tokens_per_s": B * L / (us * 1e-6),
                                                   "GB_s": prefill_bytes(cfg)["fused"] / (us * 1e-6) / 1e9}
         del ws
@@ -477,7 +579,7 @@ def run_other_prefills(args, torch, m2, si):
     def share():
         m2.mamba2_conv_ssd_prefill(us_, p["conv_w"], p["conv_b"], cs, dts_, p["dt_bias"], p["A"], p["D"], zs_, h0,
                                    h, ys_, ngroups=G, chunk=64, workspace=ws)
-    us = _time_calls(torch, share, 5, 20)
+    us = _time_calls(torch, share, 5, 20, "prefill_12b_16k_share", args.settle_ms)
     out["prefill_12b_16k_share_with_h0"] = {"us": us, "tokens_per_s": B * Ls / (us * 1e-6),
                                              "note": "one GPU's 1/8 share of the 128k sequence, from an "
                                                      "incoming state and history (the history is updated "
@@ -495,12 +597,14 @@ def run_other_prefills(args, torch, m2, si):
     def tiny():
         m2.mamba2_conv_ssd_prefill(tu, tw["conv_w"], tw["conv_b"], None, tdt, tw["dt_bias"], tw["A"], tw["D"], tz,
                                    None, th, ty, ngroups=cfg.ngroups, chunk=64)
-    out["prefill_tiny_f32"] = {"us": _time_calls(torch, tiny, 50, 200),
+    out["prefill_tiny_f32"] = {"us": _time_calls(torch, tiny, 50, 200, "prefill_tiny_f32", args.settle_ms),
                                "note": "batch 1, 256 tokens, 4 heads, 1 group, all fp32, chunk 64 (latency)"}
     return out
 
 
-def _time_calls(torch, call, warm: int, n: int) -> float:
+def _time_calls(torch, call, warm: int, n: int, name: str = "", settle_ms: float = 0.0) -> float:
+    if name:
+        settle(torch, name, lambda k: call(), settle_ms)
     for _ in range(warm):
         call()
     torch.cuda.synchronize()
@@ -539,6 +643,7 @@ def run_varlen(args, torch, m2, si, cfg):
         m2.mamba2_conv_ssd_prefill_varlen(u, w, bias, cu, slots, init, cpool, spool, dt, dtb, A, D, z, y,
                                           ngroups=cfg.ngroups, workspace=ws)
 
+    settle(torch, "prefill_varlen", lambda k: step(), args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -567,30 +672,101 @@ def copy_calibration(torch):
 
 
 # ------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(cfg, inp):
-    """The fp64 oracle timed on the whole prefill workload (same seeded inputs as the GPU
-    step): conv1d over all tokens and channels, then the sequential scan over all heads.
-    About 30 s of CPU work, a few seconds of wall time on a multi-core host."""
+def cpu_baseline(cfg, inp, si):
+    """The fp64 oracle timed on this host (built here with gcc -O3 -march=native, no
+    fast-math), on the same seeded inputs as the GPU step.
+
+    ``value``: the whole 12B-shape 8192-token prefill step (conv1d over all tokens and
+    channels, then the sequential scan over all heads) on every thread. Beside it, one
+    thread: the tiny all-fp32 layer (whole), the 12B step on one head per group (8 of
+    160 heads: the conv of their channels and their scan, scaled to all heads, labelled
+    extrapolated), and the 9B batch-64 decode step (whole); the decode step on every
+    thread too. About 10-20 s of CPU work in all."""
+    import tempfile
+
     import numpy as np
     import oracle
-    u = np.ascontiguousarray(inp["xbc"], dtype=np.float64)
-    threads = oracle.threads(0)
-    t0 = time.perf_counter()
-    xr, _ = oracle.conv1d(u, inp["conv_w"], inp["conv_b"], None)
-    t_conv = time.perf_counter() - t0
-    x, Bm, Cm = (np.ascontiguousarray(a) for a in oracle.split_xbc(xr, cfg.nheads, cfg.ngroups))
-    z = np.ascontiguousarray(inp["z"], dtype=np.float64)
-    dt = np.ascontiguousarray(inp["dt_raw"], dtype=np.float64)
-    t0 = time.perf_counter()
-    oracle.ssd_scan(x, Bm, Cm, dt, inp["dt_bias"], inp["A"], inp["D"], z, None, ngroups=cfg.ngroups)
-    t_scan = time.perf_counter() - t0
-    full = t_conv + t_scan
-    return {"value": cfg.batch * cfg.seqlen / full, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the whole prefill step once, unscaled: fp64 conv1d over {cfg.seqlen} tokens x "
-                      f"{cfg.conv_channels} channels ({t_conv:.2f} s) and the sequential fp64 scan "
-                      f"over all {cfg.nheads} heads x {cfg.seqlen} tokens ({t_scan:.2f} s), "
-                      f"{threads} OpenMP threads"}
+
+    d64 = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    out_dir = tempfile.mkdtemp(prefix="oracle_native_")
+    lib = oracle.load_native(out_dir)
+    with oracle.use(lib):
+        threads = oracle.threads(0)
+
+        def prefill(c, i, heads=None, nthreads=0):
+            """conv1d + scan of the prefill inputs ``i`` (heads: a subset, its channels only)"""
+            u = d64(i["xbc"])
+            w, b = i["conv_w"], i["conv_b"]
+            H, G = c.nheads, c.ngroups
+            if heads is not None:
+                di, gn = c.d_inner, c.ngroups * c.dstate
+                cols = np.concatenate([np.arange(h * 64, h * 64 + 64) for h in heads])
+                chans = np.concatenate([cols, np.arange(di, di + 2 * gn)])
+                u, w, b = np.ascontiguousarray(u[..., chans]), w[chans], b[chans]
+                H = len(heads)
+            t0 = time.perf_counter()
+            xr, _ = oracle.conv1d(u, w, b, None, nthreads=nthreads)
+            t1 = time.perf_counter()
+            x, Bm, Cm = (np.ascontiguousarray(a) for a in oracle.split_xbc(xr, H, G))
+            if heads is None:
+                z, dt, dtb, A, D = i["z"], i["dt_raw"], i["dt_bias"], i["A"], i["D"]
+            else:
+                z, dt = i["z"][..., cols], i["dt_raw"][..., heads]
+                dtb, A, D = i["dt_bias"][heads], i["A"][heads], i["D"][heads]
+            oracle.ssd_scan(x, Bm, Cm, d64(dt), dtb, A, D, d64(z), None, ngroups=G, nthreads=nthreads)
+            return t1 - t0, time.perf_counter() - t1
+
+        t_conv, t_scan = prefill(cfg, inp)
+        full = t_conv + t_scan
+
+        tcfg = si.TINY_F32
+        c0, s0 = prefill(tcfg, si.draw_prefill(tcfg), nthreads=1)
+        hpg = cfg.nheads // cfg.ngroups
+        heads = [g * hpg for g in range(cfg.ngroups)]
+        c1, s1 = prefill(cfg, inp, heads=heads, nthreads=1)
+        # the subset's conv covers its x channels and all B and C channels; scaled per
+        # channel and per head to the whole layer
+        di, gn = cfg.d_inner, cfg.ngroups * cfg.dstate
+        sub_ch = len(heads) * 64 + 2 * gn
+        one_thread_step = c1 * cfg.conv_channels / sub_ch + s1 * cfg.nheads / len(heads)
+
+        dcfg = si.DECODE_9B_B64
+        dp = si.draw_params(dcfg)
+        st = si.draw_decode_step(dcfg, 0)
+        h0, cs0 = d64(si.draw_h0(dcfg)), d64(si.draw_conv_state(dcfg))
+
+        def decode(nthreads):
+            t0 = time.perf_counter()
+            oracle.state_update(st["xbc"][:, 0], dp["conv_w"], dp["conv_b"], cs0, st["dt_raw"][:, 0],
+                                dp["dt_bias"], dp["A"], dp["D"], st["z"][:, 0], h0, nheads=dcfg.nheads,
+                                ngroups=dcfg.ngroups, nthreads=nthreads)
+            return time.perf_counter() - t0
+
+        dec_all = min(decode(0) for _ in range(3))
+        dec_one = min(decode(1) for _ in range(2))
+
+    tok = cfg.batch * cfg.seqlen
+    return {"value": tok / full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole 12B 8192-token prefill step once, unscaled, {threads} threads: fp64 "
+                      f"conv1d over {cfg.conv_channels} channels ({t_conv:.2f} s) and the sequential "
+                      f"scan of all {cfg.nheads} heads ({t_scan:.2f} s); oracle built with gcc -O3 "
+                      f"-march=native on this host",
+            "build": "gcc -O3 -march=native -ffp-contract=off, no fast-math, OpenMP",
+            "single_thread": {
+                "tiny_f32_prefill": {"s": c0 + s0, "tokens_per_s": tcfg.batch * tcfg.seqlen / (c0 + s0),
+                                     "note": "1 x 256 tokens, 4 heads, whole"},
+                "prefill_12b_8k": {"s": one_thread_step, "tokens_per_s": tok / one_thread_step,
+                                   "extrapolated": True,
+                                   "note": f"heads {heads} (one per group) timed: conv of their "
+                                           f"{sub_ch} channels {c1:.2f} s, scan {s1:.2f} s; scaled to "
+                                           f"{cfg.conv_channels} channels and {cfg.nheads} heads"},
+                "decode_9b_b64": {"us_per_step": dec_one * 1e6,
+                                  "tokens_per_s": dcfg.batch / dec_one, "note": "whole step"},
+            },
+            "decode_9b_b64": {"us_per_step": dec_all * 1e6, "tokens_per_s": dcfg.batch / dec_all,
+                              "threads": threads,
+                              "note": "whole step, best of 3 (the oracle returns new fp64 copies of the "
+                                      "256 MiB state and the conv cache, inside the timing)"}}
 
 
 # ------------------------------------------------------------------------------ counters
@@ -690,6 +866,9 @@ def main():
     # lower clocks
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--decode-steps", type=int, default=100)
+    # GPU time each workload runs before its warm-up, whatever --warmup is: the clocks ramp
+    # up over the first tens of milliseconds after the host has left the GPU idle
+    ap.add_argument("--settle-ms", type=float, default=250.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, help="scan chunk length of the timed prefill")
@@ -725,6 +904,7 @@ def main():
     step_gbs = by["fused"] / (step_us * 1e-6) / 1e9
     fused_kernels = counter_kernels(64)["conv_ssd_prefill"] if args.chunk == 64 else \
         ["conv1d_kernel"] + counter_kernels(args.chunk)["ssd_prefill"]
+    phases = run_phase_profile(args, torch, m2, si, cfg, inp)
     dcfg, dec_us, dec_p50 = run_decode(args, torch, m2, si)
     rms_us, rms_bytes = run_rmsnorm(args, torch, m2, si, cfg)
     vl_us, vl_lens = run_varlen(args, torch, m2, si, cfg)
@@ -760,7 +940,7 @@ def main():
                      "bound": "hbm", "achieved": step_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("conv_ssd_prefill", 64) if args.chunk == 64 else None,
-                     "algorithmic_bytes": by["fused"], "avg_launch_us": step_us},
+                     "algorithmic_bytes": by["fused"], "avg_launch_us": step_us, "phases": phases},
         "kernels": {
             "conv_ssd_prefill": {"us": step_us, "tokens_per_s": tokens / (step_us * 1e-6), "GB_s": step_gbs,
                                  "algorithmic_TFLOP_s": fl / (step_us * 1e-6) / 1e12},
@@ -787,6 +967,7 @@ def main():
         "generation_9b_b8": gen_run,
         "other_prefills": others,
         "wall_s_timed": wall,
+        "settle_ms": {k: round(v, 1) for k, v in SETTLE_MS.items()},
     }
     out["kernels"]["group_rmsnorm"] = {
         "us": rms_us, "GB_s": rms_bytes / (rms_us * 1e-6) / 1e9,
@@ -803,7 +984,7 @@ def main():
             "note": "the one call at the listed chunk runs mamba2_conv1d into the workspace, "
                     "then the chunk-128 scan"}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, si)
     print(json.dumps(out))
 
 
