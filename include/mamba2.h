@@ -208,6 +208,25 @@ int mamba2_conv_ssd_prefill_profile(const mamba2_dims* dims, const void* xBC, in
                                     size_t workspace_bytes, uint64_t* phase_cycles, void* stream);
 
 /*
+ * mamba2_conv_ssd_prefill_noalloc -- mamba2_conv_ssd_prefill without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call the allocator). The call itself allocates nothing: its
+ * workspace is a static device array of 64 MiB (67108864 bytes) that the library holds on
+ * every device it runs on until the process ends. Arguments, results and errors are those
+ * of mamba2_conv_ssd_prefill; a setting whose workspace
+ * (mamba2_conv_ssd_prefill_workspace_bytes) exceeds 64 MiB is rejected with
+ * MAMBA2_ERR_WORKSPACE (at the 12B shape, bf16: up to batch * seqlen = 8192 tokens).
+ * Every call on a device uses that device's one array: two calls in flight at once on one
+ * device (on different streams) race and give undefined results. Calls on one stream
+ * are ordered and safe. Nothing in the array needs to start at zero.
+ */
+int mamba2_conv_ssd_prefill_noalloc(const mamba2_dims* dims, const void* xBC, int64_t xbc_stride,
+                                    const float* conv_w, const float* conv_bias, void* conv_state,
+                                    const void* dt_raw, const float* dt_bias, const float* A,
+                                    const float* D, const void* z, int64_t z_stride, const float* h0,
+                                    float* h_final, void* y, int64_t y_stride, void* stream);
+
+/*
  * mamba2_conv_ssd_prefill_varlen_workspace_bytes -- device workspace of
  * mamba2_conv_ssd_prefill_varlen for `dims` (batch = number of sequences, seqlen =
  * total packed rows; bf16 io, any supported chunk: the kernels tile at 64), 0 if

@@ -71,6 +71,8 @@ lib.mamba2_conv_ssd_prefill.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _v
                                         _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp]
 lib.mamba2_conv_ssd_prefill_profile.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                 _i64, _vp, _vp, _vp, _i64, _vp, _sz, _vp, _vp]
+lib.mamba2_conv_ssd_prefill_noalloc.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _i64, _vp, _vp, _vp, _i64, _vp]
 lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes.argtypes = [_dims]
 lib.mamba2_conv_ssd_prefill_varlen_workspace_bytes.restype = _sz
 lib.mamba2_conv_ssd_prefill_varlen.argtypes = [_dims, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -201,6 +203,18 @@ def mamba2_conv_ssd_prefill_profile(xBC, conv_w, conv_bias, conv_state, dt_raw, 
         _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z), 0 if z is None else _row_stride(z),
         _ptr(h0), _ptr(h_final), _ptr(y), _row_stride(y), _ptr(workspace), ws_bytes, _ptr(phase_cycles),
         _stream()))
+
+
+def mamba2_conv_ssd_prefill_noalloc(xBC, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z, h0,
+                                    h_final, y, *, ngroups: int, chunk: int) -> None:
+    """mamba2_conv_ssd_prefill with the library's static device scratch as its workspace
+    (no allocation by the call)."""
+    B, L, H = dt_raw.shape
+    d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(xBC))
+    _check(lib.mamba2_conv_ssd_prefill_noalloc(
+        ctypes.byref(d), _ptr(xBC), _row_stride(xBC), _ptr(conv_w), _ptr(conv_bias), _ptr(conv_state),
+        _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(z), 0 if z is None else _row_stride(z),
+        _ptr(h0), _ptr(h_final), _ptr(y), _row_stride(y), _stream()))
 
 
 def mamba2_conv_ssd_prefill_varlen_workspace_bytes(d: Dims) -> int:

@@ -55,6 +55,11 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
 // Workspace of the variable-length prefill: the records of ssd_prefill_workspace for up to
 // seqlen / 64 + nseq chunks, then the sanitized offsets and the per-sequence chunk offsets.
 size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G);
+// The prefill's static scratch: a device array of PREFILL_SCRATCH_BYTES per device, for the
+// call that allocates nothing. Sets *ptr to its address on the current device (taken once
+// per device).
+constexpr size_t PREFILL_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t prefill_scratch_on_current_device(void** ptr);
 // Workspace bytes the prep/scan pair needs: per (sequence, group, chunk) the causal Gram
 // tiles in fp32 and B^T and C in MFMA operand order; per (sequence, head, chunk) dt and
 // its block prefix sums.

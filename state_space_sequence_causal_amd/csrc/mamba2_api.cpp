@@ -336,6 +336,26 @@ M2_EXPORT int mamba2_conv_ssd_prefill_profile(const mamba2_dims* d, const void* 
                                   phase_cycles);
 }
 
+M2_EXPORT int mamba2_conv_ssd_prefill_noalloc(const mamba2_dims* d, const void* xBC, int64_t xbc_stride,
+                                              const float* conv_w, const float* conv_bias, void* conv_state,
+                                              const void* dt_raw, const float* dt_bias, const float* A,
+                                              const float* D, const void* z, int64_t z_stride,
+                                              const float* h0, float* h_final, void* y, int64_t y_stride,
+                                              void* stream) {
+  const int st = check_dims(d, true);
+  if (st) return st;
+  if (!chunk_supported(d)) return fail(MAMBA2_ERR_UNSUPPORTED, "chunk %d not supported (64, 128, 256)", d->chunk);
+  const size_t need = conv_prefill_ws(d, nullptr);
+  if (need > m2::PREFILL_SCRATCH_BYTES)
+    return fail(MAMBA2_ERR_WORKSPACE, "needs %zu bytes of scratch; the static scratch holds %zu", need,
+                m2::PREFILL_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  const hipError_t e = m2::prefill_scratch_on_current_device(&scratch);
+  if (e != hipSuccess) return hip_status(e, "static scratch address");
+  return mamba2_conv_ssd_prefill(d, xBC, xbc_stride, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z,
+                                 z_stride, h0, h_final, y, y_stride, scratch, m2::PREFILL_SCRATCH_BYTES, stream);
+}
+
 namespace {
 bool varlen_supported(const mamba2_dims* d) { return d->io_dtype == MAMBA2_BF16 && chunk_supported(d); }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

@@ -41,6 +41,7 @@
 // relative. With a single bf16 rounding the error of outputs dominated by one term reaches
 // 4e-2 to 2e-1 of rms(y) on these heavy-tailed outputs, outside the 2e-2 bar; with the
 // split it stays below 1e-4. The fp32 io mode uses fp32 MFMAs and needs no split.
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -1388,5 +1389,31 @@ hipError_t launch_ssd_prefill(int io_bf16, int, const PrefillArgs& a, hipStream_
   return io_bf16 ? launch_t<bf16>(a, stream) : launch_t<float>(a, stream);
 }
 
+// ---------------------------------------------------------------------------- static scratch
+// Device memory the prefill can use as its workspace without any allocation by the call: a
+// file-scope array of PREFILL_SCRATCH_BYTES that every device the library runs on holds
+// until the process ends. In host code `prefill_scratch` names a host-side stand-in; its
+// device address, different on each device, comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+__device__ __align__(256) unsigned char prefill_scratch[PREFILL_SCRATCH_BYTES];
+
+hipError_t prefill_scratch_on_current_device(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(prefill_scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 }  // namespace m2

@@ -237,6 +237,24 @@ def test_conv_prefill_workspace_size():
     assert m2.lib.mamba2_conv_ssd_prefill_workspace_bytes(None) == 0
 
 
+def test_noalloc_prefill_rejects_before_any_launch():
+    """mamba2_conv_ssd_prefill_noalloc checks dims and its 64 MiB static scratch on the host:
+    a setting whose workspace would not fit is refused (MAMBA2_ERR_WORKSPACE) before anything
+    touches a device; at the 12B shape (bf16) 8192 tokens fit and 8256 do not."""
+    fit = dims(io=m2.MAMBA2_BF16, batch=1, seqlen=8192, nheads=160, ngroups=8)
+    assert m2.mamba2_conv_ssd_prefill_workspace_bytes(fit) == 64 << 20
+    for d, code in ((dims(io=m2.MAMBA2_BF16, batch=1, seqlen=8256, nheads=160, ngroups=8), 7),
+                    (dims(io=m2.MAMBA2_BF16, batch=2, seqlen=8192, nheads=160, ngroups=8), 7),
+                    (dims(nheads=6, ngroups=4), ESHAPE), (dims(chunk=48), EUNSUP)):
+        H, G = d.nheads, d.ngroups
+        cc = H * 64 + 2 * G * 128
+        st = m2.lib.mamba2_conv_ssd_prefill_noalloc(
+            ctypes.byref(d), BASE, cc, BASE + 4 * MB, BASE + 5 * MB, BASE + 6 * MB, BASE + 8 * MB, BASE + 9 * MB,
+            BASE + 10 * MB, BASE + 11 * MB, BASE + 12 * MB, H * 64, BASE + 16 * MB, BASE + 20 * MB, BASE + 24 * MB,
+            H * 64, None)
+        assert st == code, m2.mamba2_last_error()
+
+
 # ------------------------------------------------------------------ decode with slot pools
 def decode_slots(d, **kw):
     a = dict(u=BASE, w=BASE + 1 * MB, b=BASE + 2 * MB, cs=BASE + 3 * MB, dt=BASE + 4 * MB,
