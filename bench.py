@@ -210,7 +210,7 @@ def run_phase_profile(args, torch, m2, si, cfg, inp):
     hf = torch.empty((B, H, N, P), dtype=torch.float32, device="cuda")
     dims = m2.make_dims(B, L, H, cfg.ngroups, Q, m2.MAMBA2_BF16)
     ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
-    cyc = torch.zeros(B * H * 16 * 4, dtype=torch.int64, device="cuda")
+    cyc = torch.zeros(B * H * 16 * 8, dtype=torch.int64, device="cuda")
 
     def plain(k=0):
         m2.mamba2_conv_ssd_prefill(u, w, bias, cs, dt, dtb, A, D, z, None, hf, y, ngroups=cfg.ngroups,
@@ -229,7 +229,7 @@ def run_phase_profile(args, torch, m2, si, cfg, inp):
     e1.record()
     torch.cuda.synchronize()
     prof_us = e0.elapsed_time(e1) * 1e3
-    c = cyc.view(B * H, 16, 4).cpu().numpy().astype("float64")
+    c = cyc.view(B * H, 16, 8).cpu().numpy().astype("float64")
     nC = (L + Q - 1) // Q
     loop = float(c[:, 0, 0].mean()) / nC
     phases = {
@@ -247,6 +247,12 @@ def run_phase_profile(args, torch, m2, si, cfg, inp):
         out[name] = {"cycles_per_chunk": float(cycles), "algorithmic_flops_per_chunk": flops,
                      "frac_of_cu_peak": frac, "executed_frac_of_cu_peak": 2 * frac,
                      "frac_of_chip_peak": frac * busy, "share_of_chunk_loop": float(cycles) / loop}
+    # per role, cycles per chunk (mean over the role's waves and the workgroups): time in the
+    # chunk's barrier, and the helpers' two phases; the role that waits least sets the pace
+    roles = {"y_waves": slice(0, 4), "h_waves": slice(4, 8), "helper_waves": slice(8, 16)}
+    out["barrier_wait_cycles_per_chunk"] = {k: float(c[:, v, 4].mean()) / nC for k, v in roles.items()}
+    out["helper_build_cycles_per_chunk"] = float(c[:, 8:16, 1].mean()) / nC
+    out["helper_stage_cycles_per_chunk"] = float(c[:, 8:16, 2].mean()) / nC
     return out
 
 
@@ -454,11 +460,11 @@ def run_mixer_step(args, torch, m2, si, d_model: int = 4480):
                     "out-projection; random-init weights"}
 
 
-def run_generation(args, torch, m2, si, ring: int = 64):
+def run_generation(args, torch, m2, si):
     """The 9B generation-shaped run on one layer: batch 8, an 8192-token one-call prefill
     (chunk 64), then 16384 sequential decode steps carrying both caches. Inputs are drawn on
-    the device from a seeded generator with the recipe's distributions; the decode steps
-    cycle through a ring of 64 drawn steps (fresh values per step do not change the work).
+    the device from a seeded generator with the recipe's distributions, fresh for every
+    decode step (all 16384 steps' inputs, about 5 GB, are drawn before the timed run).
     Reports the prefill time, the mean decode step over all steps launched back to back,
     the median and 99th percentile of 1000 individually timed steps, and tokens/s over the
     whole run."""
@@ -483,8 +489,9 @@ def run_generation(args, torch, m2, si, ring: int = 64):
     y = torch.empty(B, L, di, dtype=bf, device="cuda")
     d = m2.make_dims(B, L, H, G, 64, m2.MAMBA2_BF16)
     ws = torch.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=torch.uint8, device="cuda")
-    su, sz, sdt = xbc(ring, B), torch.randn(ring, B, di, generator=gen, device="cuda").to(bf), \
-        torch.randn(ring, B, H, generator=gen, device="cuda").to(bf)
+    K = cfg.decode_steps
+    su, sz, sdt = xbc(K, B), torch.randn(K, B, di, generator=gen, device="cuda").to(bf), \
+        torch.randn(K, B, H, generator=gen, device="cuda").to(bf)
     yt = torch.empty(B, di, dtype=bf, device="cuda")
 
     def prefill():
@@ -492,7 +499,7 @@ def run_generation(args, torch, m2, si, ring: int = 64):
                                    y, ngroups=G, chunk=64, workspace=ws)
 
     def step(k):
-        i = k % ring
+        i = k % K
         m2.mamba2_state_update(su[i], p["conv_w"], p["conv_b"], cs, sdt[i], p["dt_bias"], p["A"], p["D"], sz[i],
                                h, yt, ngroups=G)
 

@@ -136,7 +136,7 @@ size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
  *           MAMBA2_ERR_WORKSPACE if missing or too small
  * x/B/C may be views into one xBC tensor (row stride = its channel count).
  * With seqlen 0 nothing per-token is read or written (those pointers may be
- * NULL) and h_final receives h0 (or zeros). Row strides above 2^25 elements are
+ * NULL) and h_final receives h0 (or zeros). Row strides above 2^23 elements are
  * rejected (MAMBA2_ERR_SHAPE).
  */
 int mamba2_ssd_prefill(const mamba2_dims* dims, const void* x, int64_t x_stride, const void* Bm,
@@ -187,15 +187,21 @@ int mamba2_conv_ssd_prefill(const mamba2_dims* dims, const void* xBC, int64_t xb
  * bitwise those of that call) with a cycle profile of the scan's contraction phases, the
  * measurement behind the per-phase MFMA rates (the MFMA contractions of the SSD scan:
  * hyper.ai summary, section "方法"). For scan workgroup k (k < batch * nheads, one per
- * (sequence, head)) and wave v (16 per workgroup), phase_cycles[(k * 16 + v) * 4 + i] gets
+ * (sequence, head)) and wave v (16 per workgroup), phase_cycles[(k * 16 + v) * 8 + i] gets
  * shader-clock cycles (s_memtime) summed over the chunk loop:
  *   i = 0  the whole chunk loop;
  *   i = 1  waves 0-3: the carried-state output H^T C^T of their 32x32 output tile;
  *          waves 4-7: the state update B^T (w x) of their 32 state rows;
+ *          waves 8-15: building the masked decay tiles of the next chunk;
  *   i = 2  waves 0-3: the intra-chunk product X^T M^T of their tile;
- *   i = 3  bits of a value the stamps read (kept so that no phase is optimised away).
- * A phase runs from before its first operand read to after the first read of its result.
- * phase_cycles: device memory of batch * nheads * 64 uint64, 8-byte aligned, not
+ *          waves 8-15: staging the next chunk (its loads' arrival, the x conv, the hi/lo
+ *          splits, the LDS stores);
+ *   i = 3  bits of a value the stamps read (kept so that no phase is optimised away);
+ *   i = 4  time spent in the chunk's barrier (waiting for the slowest role);
+ *   i = 5..7  zero.
+ * A contraction phase runs from before its first operand read to after the first read of
+ * its result.
+ * phase_cycles: device memory of batch * nheads * 128 uint64, 8-byte aligned, not
  * overlapping any other argument (MAMBA2_ERR_NULL / _ALIGN / _ALIAS otherwise); fp32 io
  * is MAMBA2_ERR_UNSUPPORTED. With seqlen 0 it is not written. The stamps slow the scan a
  * little; this call is for measurement, not for production.

@@ -194,7 +194,7 @@ def mamba2_conv_ssd_prefill(xBC, conv_w, conv_bias, conv_state, dt_raw, dt_bias,
 def mamba2_conv_ssd_prefill_profile(xBC, conv_w, conv_bias, conv_state, dt_raw, dt_bias, A, D, z, h0,
                                     h_final, y, phase_cycles, *, ngroups: int, chunk: int, workspace) -> None:
     """mamba2_conv_ssd_prefill with the scan's phase profile written to phase_cycles (an int64
-    device tensor of batch * nheads * 64 elements)."""
+    device tensor of batch * nheads * 128 elements)."""
     B, L, H = dt_raw.shape
     d = make_dims(B, L, H, ngroups, chunk, io_dtype_of(xBC))
     ws_bytes = workspace.numel() * workspace.element_size()

@@ -61,6 +61,14 @@ template <> struct Raw4<float> {
   f32x4 v;
   __device__ __forceinline__ float get(int i) const { return v[i]; }
 };
+// Accesses at a 32-bit byte offset from a base every lane of the wave shares: the compiler
+// can then use the scalar-base, 32-bit-offset form and needs no 64-bit address arithmetic.
+template <typename V> __device__ __forceinline__ V ld_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <typename V> __device__ __forceinline__ void st_at(void* base, uint32_t byte_off, const V& v) {
+  *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + byte_off) = v;
+}
 template <typename T> __device__ __forceinline__ Raw4<T> ld4(const T* p) {
   Raw4<T> r;
   r.v = *reinterpret_cast<const decltype(r.v)*>(p);

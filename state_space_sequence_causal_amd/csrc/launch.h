@@ -35,7 +35,7 @@ struct ConvArgs {
   void* state;
   int Cc;
 };
-// phase_cycles: NULL, or [B * H][16 waves][4] uint64 that receive the scan's phase profile
+// phase_cycles: NULL, or [B * H][16 waves][8] uint64 that receive the scan's phase profile
 // (cycles of the chunk loop and of each wave's contraction phases, summed over chunks).
 hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hipStream_t stream,
                                    uint64_t* phase_cycles = nullptr);

@@ -73,8 +73,8 @@ int check_stride(const char* name, const void* p, int64_t stride, int64_t width,
   return MAMBA2_OK;
 }
 
-// The prefill kernels form offsets inside a chunk's rows in 32 bits.
-constexpr int64_t kMaxStride = (int64_t)1 << 25;
+// The prefill kernels form byte offsets inside a chunk's rows in 32 bits.
+constexpr int64_t kMaxStride = (int64_t)1 << 23;
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MAMBA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -153,7 +153,7 @@ M2_EXPORT int mamba2_ssd_prefill(const mamba2_dims* d, const void* x, int64_t x_
   if (z && (st = check_stride("z", z, z_stride, H * P, io))) return st;
   if (x_stride > kMaxStride || b_stride > kMaxStride || c_stride > kMaxStride || y_stride > kMaxStride ||
       (z && z_stride > kMaxStride))
-    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^23 elements are not supported");
   if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
     return fail(MAMBA2_ERR_ALIGN, "h0 / h_final must be 16-byte aligned");
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
@@ -261,7 +261,7 @@ int conv_ssd_prefill_checked(const mamba2_dims* d, const void* xBC, int64_t xbc_
   if ((st = check_stride("y", y, y_stride, HP, io))) return st;
   if (z && (st = check_stride("z", z, z_stride, HP, io))) return st;
   if (xbc_stride > kMaxStride || y_stride > kMaxStride || (z && z_stride > kMaxStride))
-    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^23 elements are not supported");
   if (!aligned16(conv_w)) return fail(MAMBA2_ERR_ALIGN, "conv_w is not 16-byte aligned");
   if (conv_state && !aligned16(conv_state)) return fail(MAMBA2_ERR_ALIGN, "conv_state is not 16-byte aligned");
   if ((h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
@@ -301,7 +301,7 @@ int conv_ssd_prefill_checked(const mamba2_dims* d, const void* xBC, int64_t xbc_
   if (phase_cycles) {
     if (io != MAMBA2_BF16) return fail(MAMBA2_ERR_UNSUPPORTED, "the phase profile covers bf16 io");
     if (reinterpret_cast<uintptr_t>(phase_cycles) & 7u) return fail(MAMBA2_ERR_ALIGN, "phase_cycles must be 8-byte aligned");
-    const Range rpc = span(phase_cycles, 1, 0, (int64_t)d->batch * H * 64, 8);
+    const Range rpc = span(phase_cycles, 1, 0, (int64_t)d->batch * H * 128, 8);
     for (const Range& r : ins)
       if (overlap(rpc, r)) return fail(MAMBA2_ERR_ALIAS, "phase_cycles overlaps an input");
     for (const Range& r : {ry, rcs, rhf, rws, rh0})
@@ -394,7 +394,7 @@ M2_EXPORT int mamba2_conv_ssd_prefill_varlen(
   if ((st = check_stride("y", y, y_stride, HP, io))) return st;
   if (z && (st = check_stride("z", z, z_stride, HP, io))) return st;
   if (xbc_stride > kMaxStride || y_stride > kMaxStride || (z && z_stride > kMaxStride))
-    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^25 elements are not supported");
+    return fail(MAMBA2_ERR_SHAPE, "row strides above 2^23 elements are not supported");
   if (!aligned16(conv_w) || !aligned16(conv_pool) || !aligned16(ssm_pool))
     return fail(MAMBA2_ERR_ALIGN, "conv_w, conv_pool and ssm_pool must be 16-byte aligned");
   if (!aligned4(cu_seqlens) || !aligned4(slots) || !aligned4(has_init))

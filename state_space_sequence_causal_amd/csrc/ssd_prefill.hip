@@ -467,18 +467,20 @@ static_assert(sizeof(Pipe64Smem<float>) <= 160 * 1024 && sizeof(Pipe64Smem<bf16>
 // each chunk's rows from the per-chunk info and, at a sequence start, the conv history
 // from the pool. The new conv histories are written at the end.
 // The phase profile (STAMP): s_memtime at phase boundaries, held in program order by
-// scheduling barriers. Per wave: [0] cycles of the whole chunk loop, [1] cycles of the
-// wave's first contraction phase summed over chunks (Y waves: H^T C^T; H waves:
-// B^T (w x)), [2] of its second (Y waves: X^T M^T), [3] a sink that keeps the values read
-// to close a phase alive. A phase runs from before its first operand read to after the
-// first read of its accumulator.
+// scheduling barriers. Per wave, summed over chunks: [0] cycles of the whole chunk loop,
+// [1] of the wave's first phase (Y waves: the contraction H^T C^T; H waves: B^T (w x);
+// helper waves: building the decay tiles), [2] of its second (Y waves: X^T M^T; helper
+// waves: staging the next chunk, the x conv included), [3] a sink that keeps the values
+// read to close a phase alive, [4] cycles spent in the chunk's barrier, [5..7] zero. A
+// contraction phase runs from before its first operand read to after the first read of
+// its accumulator.
 __device__ __forceinline__ uint64_t phase_stamp() {
   __builtin_amdgcn_sched_barrier(0);
   const uint64_t t = __builtin_amdgcn_s_memtime();
   __builtin_amdgcn_sched_barrier(0);
   return t;
 }
-constexpr int STAMP_SLOTS = 4;
+constexpr int STAMP_SLOTS = 8;
 
 template <typename T, bool CONV, bool VARLEN = false, bool STAMP = false>
 __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -567,8 +569,18 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
   // ring, which holds chunks c - 1 .. c + 2 during iteration c (a global read in the loop would
   // be a scalar load, and a pending scalar load makes every LDS wait a full drain)
   [[maybe_unused]] auto info_at = [&](int c, bool ring) -> int4 { return ring ? S.sInfo[c % 5] : cinfo[c]; };
-  [[maybe_unused]] uint64_t st_loop = 0, st_a = 0, st_b = 0;
+  [[maybe_unused]] uint64_t st_loop = 0, st_a = 0, st_b = 0, st_wait = 0;
   [[maybe_unused]] float st_sink = 0.f;
+  // the chunk's barrier; with STAMP, the cycles spent in it are counted
+  [[maybe_unused]] auto chunk_barrier = [&]() {
+    if constexpr (STAMP) {
+      const uint64_t w0 = phase_stamp();
+      __syncthreads();
+      st_wait += phase_stamp() - w0;
+    } else {
+      __syncthreads();
+    }
+  };
   [[maybe_unused]] auto stamps_out = [&]() {
     if constexpr (STAMP) {
       if (lane == 0) {
@@ -577,6 +589,8 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         o[1] = st_a;
         o[2] = st_b;
         o[3] = __float_as_uint(st_sink);
+        o[4] = st_wait;
+        o[5] = o[6] = o[7] = 0;
       }
     }
   };
@@ -587,15 +601,18 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     const int prow = pb * 32 + col, tl = tb * 32 + col;
     // the chunk's C fragments: bf16 holds them in registers, requested a chunk ahead; fp32
     // (twice the registers) loads each k step's fragment where it is used
-    auto cf_at = [&](int c, int j) {
-      return wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES +
-             ((size_t)(tb * C::KS_N + j) * 64 + lane) * C::FB;
+    using FV = decltype(Frag<T>{}.v);
+    const uint32_t cf_lane = (uint32_t)((tb * C::KS_N * 64 + lane) * C::FB);
+    auto cf_frag = [&](int c, int j) {
+      Frag<T> f;
+      f.v = ld_at<FV>(wsg + (size_t)c * C::REC_BYTES + C::G_BYTES + C::BT_BYTES, cf_lane + (uint32_t)(j * 64 * C::FB));
+      return f;
     };
     Frag<T> cf[SPLIT ? C::KS_N : 1];
     auto fetch_c = [&](int c) {
       if constexpr (SPLIT) {
 #pragma unroll
-        for (int j = 0; j < C::KS_N; ++j) cf[j] = ld_frag<T>(cf_at(c, j));
+        for (int j = 0; j < C::KS_N; ++j) cf[j] = cf_frag(c, j);
       }
     };
     if (nC > 0) fetch_c(0);
@@ -624,7 +641,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
             mma(acc, ha[j & 3], cf[j]);
             mma(acc, la[j & 3], cf[j]);
           } else {
-            mma(acc, ha[j & 3], ld_frag<T>(cf_at(c, j)));
+            mma(acc, ha[j & 3], cf_frag(c, j));
           }
           if (j + 4 < C::KS_N) {
             const int n = hsw(prow, 16 * (j + 4) + 8 * g2);
@@ -693,7 +710,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         st_a += s1 - s0;
         st_b += s3 - s2;
       }
-      __syncthreads();
+      chunk_barrier();
     }
     if constexpr (STAMP) {
       st_loop = phase_stamp() - st_loop;
@@ -726,11 +743,12 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
     };
     load_state(h0b);
+    const uint32_t bt_lane = (uint32_t)((hw * C::KS_Q * 64 + lane) * C::FB);
     auto fetch_bt = [&](int c) {
       const unsigned char* btf = wsg + (size_t)c * C::REC_BYTES + C::G_BYTES;
 #pragma unroll
       for (int j = 0; j < C::KS_Q; ++j)
-        af[j] = ld_frag<T>(btf + ((size_t)(hw * C::KS_Q + j) * 64 + lane) * C::FB);
+        af[j].v = ld_at<decltype(af[j].v)>(btf, bt_lane + (uint32_t)(j * 64 * C::FB));
     };
     auto publish = [&](int buf) {
 #pragma unroll
@@ -811,7 +829,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
       }
       publish(cur);
       fetch_bt(min(c + 1, nC - 1));
-      __syncthreads();
+      chunk_barrier();
     }
     if constexpr (STAMP) {
       st_loop = phase_stamp() - st_loop;
@@ -893,6 +911,13 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
       // x rows of the thread's tokens; with the conv, raw rows s0 - 3 .. s0 + 1
       constexpr int NX = CONV ? 5 : 2;
       Raw4<T> rX[NX], rZ[2];
+      // byte offsets of the thread's rows in a full chunk: x rows s0 + k from the x base, z
+      // rows s0 + k
+      uint32_t oxr[NX], ozr[2];
+#pragma unroll
+      for (int k = 0; k < NX; ++k) oxr[k] = ((uint32_t)(s0 + k) * xs + p0) * (uint32_t)sizeof(T);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) ozr[k] = ((uint32_t)(s0 + k) * zs + p0) * (uint32_t)sizeof(T);
       float rRec = 0.f;
       f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7 (4 hq .. 4 hq + 3)
       // the history rows before the sequence that this thread's first tokens read (zeros
@@ -919,26 +944,38 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
         const T* xc = xb + r0 * x_stride;
         const T* zc = zb + r0 * z_stride;
-        // Rows past the end of the sequence load the last row instead (finite values; their
-        // dt and v are zero, so they add nothing), which keeps the loads unconditional.
-        const int lim = nval - 1;
+        // with the conv, x is addressed from a base 3 rows back (raw rows s0 - 3 .. s0 + 1)
+        const T* xa = CONV ? xc - 3 * x_stride : xc;
+        using XV = decltype(rX[0].v);
+        if (nval >= Q && !(CONV && first)) {
+          // a full chunk after the first: the loop-invariant offsets
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint32_t s = (uint32_t)min(s0 + k, lim);
-          if constexpr (!CONV) rX[k] = ld4(xc + (s * xs + p0));
-          if constexpr (SPLIT) rZ[k] = ld4(zc + (s * zs + p0));
+          for (int k = 0; k < (CONV ? NX : 2); ++k) rX[k].v = ld_at<XV>(xa, oxr[k]);
+          if constexpr (SPLIT) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) rZ[k].v = ld_at<XV>(zc, ozr[k]);
+          }
+        } else {
+          // Rows past the end of the sequence load the last row instead (finite values; their
+          // dt and v are zero, so they add nothing), which keeps the loads unconditional. In
+          // the first chunk the rows before the sequence are read as row 0 and replaced when
+          // that chunk is staged.
+          const int lim = nval - 1;
+          const int lo = CONV && first ? 3 : 0;
+#pragma unroll
+          for (int k = 0; k < (CONV ? NX : 2); ++k) {
+            const uint32_t s = CONV ? (uint32_t)min(max(s0 + k, lo), lim + 3) : (uint32_t)min(s0 + k, lim);
+            rX[k].v = ld_at<XV>(xa, (s * xs + p0) * (uint32_t)sizeof(T));
+          }
+          if constexpr (SPLIT) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const uint32_t s = (uint32_t)min(s0 + k, lim);
+              rZ[k].v = ld_at<XV>(zc, (s * zs + p0) * (uint32_t)sizeof(T));
+            }
+          }
         }
         if constexpr (CONV) {
-          // raw rows s0 - 3 .. s0 + 1 of the chunk, addressed from a base 3 rows back; past the
-          // end the last row is read, and in the first chunk the rows before the sequence are
-          // read as row 0 and replaced when that chunk is staged
-          const T* xh = xc - 3 * x_stride;
-          const int lo = first ? 3 : 0;
-#pragma unroll
-          for (int k = 0; k < NX; ++k) {
-            const uint32_t s = (uint32_t)min(max(s0 + k, lo), lim + 3);
-            rX[k] = ld4(xh + (s * xs + p0));
-          }
           if constexpr (HIST) {
             // every chunk issues the same 3 loads (used only where a sequence starts)
             const T* hp = vd.hist + (size_t)(gc0 + c) * 3 * (H * SP) + h * SP + p0;
@@ -948,7 +985,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
       };
       auto load_rec = [&](int c) {
-        if constexpr (REC) rRec = hrec[(size_t)c * C::HREC_WORDS + htid];
+        if constexpr (REC) rRec = ld_at<float>(hrec + (size_t)c * C::HREC_WORDS, (uint32_t)htid * 4u);
       };
       auto put_rec = [&](int c) {
         if constexpr (REC) S.sRec[c % 3][htid] = rRec;
@@ -968,7 +1005,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         for (int k = 0; k < 2; ++k) {
           const int s = s0 + k;
           const Raw4<bf16> v = ld4(&S.sZ[c & 1][s][zpos(s, p0)]);
-          if (full || s < nval) *reinterpret_cast<bf16x4*>(yc + ((uint32_t)s * ys + p0)) = v.v;
+          if (full || s < nval) st_at(yc, ((uint32_t)s * ys + p0) * 2u, v.v);
         }
       };
       auto load_hist = [&]() {   // one sequence: the history rows, once
@@ -998,6 +1035,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         const float wb = s0 < 32 ? exp2_hw(rec[Q + 63]) : 1.f;
         const float w0 = vs.x * wb, w1 = vs.y * wb;
         T xv[2][4];
+        [[maybe_unused]] uint32_t xpk[4];   // CONV: the pair (token s0, s0 + 1) of column p0 + e
         if constexpr (CONV) {
           Raw4<T> r[NX];
 #pragma unroll
@@ -1008,11 +1046,13 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
               if (s0 - 3 + k < 0) r[k] = rH[k];   // rH[k] holds history row s0 + k
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < 4; ++e) {
+            float f[2];
 #pragma unroll
             for (int k = 0; k < 2; ++k)
-              xv[k][e] = (T)conv4_silu(cw[e], cb[e], r[k].get(e), r[k + 1].get(e), r[k + 2].get(e),
-                                       r[k + 3].get(e));
+              f[k] = conv4_silu(cw[e], cb[e], r[k].get(e), r[k + 1].get(e), r[k + 2].get(e), r[k + 3].get(e));
+            xpk[e] = pack_bf16(f[0], f[1]);
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1022,8 +1062,16 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const T x0 = xv[0][e], x1 = xv[1][e];
           const int p = p0 + e, sw = xs64(p, s0);
+          if constexpr (CONV) {
+            *reinterpret_cast<uint32_t*>(&S.sXt[buf][p][sw]) = xpk[e];
+            const float x0 = __uint_as_float(xpk[e] << 16), x1 = __uint_as_float(xpk[e] & 0xffff0000u);
+            const Split2 v = split2(x0 * w0, x1 * w1);
+            *reinterpret_cast<uint32_t*>(&S.sXW[buf][p][sw]) = v.hi;
+            *reinterpret_cast<uint32_t*>(&S.sXWlo[buf][p][sw]) = v.lo;
+            continue;
+          }
+          const T x0 = xv[0][e], x1 = xv[1][e];
           st_pair(&S.sXt[buf][p][sw], x0, x1);
           if constexpr (SPLIT) {
             const Split2 v = split2(to_f(x0) * w0, to_f(x1) * w1);
@@ -1035,13 +1083,13 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
       };
       auto fetch_gram = [&](int c) {   // quads 2 hm, 2 hm + 1 (or quad hq) of the stored tile
-        const float* tile = reinterpret_cast<const float*>(wsg + (size_t)c * C::REC_BYTES) +
-                            (size_t)kb * 1024 + 4 * lane;
+        const unsigned char* tile = wsg + (size_t)c * C::REC_BYTES + (size_t)kb * 4096;
+        const uint32_t lo = 16u * lane;
         if constexpr (PART == 2) {
-          gram[0] = *reinterpret_cast<const f32x4*>(tile + 512 * hm);
-          gram[1] = *reinterpret_cast<const f32x4*>(tile + 512 * hm + 256);
+          gram[0] = ld_at<f32x4>(tile, lo + 2048u * hm);
+          gram[1] = ld_at<f32x4>(tile, lo + 2048u * hm + 1024u);
         } else {
-          gram[0] = *reinterpret_cast<const f32x4*>(tile + 256 * hq);
+          gram[0] = ld_at<f32x4>(tile, lo + 1024u * hq);
         }
       };
       // half hm of tile kb of chunk c into sM[c & 1]: Gram tile times the decay from s to t
@@ -1077,6 +1125,25 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
           const int tl = tb * 32 + col;
           float mv[8];
           const float pit = sPi[tl], plt = sPl[tl];
+          // Where the block's decay stays above 2^-96 the decay from s to t factors into
+          // v_s = dt_s 2^(pi_end - pi_s) (the record) and 2^(pi_t - pi_end) <= 2^96, both
+          // normal floats: one exponential per lane instead of one per element.
+          const float pe = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sPi[tb * 32 + 31])));
+          const float pel = sPl[tb * 32 + 31];
+          if (SPLIT && pe > -96.f) {
+            const float at = exp2_hw((pit - pe) + (plt - pel));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
+              const f32x4 vs = *reinterpret_cast<const f32x4*>(&rec[2 * Q + sr]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float v = (sr + q <= tl) ? gram[j][q] * (vs[q] * at) : 0.f;
+                if (sr + q == tl) v += Dh;
+                mv[4 * j + q] = v;
+              }
+            }
+          } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int sr = tb * 32 + 16 * hm + 8 * j + 4 * g2;
@@ -1089,6 +1156,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
               if (sr + q == tl) v += Dh;
               mv[4 * j + q] = v;
             }
+          }
           }
           if constexpr (SPLIT) {
             Frag<bf16> mh, ml;
@@ -1154,12 +1222,20 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         }
         // ---- chunk c + 1: tiles and staging. Chunk indices are clamped, so every iteration
         // issues the same memory operations (the last stages a copy nobody reads).
+        [[maybe_unused]] uint64_t s0 = 0, s1 = 0;
+        if constexpr (STAMP) s0 = phase_stamp();
         build(c + 1);
+        if constexpr (STAMP) {
+          s1 = phase_stamp();
+          st_a += s1 - s0;
+        }
         fetch_gram(min(c + 2, nC - 1));
         if constexpr (SPLIT) {
           if (c >= 1) flush_y(c - 1, !VARLEN, im1);   // one sequence: chunk c - 1 < nC - 1 is full
         }
+        if constexpr (STAMP) s0 = phase_stamp();
         stage(c + 1, std::false_type{}, ip1);
+        if constexpr (STAMP) st_b += phase_stamp() - s0;
         put_rec(c + 2);
         load_set(min(c + 2, nC - 1), ip2);
         load_rec(min(c + 3, nC - 1));
@@ -1167,7 +1243,7 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
           reinterpret_cast<int*>(&S.sInfo[(c + 3) % 5])[lane & 3] = rInfo;
           rInfo = info_word(c + 4);
         }
-        __syncthreads();
+        chunk_barrier();
       }
       if constexpr (STAMP) {
         st_loop = phase_stamp() - st_loop;

@@ -98,7 +98,7 @@ def test_prefill_rejects_dims(kw, code):
     (dict(bs=100), ESHAPE), (dict(ys=250), ESHAPE), (dict(h0=BASE + 16 * MB + 8), EALIGN),
     (dict(y=BASE + 4 * MB), EALIAS), (dict(y=BASE), EALIAS), (dict(hf=BASE + 12 * MB), EALIAS),
     (dict(y=BASE + 20 * MB), EALIAS), (dict(hf=BASE + 16 * MB + 4096), EALIAS),
-    (dict(xs=(1 << 25) + 4), ESHAPE), (dict(zs=(1 << 25) + 4), ESHAPE),
+    (dict(xs=(1 << 23) + 4), ESHAPE), (dict(zs=(1 << 23) + 4), ESHAPE),
 ])
 def test_prefill_rejects_pointers(kw, code):
     assert prefill(dims(), **kw) == code, m2.mamba2_last_error()
@@ -207,7 +207,7 @@ def conv_prefill(d, **kw):
     (dict(dtb=None), ENULL), (dict(A=None), ENULL),
     (dict(us=500), ESHAPE), (dict(us=1028), EALIGN), (dict(u=BASE + 8), EALIGN),
     (dict(w=BASE + 4 * MB + 4), EALIGN), (dict(cs=BASE + 6 * MB + 8), EALIGN),
-    (dict(us=(1 << 25) + 8), ESHAPE), (dict(ys=250), ESHAPE),
+    (dict(us=(1 << 23) + 8), ESHAPE), (dict(ys=250), ESHAPE),
     (dict(y=BASE), EALIAS), (dict(y=BASE + 6 * MB), EALIAS), (dict(cs=BASE), EALIAS),
     (dict(cs=BASE + 24 * MB), EALIAS), (dict(hf=BASE), EALIAS), (dict(cs=BASE + 16 * MB), EALIAS),
     (dict(ws=BASE + 6 * MB), EALIAS), (dict(ws=None), 7), (dict(wsb=1000), 7),

@@ -179,14 +179,16 @@ def test_profile_call_bitwise_and_cycles():
     o = _operands(cfg, inp, cs0, True, True, True, True, 0)
     d = m2.make_dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.ngroups, 64, m2.MAMBA2_BF16)
     ws = t.empty(m2.mamba2_conv_ssd_prefill_workspace_bytes(d), dtype=t.uint8, device="cuda")
-    cyc = t.zeros(cfg.batch * cfg.nheads * 64, dtype=t.int64, device="cuda")
+    cyc = t.zeros(cfg.batch * cfg.nheads * 128, dtype=t.int64, device="cuda")
     m2.mamba2_conv_ssd_prefill_profile(o["u"], o["w"], o["b"], o["cs"], o["dt"], o["dtb"], o["A"], o["D"], o["z"],
                                        o["h0"], o["hf"], o["y"], cyc, ngroups=cfg.ngroups, chunk=64, workspace=ws)
     t.cuda.synchronize()
     np.testing.assert_array_equal(host(o["y"]), y0)
     np.testing.assert_array_equal(host(o["hf"]), h0_)
     np.testing.assert_array_equal(host(o["cs"]), c0)
-    c = cyc.view(cfg.batch * cfg.nheads, 16, 4).cpu().numpy()
+    c = cyc.view(cfg.batch * cfg.nheads, 16, 8).cpu().numpy()
     assert (c[:, :, 0] > 0).all()
-    assert (c[:, 0:8, 1] > 0).all() and (c[:, 0:8, 1] < c[:, 0:8, 0]).all()
+    assert (c[:, :, 1] > 0).all() and (c[:, :, 1] < c[:, :, 0]).all()
     assert (c[:, 0:4, 2] > 0).all() and (c[:, 0:4, 2] < c[:, 0:4, 0]).all()
+    assert (c[:, 8:16, 2] > 0).all() and (c[:, 8:16, 2] < c[:, 8:16, 0]).all()
+    assert (c[:, :, 4] < c[:, :, 0]).all() and (c[:, :, 5:] == 0).all()
