@@ -26,8 +26,12 @@
 // after, so the conv that gates the stream does not wait behind the state. A
 // head's z is requested when its stream starts and used when it ends. y is
 // reduced over the four row groups with cross-lane shuffles. At batch 64 the
-// kernel streams about 5.35 TB/s, against about 5.8 TB/s for a plain in-place
-// stream of the same size on this part.
+// kernel streams about 5.8 TB/s, the rate of a plain in-place stream of the same
+// size on this part (an elementwise in-place multiply: 5.87 TB/s). The order in
+// which the chip's XCDs take the state blocks matters: with the blocks of each
+// XCD contiguous the same kernel streamed 5.45 TB/s; walking a head's parts from
+// a start that differs between waves, or letting a workgroup's waves move through
+// its heads together, 4.6 to 4.8 TB/s.
 #include "device.h"
 #include "launch.h"
 
@@ -84,8 +88,10 @@ void state_update_kernel(
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
   const int hpg = H / G;
-  const int nblk = gridDim.x;
-  const int id = xcd_local_order(blockIdx.x, nblk);
+  // Workgroups in launch order, which the dispatcher deals to the XCDs in turn: each XCD then
+  // streams every eighth state block rather than one contiguous eighth of the cache (9B batch
+  // 64: 93.8 us against 100.5 us with the blocks of an XCD contiguous).
+  const int id = blockIdx.x;
   const int part = id % SPLIT;
   const int b = id / SPLIT / G, g = id / SPLIT % G;
   const int hpp = hpg / SPLIT;         // heads of this workgroup
