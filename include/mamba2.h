@@ -106,11 +106,9 @@ int mamba2_conv1d(const mamba2_dims* dims, int32_t channels, const void* u, int6
  * needs for `dims` (0 if `dims` is invalid or the sequence is empty). The scan
  * first computes, once per (sequence, group, chunk), the causal Gram tiles
  * B_s . C_t of the chunk in fp32 and B^T and C laid out as MFMA operands, which
- * every head of the group then reads, and per (sequence, head, chunk) dt, its
- * prefix sums (a hi and a lo part) and per-token decay weights (4 fp32 per token).
- * The kernels tile at 64 tokens whatever chunk dims names, so with e = sizeof(io):
- *   nchunks * (batch * ngroups * (12288 + 16384 * e) + batch * nheads * 1024)
- *                                                       nchunks = ceil(seqlen / 64)
+ * every head of the group then reads. The kernels tile at 64 tokens whatever
+ * chunk dims names, so with e = sizeof(io):
+ *   nchunks * batch * ngroups * (12288 + 16384 * e),   nchunks = ceil(seqlen / 64)
  * The caller owns it; its contents are scratch (nothing is kept between calls).
  */
 size_t mamba2_ssd_prefill_workspace_bytes(const mamba2_dims* dims);
@@ -221,7 +219,7 @@ int mamba2_conv_ssd_prefill_profile(const mamba2_dims* dims, const void* xBC, in
  * every device it runs on until the process ends. Arguments, results and errors are those
  * of mamba2_conv_ssd_prefill; a setting whose workspace
  * (mamba2_conv_ssd_prefill_workspace_bytes) exceeds 64 MiB is rejected with
- * MAMBA2_ERR_WORKSPACE (at the 12B shape, bf16: up to batch * seqlen = 8192 tokens).
+ * MAMBA2_ERR_WORKSPACE (at the 12B shape, bf16: up to batch * seqlen = 11904 tokens).
  * Every call on a device uses that device's one array: two calls in flight at once on one
  * device (on different streams) race and give undefined results. Calls on one stream
  * are ordered and safe. Nothing in the array needs to start at zero.
@@ -237,7 +235,7 @@ int mamba2_conv_ssd_prefill_noalloc(const mamba2_dims* dims, const void* xBC, in
  * mamba2_conv_ssd_prefill_varlen for `dims` (batch = number of sequences, seqlen =
  * total packed rows; bf16 io, any supported chunk: the kernels tile at 64), 0 if
  * `dims` is invalid or another setting:
- *   M * (ngroups * R + nheads * 1024 + 16 + 384 * nheads) + 8 * (batch + 1),
+ *   M * (ngroups * R + 16 + 384 * nheads) + 8 * (batch + 1),
  *   M = seqlen / 64 + batch
  * with R the per-(group, chunk) record of mamba2_ssd_prefill_workspace_bytes at chunk 64
  * (4096 * 3 + 2 * 128 * 64 * 2 bytes).

@@ -93,7 +93,48 @@ __device__ __forceinline__ void st_pair(float* p, float a, float b) {
 
 // ---------------------------------------------------------------- math
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 __device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(expf(v)); }
+// softplus from the hardware exponential, logarithm and reciprocal (a few ulp, against the
+// libm form above): max(v, 0) + log1p(e) with e = exp(-|v|) <= 1, and log1p(e) = e where
+// u = 1 + e rounds to 1, else log(u) e / (u - 1), whose quotient cancels the rounding of u
+// (Goldberg, "What every computer scientist should know about floating-point arithmetic",
+// the log1p example). Above 20 it is v, as softplus_f.
+__device__ __forceinline__ float softplus_hw(float v) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+  const float u = 1.f + e;
+  const float l = u == 1.f ? e : __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(u - 1.f));
+  return v > 20.f ? v : fmaxf(v, 0.f) + l;
+}
+// fp64 row moves across lanes (DPP, both 32-bit halves; lanes without a source and rows
+// outside ROWS read 0)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, 0xf, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xf, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Inclusive fp64 sum over each 32-lane half of the wave: doubling shifts inside rows of 16
+// lanes (row_shr 1, 2, 4, 8), then the total of row 0 (row 2) added to row 1 (row 3)
+// (row_bcast:15 into rows 1 and 3).
+__device__ __forceinline__ double scan32_f64(double v) {
+  v += dpp_f64<0x111, 0xf>(v);
+  v += dpp_f64<0x112, 0xf>(v);
+  v += dpp_f64<0x114, 0xf>(v);
+  v += dpp_f64<0x118, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  return v;
+}
+// lane 31's value in lanes 0..31, lane 63's in lanes 32..63
+__device__ __forceinline__ double half_last_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const int src = lane < 32 ? 31 : 63;
+  const uint32_t lo31 = __builtin_amdgcn_readlane((int)(uint32_t)b, 31), lo63 = __builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint32_t hi31 = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 31),
+                 hi63 = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __builtin_bit_cast(double, src == 31 ? ((uint64_t)hi31 << 32) | lo31 : ((uint64_t)hi63 << 32) | lo63);
+}
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + expf(-v)); }
 // 2^v with the hardware exponential (v_exp_f32, about 1 ulp); used for decay factors,
 // whose arguments are <= 0.

@@ -61,8 +61,7 @@ size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G);
 constexpr size_t PREFILL_SCRATCH_BYTES = (size_t)64 << 20;
 hipError_t prefill_scratch_on_current_device(void** ptr);
 // Workspace bytes the prep/scan pair needs: per (sequence, group, chunk) the causal Gram
-// tiles in fp32 and B^T and C in MFMA operand order; per (sequence, head, chunk) dt and
-// its block prefix sums.
+// tiles in fp32 and B^T and C in MFMA operand order.
 size_t ssd_prefill_workspace(int io_bf16, int chunk, int B, int L, int H, int G);
 
 struct DecodeArgs {

@@ -15,15 +15,15 @@
 //    Gram tiles G^T[s][t] = B_s . C_t of the causal lower triangle in fp32 (MFMA, exact
 //    products of the bf16 inputs) in MFMA accumulator order, and B^T and C in MFMA operand
 //    order, so that each wave later reads every operand as 1 KiB contiguous per
-//    instruction; these are shared by all heads of the group. For each head of the group
-//    it writes dt = softplus(dt_raw + dt_bias), the inclusive prefix pi of dt*A*log2(e)
-//    inside 32-token blocks, and v_s = exp2(pi_end - pi_s) dt_s (decay from token s to the
-//    end of its block, times dt_s). The prefix is summed in fp64 and kept as an fp32 pair
-//    pi = pi_hi + pi_lo: after a token whose decay is very strong the prefix values of a
-//    block are large, and the decay between two later tokens, a difference of two of them,
-//    would otherwise carry the rounding of their size rather than of its own.
+//    instruction; these are shared by all heads of the group.
 //  * ssd_scan64, one workgroup of 16 waves per (b, h), described at its definition. The fp32
-//    state stays on chip for the whole sequence.
+//    state stays on chip for the whole sequence. One of its waves forms each chunk's per-token
+//    records from dt_raw: dt = softplus(dt_raw + dt_bias), the inclusive prefix pi of
+//    dt*A*log2(e) inside 32-token blocks, and v_s = exp2(pi_end - pi_s) dt_s (decay from
+//    token s to the end of its block, times dt_s). The prefix is summed in fp64 and kept as
+//    an fp32 pair pi = pi_hi + pi_lo: after a token whose decay is very strong the prefix
+//    values of a block are large, and the decay between two later tokens, a difference of
+//    two of them, would otherwise carry the rounding of their size rather than of its own.
 //
 // The chunk length a call names (64, 128 or 256) is a tiling choice: the result does not
 // depend on it up to rounding, and both kernels always tile at 64 tokens.
@@ -49,6 +49,15 @@
 
 namespace m2 {
 
+// dt inputs of the scan: dt_raw [rows][stride] (head h at column h), dt_bias [H], A [H]
+template <typename T>
+struct DtDev {
+  const T* raw;
+  int64_t stride;
+  const float* bias;
+  const float* A;
+};
+
 constexpr int SP = 64;   // head dim
 constexpr int SN = 128;  // state dim
 constexpr int PREP_THREADS = 256;
@@ -69,10 +78,6 @@ struct Cfg {
   static constexpr size_t BT_BYTES = (size_t)(SN / 32) * KS_Q * 64 * FB;
   static constexpr size_t CF_BYTES = (size_t)NTB * KS_N * 64 * FB;
   static constexpr size_t REC_BYTES = G_BYTES + BT_BYTES + CF_BYTES;
-  // workspace record per (b, h, chunk): dt[Q] | pi_hi[Q] | v[Q] | pi_lo[Q]
-  static constexpr int HREC_WORDS = 4 * Q;
-  static constexpr size_t HREC_BYTES = HREC_WORDS * sizeof(float);
-  static constexpr int TPL = Q / 64;                        // decay tokens per lane (lane + 64 k)
 };
 
 __device__ __forceinline__ int tile_tb(int k) {  // column block of lower-triangle tile k < 36
@@ -182,8 +187,7 @@ __global__ __launch_bounds__(VIDX_THREADS) void varlen_index_kernel(const int32_
 template <typename T, int Q, bool CONV, bool VARLEN = false>
 __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void ssd_prep_kernel(
     const T* __restrict__ Bm, int64_t b_stride, const T* __restrict__ Cm, int64_t c_stride,
-    const T* __restrict__ dt_raw, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    int64_t dt_stride, unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv, VarlenDev vd) {
+    unsigned char* __restrict__ ws, int L, int H, int G, int nC, ConvArgs cv, VarlenDev vd) {
   static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
   using C = Cfg<T, Q>;
   constexpr int VE = C::VE;
@@ -227,10 +231,9 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
   const int col = lane & 31, g2 = lane >> 5;
   const int nvalid = min(Q, len - t0);
 
-  // The B and C rows are requested first; the dt records are formed while they arrive, and
-  // then the rows go to LDS (zero past the end of the sequence).
+  // The B and C rows are requested first, then go to LDS (zero past the end of the sequence).
   constexpr int NR = CONV ? 11 : Q * SN / VE / PREP_THREADS;   // 16-byte row vectors per thread
-  constexpr bool HOLD = CONV;   // rows held in registers across the dt phase
+  constexpr bool HOLD = CONV;   // rows held in registers for the conv
   Vec<T> rB[HOLD ? NR : 1], rC[CONV || !HOLD ? 1 : NR];
   // CONV: a thread convolves one 16-byte vector of B (vectors 0..15) or C (16..31) over 8
   // consecutive tokens s1 .. s1 + 7, from the 11 raw rows s1 - 3 .. s1 + 7 (chunk-relative;
@@ -265,46 +268,6 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
       const bool ok = s < nvalid;
       st16(&sB[s][e0], ok ? ld16(Bb + (int64_t)s * b_stride + e0) : zero16<T>());
       st16(&sC[s][e0], ok ? ld16(Cb + (int64_t)s * c_stride + e0) : zero16<T>());
-    }
-  }
-  // per head of the group: dt and the 32-token block prefix of dt*A*log2(e); a wave takes
-  // items wave, wave + 4, ... and requests up to 8 of them at once
-  {
-    const int hpg = H / G, nitems = hpg * C::TPL;
-    const size_t hrec0 = (size_t)b * H * nC;
-    unsigned char* hbase = ws + (size_t)gridDim.x * C::REC_BYTES;
-    constexpr int DB = 8;
-    for (int i0 = wave; i0 < nitems; i0 += DB * (PREP_THREADS / 64)) {
-      float raw[DB];
-#pragma unroll
-      for (int u = 0; u < DB; ++u) {
-        const int item = i0 + u * (PREP_THREADS / 64);
-        const int j = item / C::TPL, s = 64 * (item % C::TPL) + lane;
-        raw[u] = item < nitems && s < nvalid ? to_f(dt_raw[(row0 + s) * dt_stride + g * hpg + j]) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < DB; ++u) {
-        const int item = i0 + u * (PREP_THREADS / 64);
-        if (item >= nitems) break;
-        const int j = item / C::TPL, k = item % C::TPL;
-        const int h = g * hpg + j;
-        const int s = 64 * k + lane;
-        const float dt = s < nvalid ? softplus_f(raw[u] + dt_bias[h]) : 0.f;
-        // the block prefix in fp64 (each step dt*A*log2e rounded once, in fp32)
-        double run = (double)(dt * A[h] * kLog2e);
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) {
-          const double o = __shfl_up(run, d, 32);
-          if ((lane & 31) >= d) run += o;
-        }
-        const double tot = __shfl(run, (lane & 32) + 31);   // the block's total
-        const float hi = (float)run;
-        float* hr = reinterpret_cast<float*>(hbase + (hrec0 + (size_t)h * nC + c) * C::HREC_BYTES);
-        hr[s] = dt;
-        hr[Q + s] = hi;
-        hr[2 * Q + s] = exp2_hw((float)(tot - run)) * dt;   // decay from s to the end of its block, times dt
-        hr[3 * Q + s] = (float)(run - (double)hi);
-      }
     }
   }
   if constexpr (CONV) {
@@ -487,7 +450,8 @@ __global__ __launch_bounds__(P64_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
 void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* __restrict__ D,
                        const T* __restrict__ z, int64_t z_stride, const float* h0, float* h_final,
                        T* __restrict__ y, int64_t y_stride, const unsigned char* __restrict__ ws,
-                       int Lrows, int H, int G, ConvArgs cv, VarlenDev vd, uint64_t* __restrict__ stamps) {
+                       int Lrows, int H, int G, ConvArgs cv, VarlenDev vd, DtDev<T> dd,
+                       uint64_t* __restrict__ stamps) {
   static_assert(!VARLEN || CONV, "the packed batch runs with the conv fused");
   static_assert(!CONV || sizeof(T) == 2, "the conv runs inside the scan for bf16 io");
   static_assert(!STAMP || (CONV && !VARLEN), "the phase profile covers the one-call prefill");
@@ -512,7 +476,6 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
   [[maybe_unused]] int s_begin = 0, s_end = 0, gc0 = 0;
   [[maybe_unused]] const int4* cinfo = nullptr;
   const unsigned char* wsg;
-  const float* hrec;
   const float* h0b;
   float* hfb;
   const T* hist_rd = nullptr;
@@ -539,8 +502,6 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     row0 = 0;
     cinfo = vd.info + gc0;
     wsg = ws + ((size_t)g * vd.maxC + gc0) * C::REC_BYTES;
-    hrec = reinterpret_cast<const float*>(ws + (size_t)G * vd.maxC * C::REC_BYTES +
-                                          ((size_t)h * vd.maxC + gc0) * C::HREC_BYTES);
     h0b = nullptr;                  // the initial state of the stream's first sequence
     hfb = nullptr;                  // states are stored per sequence
     if (L > 0) {
@@ -552,8 +513,6 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     row0 = (int64_t)b * L;
     const int nCw = (L + Q - 1) / Q;
     wsg = ws + (size_t)(b * G + g) * nCw * C::REC_BYTES;
-    hrec = reinterpret_cast<const float*>(ws + (size_t)G * nCw * C::REC_BYTES * (size_t)(gridDim.x / H) +
-                                          ((size_t)b * H + h) * nCw * C::HREC_BYTES);
     const int64_t sbase = ((int64_t)b * H + h) * SN * SP;
     h0b = h0 ? h0 + sbase : nullptr;
     hfb = h_final ? h_final + sbase : nullptr;
@@ -901,13 +860,14 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
     // copy issues a fixed sequence of memory operations and the compiler's count of
     // outstanding loads stays exact: a merged count would wait for loads just issued.
-    auto helpers = [&](auto part_tag, auto rec_tag, auto duty_tag) {
+    auto helpers = [&](auto part_tag, auto duty_tag) {
       constexpr int PART = decltype(part_tag)::value;   // 2: a diagonal half, 4: an off quarter
-      constexpr bool REC = decltype(rec_tag)::value;
       // VARLEN duties: HIST, helper wave 0 (whose threads hold the first tokens of a chunk),
-      // loads each chunk's conv history rows; RING, helper wave 4, keeps the info ring
+      // loads each chunk's conv history rows; RING, helper wave 4, keeps the info ring.
+      // RECS, helper wave 5: the dt / pi_hi / v / pi_lo records of each chunk, two chunks ahead
       constexpr bool HIST = VARLEN && decltype(duty_tag)::value == 1;
       constexpr bool RING = VARLEN && decltype(duty_tag)::value == 2;
+      constexpr bool RECS = decltype(duty_tag)::value == 3;
       // x rows of the thread's tokens; with the conv, raw rows s0 - 3 .. s0 + 1
       constexpr int NX = CONV ? 5 : 2;
       Raw4<T> rX[NX], rZ[2];
@@ -918,7 +878,8 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
       for (int k = 0; k < NX; ++k) oxr[k] = ((uint32_t)(s0 + k) * xs + p0) * (uint32_t)sizeof(T);
 #pragma unroll
       for (int k = 0; k < 2; ++k) ozr[k] = ((uint32_t)(s0 + k) * zs + p0) * (uint32_t)sizeof(T);
-      float rRec = 0.f;
+      [[maybe_unused]] float rDt = 0.f;   // RECS: dt_raw of token `lane` of the chunk in flight
+      [[maybe_unused]] const float dtb = RECS ? dd.bias[h] : 0.f, Ah = RECS ? dd.A[h] : 0.f;
       f32x4 gram[2];                     // Gram tile registers 8 hm .. 8 hm + 7 (4 hq .. 4 hq + 3)
       // the history rows before the sequence that this thread's first tokens read (zeros
       // without a history): for one sequence loaded once in the prologue, for a packed batch
@@ -984,11 +945,45 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
           }
         }
       };
-      auto load_rec = [&](int c) {
-        if constexpr (REC) rRec = ld_at<float>(hrec + (size_t)c * C::HREC_WORDS, (uint32_t)htid * 4u);
+      // RECS: chunk c's rows (its first row, its valid rows), then its dt_raw into rDt (past
+      // the end of the sequence the last row is read and not used)
+      [[maybe_unused]] auto rows_of = [&](int c, int4 ci, int64_t& r0, int& nval) {
+        if constexpr (VARLEN) {
+          r0 = ci.x;
+          nval = ci.y & 255;
+        } else {
+          r0 = row0 + (int64_t)c * Q;
+          nval = L - c * Q;
+        }
       };
-      auto put_rec = [&](int c) {
-        if constexpr (REC) S.sRec[c % 3][htid] = rRec;
+      auto load_dt = [&](int c, int4 ci) {
+        if constexpr (RECS) {
+          int64_t r0;
+          int nval;
+          rows_of(c, ci, r0, nval);
+          rDt = to_f(dd.raw[(r0 + min(lane, nval - 1)) * dd.stride + h]);
+        }
+      };
+      // RECS: the records of chunk c (whose dt_raw is in rDt) into slot `slot` % 3: per token
+      // dt = softplus(dt_raw + dt_bias) (zero past the end), the prefix pi of dt A log2(e) over
+      // its 32-token block summed in fp64 (each term rounded once in fp32) and kept as
+      // pi_hi + pi_lo, and v = dt 2^(pi at the block end - pi), the decay from the token to
+      // the end of its block
+      auto make_rec = [&](int slot, int c, int4 ci) {
+        if constexpr (RECS) {
+          int64_t r0;
+          int nval;
+          rows_of(c, ci, r0, nval);
+          const float dt = lane < nval ? softplus_hw(rDt + dtb) : 0.f;
+          const double run = scan32_f64((double)(dt * Ah * kLog2e));
+          const double tot = half_last_f64(run, lane);
+          const float hi = (float)run;
+          float* r = S.sRec[slot % 3];
+          r[lane] = dt;
+          r[Q + lane] = hi;
+          r[2 * Q + lane] = exp2_hw((float)(tot - run)) * dt;
+          r[3 * Q + lane] = (float)(run - (double)hi);
+        }
       };
       auto flush_y = [&](int c, bool full, int4 cf) {   // y of chunk c out of sZ[c & 1] (bf16)
         int64_t r0;
@@ -1195,12 +1190,11 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
       if (nC > 0) {
         load_hist();
         load_set(0, ci0);
-        load_rec(0);
-        put_rec(0);
-        load_rec(min(1, nC - 1));
-        put_rec(1);
+        load_dt(0, ci0);
+        make_rec(0, 0, ci0);
+        load_dt(min(1, nC - 1), ci1);
+        make_rec(1, min(1, nC - 1), ci1);
         fetch_gram(0);
-        load_rec(min(2, nC - 1));
       }
       __syncthreads();
       if (nC > 0) {
@@ -1220,6 +1214,8 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
           ip1 = S.sInfo[min(c + 1, nC - 1) % 5];
           ip2 = S.sInfo[min(c + 2, nC - 1) % 5];
         }
+        // RECS: chunk c + 2's dt_raw, used for its records at the end of this iteration
+        load_dt(min(c + 2, nC - 1), ip2);
         // ---- chunk c + 1: tiles and staging. Chunk indices are clamped, so every iteration
         // issues the same memory operations (the last stages a copy nobody reads).
         [[maybe_unused]] uint64_t s0 = 0, s1 = 0;
@@ -1236,9 +1232,8 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
         if constexpr (STAMP) s0 = phase_stamp();
         stage(c + 1, std::false_type{}, ip1);
         if constexpr (STAMP) st_b += phase_stamp() - s0;
-        put_rec(c + 2);
+        make_rec(c + 2, min(c + 2, nC - 1), ip2);
         load_set(min(c + 2, nC - 1), ip2);
-        load_rec(min(c + 3, nC - 1));
         if constexpr (RING) {
           reinterpret_cast<int*>(&S.sInfo[(c + 3) % 5])[lane & 3] = rInfo;
           rInfo = info_word(c + 4);
@@ -1305,16 +1300,22 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     using NoDuty = std::integral_constant<int, 0>;
     using Hist = std::integral_constant<int, 1>;
     using Ring = std::integral_constant<int, 2>;
-    if (VARLEN && hv == 0) helpers(Half{}, std::true_type{}, Hist{});
-    else if (hv < 4) helpers(Half{}, std::true_type{}, NoDuty{});
-    else if (VARLEN && hv == 4) helpers(Quarter{}, std::false_type{}, Ring{});
-    else helpers(Quarter{}, std::false_type{}, NoDuty{});
+    using Recs = std::integral_constant<int, 3>;
+    if (VARLEN && hv == 0) helpers(Half{}, Hist{});
+    else if (hv < 4) helpers(Half{}, NoDuty{});
+    else if (VARLEN && hv == 4) helpers(Quarter{}, Ring{});
+    else if (hv == 5) helpers(Quarter{}, Recs{});
+    else helpers(Quarter{}, NoDuty{});
   }
 }
 
 // ---------------------------------------------------------------------------- host side
 // row stride of dt_raw in elements: dense [rows][H] unless the caller gave one
 static int64_t dt_stride(const PrefillArgs& a) { return a.dt_stride > 0 ? a.dt_stride : a.H; }
+template <typename T>
+static DtDev<T> dt_dev(const PrefillArgs& a) {
+  return {static_cast<const T*>(a.dt_raw), dt_stride(a), a.dt_bias, a.A};
+}
 
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -1337,13 +1338,14 @@ static hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   if (nC > 0) {
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, false>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
-                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{}, VarlenDev{});
+                       a.c_stride, static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, ConvArgs{},
+                       VarlenDev{});
   }
   hipLaunchKernelGGL((ssd_scan64_kernel<T, false>), dim3(a.B * a.H), dim3(P64_THREADS), scan_lds, stream,
                      static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{}, VarlenDev{}, nullptr);
+                     static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, ConvArgs{}, VarlenDev{},
+                     dt_dev<T>(a), nullptr);
   return hipGetLastError();
 }
 
@@ -1367,19 +1369,20 @@ hipError_t launch_ssd_prefill_conv(const PrefillArgs& a, const ConvArgs& cv, hip
   if (nC > 0) {
     hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true>), dim3(a.B * a.G * nC), dim3(PREP_THREADS), prep_lds,
                        stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                       a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a),
-                       static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv, VarlenDev{});
+                       a.c_stride, static_cast<unsigned char*>(a.workspace), a.L, a.H, a.G, nC, cv, VarlenDev{});
   }
   if (phase_cycles) {
     hipLaunchKernelGGL((ssd_scan64_kernel<T, true, false, true>), dim3(a.B * a.H), dim3(P64_THREADS),
                        sizeof(Pipe64Smem<T>), stream, static_cast<const T*>(a.x), a.x_stride, a.D,
                        static_cast<const T*>(a.z), a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, phase_cycles);
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, dt_dev<T>(a),
+                       phase_cycles);
   } else {
     hipLaunchKernelGGL((ssd_scan64_kernel<T, true>), dim3(a.B * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem<T>),
                        stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                        a.z_stride, a.h0, a.h_final, static_cast<T*>(a.y), a.y_stride,
-                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, nullptr);
+                       static_cast<const unsigned char*>(a.workspace), a.L, a.H, a.G, cv, VarlenDev{}, dt_dev<T>(a),
+                       nullptr);
   }
   return hipGetLastError();
 }
@@ -1392,8 +1395,7 @@ static int varlen_max_chunks(int total, int nseq) { return total / P64 + nseq; }
 size_t ssd_prefill_varlen_workspace(int total, int nseq, int H, int G) {
   using C = Cfg<bf16, P64>;
   const size_t maxC = (size_t)varlen_max_chunks(total, nseq);
-  return maxC * ((size_t)G * C::REC_BYTES + (size_t)H * C::HREC_BYTES + sizeof(int4) +
-                 (size_t)3 * H * SP * sizeof(bf16)) +
+  return maxC * ((size_t)G * C::REC_BYTES + sizeof(int4) + (size_t)3 * H * SP * sizeof(bf16)) +
          2 * ((size_t)nseq + 1) * sizeof(int32_t);
 }
 
@@ -1429,7 +1431,7 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
   }
   const int maxC = varlen_max_chunks(a.L, va.nseq);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  int4* info = reinterpret_cast<int4*>(ws + (size_t)maxC * ((size_t)a.G * C::REC_BYTES + (size_t)a.H * C::HREC_BYTES));
+  int4* info = reinterpret_cast<int4*>(ws + (size_t)maxC * (size_t)a.G * C::REC_BYTES);
   bf16* hist = reinterpret_cast<bf16*>(info + maxC);
   int32_t* cu = reinterpret_cast<int32_t*>(hist + (size_t)maxC * 3 * a.H * SP);
   int32_t* cc = cu + va.nseq + 1;
@@ -1440,12 +1442,11 @@ hipError_t launch_ssd_prefill_varlen(const PrefillArgs& a, const ConvArgs& cv, c
                      hist, va.nseq, va.npool, maxC, K};
   hipLaunchKernelGGL((ssd_prep_kernel<T, Q, true, true>), dim3(a.G * maxC), dim3(PREP_THREADS), prep_lds,
                      stream, static_cast<const T*>(a.Bm), a.b_stride, static_cast<const T*>(a.Cm),
-                     a.c_stride, static_cast<const T*>(a.dt_raw), a.dt_bias, a.A, dt_stride(a), ws, a.L, a.H, a.G, maxC,
-                     cv, vd);
+                     a.c_stride, ws, a.L, a.H, a.G, maxC, cv, vd);
   hipLaunchKernelGGL((ssd_scan64_kernel<T, true, true>), dim3(K * a.H), dim3(P64_THREADS), sizeof(Pipe64Smem<T>),
                      stream, static_cast<const T*>(a.x), a.x_stride, a.D, static_cast<const T*>(a.z),
                      a.z_stride, nullptr, nullptr, static_cast<T*>(a.y), a.y_stride, ws, a.L, a.H, a.G, cv, vd,
-                     nullptr);
+                     dt_dev<T>(a), nullptr);
   return hipGetLastError();
 }
 
@@ -1453,7 +1454,7 @@ template <typename T, int Q>
 static size_t ws_bytes(int B, int L, int H, int G) {
   using C = Cfg<T, Q>;
   const size_t nC = ((size_t)L + Q - 1) / Q;
-  return nC * ((size_t)B * G * C::REC_BYTES + (size_t)B * H * C::HREC_BYTES);
+  return nC * (size_t)B * G * C::REC_BYTES;
 }
 
 // The chunk a call names does not change the tiling: every supported chunk runs at 64.

@@ -145,14 +145,13 @@ def test_decode_token_count():
 
 def test_workspace_size_formula():
     """Per (sequence, group, 64-token chunk): fp32 causal Gram tiles + B^T and C operand
-    tiles; per (sequence, head, chunk): dt, its prefix sums (hi and lo) and per-token decay
-    weights. The named chunk is a tiling choice: every supported one tiles at 64."""
+    tiles. The named chunk is a tiling choice: every supported one tiles at 64."""
     for io, es in ((m2.MAMBA2_BF16, 2), (m2.MAMBA2_F32, 4)):
         for chunk in (64, 128, 256):
             d = dims(io=io, chunk=chunk, batch=3, seqlen=1000, nheads=16, ngroups=8)
             rec = 4 * 1024 * 3 + 2 * 128 * 64 * es
             nc = -(-1000 // 64)
-            assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * (3 * 8 * rec + 3 * 16 * 16 * 64)
+            assert m2.mamba2_ssd_prefill_workspace_bytes(d) == nc * 3 * 8 * rec
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(seqlen=0)) == 0
     assert m2.mamba2_ssd_prefill_workspace_bytes(dims(chunk=100)) == 0
     assert m2.lib.mamba2_ssd_prefill_workspace_bytes(None) == 0
@@ -240,10 +239,10 @@ def test_conv_prefill_workspace_size():
 def test_noalloc_prefill_rejects_before_any_launch():
     """mamba2_conv_ssd_prefill_noalloc checks dims and its 64 MiB static scratch on the host:
     a setting whose workspace would not fit is refused (MAMBA2_ERR_WORKSPACE) before anything
-    touches a device; at the 12B shape (bf16) 8192 tokens fit and 8256 do not."""
-    fit = dims(io=m2.MAMBA2_BF16, batch=1, seqlen=8192, nheads=160, ngroups=8)
-    assert m2.mamba2_conv_ssd_prefill_workspace_bytes(fit) == 64 << 20
-    for d, code in ((dims(io=m2.MAMBA2_BF16, batch=1, seqlen=8256, nheads=160, ngroups=8), 7),
+    touches a device; at the 12B shape (bf16) 11904 tokens (186 chunks) fit and 11905 do not."""
+    fit = dims(io=m2.MAMBA2_BF16, batch=1, seqlen=11904, nheads=160, ngroups=8)
+    assert m2.mamba2_conv_ssd_prefill_workspace_bytes(fit) <= 64 << 20
+    for d, code in ((dims(io=m2.MAMBA2_BF16, batch=1, seqlen=11905, nheads=160, ngroups=8), 7),
                     (dims(io=m2.MAMBA2_BF16, batch=2, seqlen=8192, nheads=160, ngroups=8), 7),
                     (dims(nheads=6, ngroups=4), ESHAPE), (dims(chunk=48), EUNSUP)):
         H, G = d.nheads, d.ngroups
@@ -311,7 +310,7 @@ def test_varlen_settings_and_workspace():
     for chunk in (64, 128, 256):
         d = dims(io=m2.MAMBA2_BF16, batch=5, seqlen=1000, nheads=16, ngroups=8, chunk=chunk)
         assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(d) == \
-            m * (8 * rec + 16 * 1024 + 16 + 384 * 16) + 8 * 6
+            m * (8 * rec + 16 + 384 * 16) + 8 * 6
     assert m2.mamba2_conv_ssd_prefill_varlen_workspace_bytes(dims(io=m2.MAMBA2_F32)) == 0
 
 
