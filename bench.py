@@ -172,17 +172,22 @@ def run_prefill(args, torch, m2, si, cfg, inp, chunk, fused=True):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    # the timed region: the steps back to back between two events (an event recorded between
+    # two launches leaves the GPU idle for a few microseconds, so none is recorded inside it)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
     for k in range(args.steps):
-        step(evs[k])
+        step()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_start.elapsed_time(t_end)
+    # then the same steps with events around each call, for the per-call durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
     per_call = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) * 1e3 / args.steps for i in range(len(calls))]
     return total_ms / args.steps, wall, per_call
 
