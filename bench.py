@@ -56,6 +56,26 @@ def kernel_source_hash(name: str) -> str:
     return h.hexdigest()[:16]
 
 
+def run_environment(torch) -> dict:
+    """What the line was measured on: the device, the ROCm and torch builds, and a hash of the
+    library's sources (the run's working copy need not be a git checkout)."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "state_space_sequence_causal_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "rocm": rocm, "hip": torch.version.hip, "torch": torch.__version__,
+            "library_sources_sha256_16": h.hexdigest()[:16]}
+
+
 def measured_traffic(name: str, chunk: int | None = None):
     """HBM bytes per launch from the committed counter summary, or None when the kernel
     source changed since the counters were taken (or they were taken at another chunk)."""
@@ -1013,6 +1033,7 @@ def main():
         "other_prefills": others,
         "wall_s_timed": wall,
         "settle_ms": {k: round(v, 1) for k, v in SETTLE_MS.items()},
+        "environment": run_environment(torch),
     }
     out["kernels"]["group_rmsnorm"] = {
         "us": rms_us, "GB_s": rms_bytes / (rms_us * 1e-6) / 1e9,
