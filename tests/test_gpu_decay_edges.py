@@ -8,7 +8,11 @@ scalar decay per head: hyper.ai summary, section "方法"; neurohive, section
   kernels take softplus(v) = v (the oracle evaluates softplus exactly); the decay of those
   tokens is exp(-20 .. -500) and their input term is ~1000x the usual one;
 * strong decay: A scaled by 500 on every other head, so that exp(dt A) underflows within a
-  few tokens and the decay across a 32-token block is exactly zero in fp32.
+  few tokens and the decay across a 32-token block is exactly zero in fp32;
+* decay at the split: A per head such that a 32-token block's sum of dt A log2(e) averages
+  -96, the value where the bf16 kernels' diagonal decay tiles switch from the factored form
+  (2^(pi_t - pi_end) times the record v_s) to the exact difference; about half the blocks of
+  every head take each form.
 
 Each case runs the scan (mamba2_ssd_prefill, bf16 and all-fp32), the one-call prefill with
 the conv inside (mamba2_conv_ssd_prefill, bf16 and fp32; checked on identical inputs: the
@@ -35,7 +39,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-EDGES = ("a_zero", "dt_past_shortcut", "strong_decay")
+EDGES = ("a_zero", "dt_past_shortcut", "strong_decay", "decay_at_split")
 
 
 def edge_inputs(edge: str, io: str, cid: int, seqlen: int):
@@ -52,6 +56,16 @@ def edge_inputs(edge: str, io: str, cid: int, seqlen: int):
         assert ((inp["dt_raw"] + inp["dt_bias"][None, None, :]) > 20.0).any()
     elif edge == "strong_decay":
         inp["A"] = (inp["A"] * np.where(np.arange(cfg.nheads) % 2 == 0, 500.0, 1.0)).astype(np.float32)
+    elif edge == "decay_at_split":
+        v = inp["dt_raw"].astype(np.float64) + inp["dt_bias"][None, None, :]
+        dt = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+        inp["A"] = (-3.0 / (dt.mean(axis=(0, 1)) * np.log2(np.e))).astype(np.float32)
+        lam = dt * inp["A"][None, None, :].astype(np.float64) * np.log2(np.e)
+        nb = cfg.seqlen // 32
+        if nb:   # both forms run in every head
+            blk = lam[:, :nb * 32].reshape(cfg.batch, nb, 32, cfg.nheads).sum(axis=2)
+            above = (blk > -96.0).mean(axis=(0, 1))
+            assert ((above > 0.2) & (above < 0.8)).all(), above
     else:
         raise ValueError(edge)
     return cfg, inp
