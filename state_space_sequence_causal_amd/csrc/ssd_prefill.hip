@@ -822,13 +822,14 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     }
   } else {
     // ========================================================== helper waves
-    // With the conv, the helpers issue ahead of the Y and H waves that share their SIMDs:
-    // their chain (loads, the x conv, the tiles of chunk c+1) is then the longest of a chunk,
+    // The helpers issue ahead of the Y and H waves that share their SIMDs: their chain (loads,
+    // the x conv, the tiles of chunk c+1, the records of chunk c+2) is the longest of a chunk,
     // and at equal priority the arbiter often picked the other roles first and the helpers
-    // finished last. At 12B 8k the one-call step goes from 320 to 291 us. Raising the H waves
-    // instead made it slower (339 us), the Y waves' priority made no difference, and without
-    // the conv the same priority slows the scan (240 to 260 us).
-    if constexpr (CONV) __builtin_amdgcn_s_setprio(1);
+    // finished last. At 12B 8k the one-call step went from 320 to 291 us with it; raising the
+    // H waves instead made it slower (339 us), and the Y waves' priority made no difference.
+    // Without the conv it helps since the records moved into this loop (the scan of the
+    // two-call path: 285 to 281 us per call with its prep).
+    __builtin_amdgcn_s_setprio(1);
     const int htid = tid - 512, hv = wave - 8;
     const T* xb = x + h * SP;
     const T* zb = z ? z + h * SP : xb;   // without z, x is loaded in its place and not used
