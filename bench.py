@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,11 +49,37 @@ KERNEL_SOURCES = {
 }
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def _code_only(src: str) -> str:
+    """The source with comments dropped and whitespace runs folded to one space (string and
+    character literals kept as written), so that editing a comment keeps the hash."""
+    out, pos, gap = [], 0, False
+    for m in _CODE_TOKENS.finditer(src):
+        if m.start() > pos:
+            out.append(" " if gap and out else "")
+            out.append(src[pos:m.start()])
+            gap = False
+        t = m.group(0)
+        if t[0] in "\"'":
+            out.append(" " if gap and out else "")
+            out.append(t)
+            gap = False
+        else:
+            gap = True
+        pos = m.end()
+    if pos < len(src):
+        out.append((" " if gap and out else "") + src[pos:])
+    return "".join(out)
+
+
 def kernel_source_hash(name: str) -> str:
+    """Hash of the code (not the comments) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[name]:
-        with open(os.path.join(ROOT, "state_space_sequence_causal_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "state_space_sequence_causal_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

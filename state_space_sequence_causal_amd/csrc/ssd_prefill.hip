@@ -379,8 +379,9 @@ __global__ __launch_bounds__(PREP_THREADS) __attribute__((amdgpu_waves_per_eu(4)
 //                   published into the other half of a double-buffered H^T.
 //   helper waves 8..15: chunk c+1's staging (flush of y(c-1), z, x^T, (w x)^T hi/lo), its
 //                   masked decay tiles M^T (the diagonal ones in halves by helper waves 0..3,
-//                   the other in quarters by helper waves 4..7), the dt / pi / v record of
-//                   chunk c+2, and the loads for the chunks after.
+//                   the other in quarters by helper waves 4..7), and the loads for the
+//                   chunks after; helper wave 5 also forms chunk c+2's dt / pi / v records
+//                   from dt_raw.
 // Everything chunk c+1 needs goes to the other half of double-buffered LDS tiles, so the
 // barrier that ends the iteration is the only synchronisation; records are staged two chunks
 // ahead (three buffers). Four waves per SIMD (one of each kind plus two helpers) hide each
@@ -854,8 +855,8 @@ void ssd_scan64_kernel(const T* __restrict__ x, int64_t x_stride, const float* _
     // M^T tiles: helper waves 0, 1 build tile 0 (diagonal 0) in halves (k steps hm of 16
     // source tokens), waves 2, 3 tile 2 (diagonal 1); waves 4..7 build tile 1 (block 1 from
     // block 0, no exponentials) in quarters of 8 source tokens. Helper wave v runs on SIMD
-    // v % 4, so every SIMD gets half a diagonal tile and a quarter of the other. Waves 0..3
-    // also carry the dt / pi_hi / v / pi_lo records (4Q words, a word a thread).
+    // v % 4, so every SIMD gets half a diagonal tile and a quarter of the other. Wave 5 also
+    // forms the dt / pi_hi / v / pi_lo records (4Q words, a word a thread) from dt_raw.
     const int kb = hv < 2 ? 0 : hv < 4 ? 2 : 1;
     const int hm = hv & 1, hq = hv & 3;
     // Each role (records or not, tiles or not) runs its own copy of the loop, so that every
