@@ -75,7 +75,11 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // SPLIT workgroups share a (sequence, group), each with hpg / SPLIT of its heads (small
 // batches, so that more CUs stream state). Each convolves B and C from the cache and leaves
 // the B and C cache columns alone: conv_shift_bc_kernel, next on the stream, shifts them.
-template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
+// STAGED (split launches whose share is at most 4 heads, 16 % hpp == 0): every wave of the
+// workgroup takes 32 hpp / 16 consecutive parts of one head, all requested at once, updates
+// them and stores them, and puts the new parts in LDS; after a barrier the head's first wave
+// forms y from LDS in the part order of the one-wave stream, so the bits are the same.
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 && NB == DEC_NB ? 8 : 4, 8)))
 void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
@@ -85,6 +89,7 @@ void state_update_kernel(
     int npool, int64_t us, int64_t zs, int64_t dtrs) {
   static_assert(DEC_IPH % NB == 0, "a head's parts fill whole rounds of the buffers");
   static_assert(SPLIT == 1 || NT == 1, "split launches take one token");
+  static_assert(!STAGED || (SPLIT > 1 && NB >= DEC_IPH / 4), "staged launches: split, one token, up to 8 parts a wave");
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
   const int hpg = H / G;
@@ -107,6 +112,8 @@ void state_update_kernel(
   auto csm = [&](int t) { return smem + t * nch + nx + DEC_N; };
   float* dts = smem + NT * nch;        // [NT][hpp]
   float* das = dts + NT * hpp;         // [NT][hpp]
+  // STAGED: the new state parts, [head][part][lane] 16 bytes each, 16-byte aligned
+  f32x4* stg = reinterpret_cast<f32x4*>(smem + ((NT * nch + 2 * NT * hpp + 3) & ~3));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -185,8 +192,19 @@ void state_update_kernel(
     dtb = dt_bias[h];
     av = A[h];
   }
+  // STAGED: wave w takes parts sub * ipw .. sub * ipw + ipw - 1 of head jw
+  const int wph = DEC_WAVES / hpp, ipw = DEC_IPH / wph;
+  const int jw = wave / wph, sub = wave % wph;
+  const char* sbase = reinterpret_cast<const char*>(ssm_state + ((int64_t)sb * H + h0w + jw) * DEC_N * DEC_P);
+  auto spart = [&](int m) {   // part m of head jw (clamped to the wave's last: never used)
+    return const_cast<float*>(reinterpret_cast<const float*>(
+        sbase + ((uint32_t)(sub * ipw + min(m, ipw - 1)) * 4 * DEC_P * 4u + lane_off)));
+  };
   // the state does not depend on the conv: its first parts are in flight during the conv
-  if (nitems > 0) {
+  if constexpr (STAGED) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) buf[k][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(spart(k)));
+  } else if (nitems > 0) {
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k) load_item(k, buf[k]);
   }
@@ -235,9 +253,53 @@ void state_update_kernel(
   }
   __syncthreads();
 
+  const T* zsrc = z_t ? z_t : u_t;     // without z a valid row is read and not used
+  if constexpr (STAGED) {
+    // update the wave's parts, store them, keep them in LDS for the head's y
+    {
+      const float a0 = das[jw];
+      const f32x4 dx0 = dts[jw] * *reinterpret_cast<const f32x4*>(xs(0) + jw * DEC_P + 4 * q);
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (k < ipw) {
+          const int m = sub * ipw + k;
+          const int n0 = 4 * m + rg;
+          const float bn = bsm(0)[n0];
+          const f32x4 nv = __builtin_elementwise_fma((f32x4)a0, buf[k][0], bn * dx0);
+          __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(spart(k)));
+          stg[(jw * DEC_IPH + m) * 64 + lane] = nv;
+        }
+      }
+    }
+    __syncthreads();
+    if (sub == 0) {
+      const int h = h0w + jw;
+      const Raw4<T> zz = ld4(zsrc + (int64_t)b * (z_t ? zs : us) + h * DEC_P + 4 * q);
+      f32x4 yacc = (f32x4){0.f, 0.f, 0.f, 0.f};
+      // the parts in the order of the one-wave stream: the same fma chain, the same bits
+#pragma unroll 8
+      for (int m = 0; m < DEC_IPH; ++m) {
+        const float cn = csm(0)[4 * m + rg];
+        yacc = __builtin_elementwise_fma((f32x4)cn, stg[(jw * DEC_IPH + m) * 64 + lane], yacc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        yacc[i] += __shfl_xor(yacc[i], 16);
+        yacc[i] += __shfl_xor(yacc[i], 32);
+      }
+      const float dh = D ? D[h] : 0.f;
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(xs(0) + jw * DEC_P + 4 * q);
+      f32x4 o = yacc + dh * x4;
+      if (z_t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= silu_fast(zz.get(i));
+      }
+      store4(y_t + (int64_t)b * di + h * DEC_P + 4 * q, o[0], o[1], o[2], o[3]);
+    }
+    return;
+  }
   // stream the heads: per part, request part it + NB - 1, then update part it in place
   // (NT times, one token after the other)
-  const T* zsrc = z_t ? z_t : u_t;     // without z a valid row is read and not used
   for (int hj = 0; hj < nheads_w; ++hj) {
     const int j = wave + DEC_WAVES * hj;   // head of this workgroup
     const int h = h0w + j;
@@ -340,16 +402,18 @@ __global__ __launch_bounds__(256) void conv_shift_bc_kernel(const T* __restrict_
   st16(cs + 2 * Cc, u);
 }
 
-template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1>
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false>
 static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int hpp = a.H / a.G / SPLIT;
-  const size_t lds = sizeof(float) * ((size_t)NT * (hpp * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpp);
+  size_t lds = sizeof(float) * ((size_t)NT * (hpp * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpp);
+  if (STAGED) lds = ((lds + 15) & ~(size_t)15) + (size_t)hpp * DEC_IPH * 64 * sizeof(f32x4);
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT, STAGED>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT>), dim3(a.B * a.G * SPLIT), dim3(DEC_THREADS), lds, stream,
+  hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT, STAGED>), dim3(a.B * a.G * SPLIT), dim3(DEC_THREADS), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
@@ -389,8 +453,10 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
       // two rounds, took 32 us against 18 us. The B and C channels must stay inside the
       // single conv pass (at most 4096 channels).
       const int hpg = a.H / a.G, bg = a.B * a.G, cus = num_cus();
-      if (hpg % 4 == 0 && hpg / 4 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 4 <= cus)
+      if (hpg % 4 == 0 && hpg / 4 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 4 <= cus) {
+        if (hpg / 4 <= 4 && DEC_WAVES % (hpg / 4) == 0) return launch_nt<T, 1, 2 * DEC_NB, 4, true>(a, stream);
         return launch_nt<T, 1, 2 * DEC_NB, 4>(a, stream);
+      }
       if (hpg % 2 == 0 && hpg / 2 * DEC_P + 2 * DEC_N <= DEC_THREADS * 4 && bg * 2 <= cus)
         return launch_nt<T, 1, 2 * DEC_NB, 2>(a, stream);
       return launch_nt<T, 1>(a, stream);
