@@ -15,8 +15,10 @@
 // few (sequence, group) pairs, 2 or 4 workgroups share a pair, each with its
 // share of the heads and their x channels; the shared B and C columns are then
 // shifted by a second, small kernel on the same stream, which the stream starts
-// only after every read of the old cache is done (see SPLIT below). Each of
-// its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
+// only after every read of the old cache is done (see SPLIT below). When such a
+// workgroup holds at most 4 heads, its 16 waves share them: each requests all of
+// its 8 parts of one head at once, and y is formed from LDS afterwards (STAGED
+// below). Otherwise each of its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
 // (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of row n = 4m + rg, so one wave
 // instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
 // buffers with 3 in flight; every load is unconditional (loads past the wave's
