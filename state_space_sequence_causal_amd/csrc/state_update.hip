@@ -194,8 +194,8 @@ void state_update_kernel(
     dtb = dt_bias[h];
     av = A[h];
   }
-  // STAGED: wave w takes parts sub * ipw .. sub * ipw + ipw - 1 of head jw
-  const int wph = DEC_WAVES / hpp, ipw = DEC_IPH / wph;
+  // STAGED: wave w takes parts sub * ipw .. sub * ipw + ipw - 1 of head jw (hpp divides 16)
+  const int wph = STAGED ? DEC_WAVES / hpp : 1, ipw = DEC_IPH / wph;
   const int jw = wave / wph, sub = wave % wph;
   const char* sbase = reinterpret_cast<const char*>(ssm_state + ((int64_t)sb * H + h0w + jw) * DEC_N * DEC_P);
   auto spart = [&](int m) {   // part m of head jw (clamped to the wave's last: never used)
