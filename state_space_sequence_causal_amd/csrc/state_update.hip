@@ -409,11 +409,14 @@ static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int hpp = a.H / a.G / SPLIT;
   size_t lds = sizeof(float) * ((size_t)NT * (hpp * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpp);
   if (STAGED) lds = ((lds + 15) & ~(size_t)15) + (size_t)hpp * DEC_IPH * 64 * sizeof(f32x4);
-  if (lds > 64 * 1024) {
+  // the LDS limit is raised once per instance, and again only for a larger request
+  static size_t lds_set = 64 * 1024;
+  if (lds > lds_set) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT, STAGED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    lds_set = lds;
   }
   hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT, STAGED>), dim3(a.B * a.G * SPLIT), dim3(DEC_THREADS), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
