@@ -18,7 +18,8 @@
 // only after every read of the old cache is done (see SPLIT below). When such a
 // workgroup holds at most 4 heads, its 16 waves share them: each requests all of
 // its 8 parts of one head at once, and y is formed from LDS afterwards (STAGED
-// below). Otherwise each of its 16 waves streams one head (two for wider groups) in parts of 4 rows: lane
+// below). Otherwise each of its 16 waves (8 for several tokens a call) streams one head (two or
+// more for wider groups, and at 8 waves) in parts of 4 rows: lane
 // (q = l % 16, rg = l / 16) handles p = 4q..4q+3 of row n = 4m + rg, so one wave
 // instruction touches 1 KiB of contiguous state. Parts rotate through 4 register
 // buffers with 3 in flight; every load is unconditional (loads past the wave's
@@ -81,8 +82,10 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
 // workgroup takes 32 hpp / 16 consecutive parts of one head, all requested at once, updates
 // them and stores them, and puts the new parts in LDS; after a barrier the head's first wave
 // forms y from LDS in the part order of the one-wave stream, so the bits are the same.
-template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false>
-__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(NT == 1 && NB == DEC_NB ? 8 : 4, 8)))
+// WAVES: waves per workgroup (16; 8 for several tokens, whose register use lets only one
+// 16-wave workgroup per CU: with 8, two heads a wave, the 9B batch-64 grid fits in one round).
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false, int WAVES = DEC_WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 && NB == DEC_NB ? 8 : 4, 8)))
 void state_update_kernel(
     const T* __restrict__ u_t, const float* __restrict__ w, const float* __restrict__ bias,
     T* __restrict__ conv_state, const T* __restrict__ dt_raw_t, const float* __restrict__ dt_bias,
@@ -91,6 +94,8 @@ void state_update_kernel(
     int npool, int64_t us, int64_t zs, int64_t dtrs) {
   static_assert(DEC_IPH % NB == 0, "a head's parts fill whole rounds of the buffers");
   static_assert(SPLIT == 1 || NT == 1, "split launches take one token");
+  constexpr int NWAVES = WAVES, NTHREADS = WAVES * 64;
+  static_assert(DEC_MAX_HPG <= NTHREADS, "one thread per head for dt");
   static_assert(!STAGED || (SPLIT > 1 && NB >= DEC_IPH / 4), "staged launches: split, one token, up to 8 parts a wave");
   extern __shared__ float smem[];
   constexpr int VE = Vec<T>::VE;
@@ -125,7 +130,7 @@ void state_update_kernel(
   if (slots) {
     sb = slots[b];
     if (sb < 0 || sb >= npool) {
-      for (int i = tid; i < NT * hpp * DEC_P / 4; i += DEC_THREADS) {
+      for (int i = tid; i < NT * hpp * DEC_P / 4; i += NTHREADS) {
         const int t = i / (hpp * DEC_P / 4), k = i % (hpp * DEC_P / 4);
         store4(y_t + ((int64_t)b * NT + t) * di + h0w * DEC_P + 4 * k, 0.f, 0.f, 0.f, 0.f);
       }
@@ -134,18 +139,18 @@ void state_update_kernel(
   }
   const int q = lane & 15, rg = lane >> 4;
 
-  // Work items of this wave: (head j, part) for j = wave, wave + DEC_WAVES, ...; part m holds
+  // Work items of this wave: (head j, part) for j = wave, wave + NWAVES, ...; part m holds
   // the 4 DEC_K state rows n = 4 DEC_K m + rg + 4k, k < DEC_K. Item it of the wave is part
   // it % DEC_IPH of its head it / DEC_IPH.
-  const int nheads_w = (hpp - wave + DEC_WAVES - 1) / DEC_WAVES;
+  const int nheads_w = (hpp - wave + NWAVES - 1) / NWAVES;
   const int nitems = nheads_w * DEC_IPH;
   // the wave's state base is uniform; an item is a 32-bit byte offset from it (heads of a
-  // wave are DEC_WAVES apart, parts of a head 4 DEC_K rows apart)
+  // wave are NWAVES apart, parts of a head 4 DEC_K rows apart)
   const char* wbase = reinterpret_cast<const char*>(
       ssm_state + ((int64_t)sb * H + h0w + wave) * DEC_N * DEC_P);
   const uint32_t lane_off = (uint32_t)(rg * DEC_P + 4 * q) * 4u;
   auto item_off = [&](int it) -> uint32_t {
-    return (uint32_t)((it / DEC_IPH) * DEC_WAVES * DEC_N * DEC_P + (it % DEC_IPH) * 4 * DEC_K * DEC_P) * 4u;
+    return (uint32_t)((it / DEC_IPH) * NWAVES * DEC_N * DEC_P + (it % DEC_IPH) * 4 * DEC_K * DEC_P) * 4u;
   };
   auto item_ptr = [&](int it) {
     return const_cast<float*>(reinterpret_cast<const float*>(wbase + (item_off(it) + lane_off)));
@@ -195,7 +200,7 @@ void state_update_kernel(
     av = A[h];
   }
   // STAGED: wave w takes parts sub * ipw .. sub * ipw + ipw - 1 of head jw (hpp divides 16)
-  const int wph = STAGED ? DEC_WAVES / hpp : 1, ipw = DEC_IPH / wph;
+  const int wph = STAGED ? NWAVES / hpp : 1, ipw = DEC_IPH / wph;
   const int jw = wave / wph, sub = wave % wph;
   const char* sbase = reinterpret_cast<const char*>(ssm_state + ((int64_t)sb * H + h0w + jw) * DEC_N * DEC_P);
   auto spart = [&](int m) {   // part m of head jw (clamped to the wave's last: never used)
@@ -223,8 +228,8 @@ void state_update_kernel(
       for (int k = 0; k < 3; ++k) *reinterpret_cast<decltype(e[0].v)*>(csb + k * Cc + c) = e[NT + k].v;
     }
   }
-  // groups wider than DEC_THREADS * CV channels: the rest, plainly
-  for (int l2 = lc + DEC_THREADS * CV; l2 < nch; l2 += DEC_THREADS * CV) {
+  // groups wider than NTHREADS * CV channels: the rest, plainly
+  for (int l2 = lc + NTHREADS * CV; l2 < nch; l2 += NTHREADS * CV) {
     const int c2 = l2 < nx ? h0w * DEC_P + l2
                            : (l2 < nx + DEC_N ? di + g * DEC_N + (l2 - nx) : di + G * DEC_N + g * DEC_N + (l2 - nx - DEC_N));
     Raw4<T> a[NT + 3];
@@ -303,7 +308,7 @@ void state_update_kernel(
   // stream the heads: per part, request part it + NB - 1, then update part it in place
   // (NT times, one token after the other)
   for (int hj = 0; hj < nheads_w; ++hj) {
-    const int j = wave + DEC_WAVES * hj;   // head of this workgroup
+    const int j = wave + NWAVES * hj;   // head of this workgroup
     const int h = h0w + j;
     float a[NT];
     f32x4 dx[NT], yacc[NT];
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(256) void conv_shift_bc_kernel(const T* __restrict_
   st16(cs + 2 * Cc, u);
 }
 
-template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false>
+template <typename T, int NT, int NB = DEC_NB, int SPLIT = 1, bool STAGED = false, int WAVES = DEC_WAVES>
 static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int hpp = a.H / a.G / SPLIT;
   size_t lds = sizeof(float) * ((size_t)NT * (hpp * DEC_P + 2 * DEC_N) + 2 * (size_t)NT * hpp);
@@ -413,12 +418,12 @@ static hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   static size_t lds_set = 64 * 1024;
   if (lds > lds_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT, STAGED>),
+        reinterpret_cast<const void*>(&state_update_kernel<T, NT, NB, SPLIT, STAGED, WAVES>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_set = lds;
   }
-  hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT, STAGED>), dim3(a.B * a.G * SPLIT), dim3(DEC_THREADS), lds, stream,
+  hipLaunchKernelGGL((state_update_kernel<T, NT, NB, SPLIT, STAGED, WAVES>), dim3(a.B * a.G * SPLIT), dim3(WAVES * 64), lds, stream,
                      static_cast<const T*>(a.u_t), a.w, a.bias, static_cast<T*>(a.conv_state),
                      static_cast<const T*>(a.dt_raw_t), a.dt_bias, a.A, a.D,
                      static_cast<const T*>(a.z_t), a.ssm_state, static_cast<T*>(a.y_t), a.H, a.G, a.slots,
@@ -466,11 +471,11 @@ static hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
         return launch_nt<T, 1, 2 * DEC_NB, 2>(a, stream);
       return launch_nt<T, 1>(a, stream);
     }
-    case 2: return launch_nt<T, 2>(a, stream);
-    case 3: return launch_nt<T, 3>(a, stream);
-    case 4: return launch_nt<T, 4>(a, stream);
-    case 5: return launch_nt<T, 5>(a, stream);
-    case 6: return launch_nt<T, 6>(a, stream);
+    case 2: return launch_nt<T, 2, DEC_NB, 1, false, 8>(a, stream);
+    case 3: return launch_nt<T, 3, DEC_NB, 1, false, 8>(a, stream);
+    case 4: return launch_nt<T, 4, DEC_NB, 1, false, 8>(a, stream);
+    case 5: return launch_nt<T, 5, DEC_NB, 1, false, 8>(a, stream);
+    case 6: return launch_nt<T, 6, DEC_NB, 1, false, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
