@@ -4,8 +4,9 @@ T = dims->seqlen new tokens per sequence.
 The call promises the bits of T one-token calls in order (test_gpu_parity.py ties the
 one-token call to the oracle); each case runs both and compares y, the conv cache and the
 state bitwise, for T = 2 .. 6 in bf16 and fp32, the 9B-shape batch of 64 at T = 4, one
-group of 20 heads, the slot form against gather / T-token call / scatter, and once against
-the oracle (oracle.state_update_tokens).
+group of 20 heads, shapes whose one-token calls take the split form with 1, 2 or 4 heads
+per workgroup shared by all its waves, the slot form against gather / T-token call /
+scatter, and once against the oracle (oracle.state_update_tokens).
 """
 import numpy as np
 import pytest
@@ -84,6 +85,14 @@ def test_9b_batch64_four_tokens():
 
 def test_one_group_twenty_heads():
     check(611, 2, 3, H=20, G=1)
+
+
+@pytest.mark.parametrize("H, G", [(32, 8), (32, 4), (64, 4)])
+def test_tokens_equal_staged_one_token_calls(H, G):
+    """One-token calls at these small batches split each (sequence, group) over 4 workgroups
+    whose 16 waves share 1, 2 or 4 heads and form y from LDS; the T-token call streams whole
+    heads. Both must give the same bits."""
+    check(620 + H // G, 2, 3, H=H, G=G)
 
 
 def test_slots_three_tokens():
